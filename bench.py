@@ -1,0 +1,246 @@
+"""Benchmark of the verify step on one MI355X.
+
+One step = the whole hot path over one batch of the chain workload (B=32, K=5, V=32000 bf16
+logits, T=1; attention over a 2048-token bf16 KV cache, 32 query / 8 KV heads, head size 128):
+  specv_build_tree_mask -> specv_tree_attn_verify (one layer) -> specv_accept_resample.
+value = draft positions verified per second = B*K / step time.  Inputs are resident in HBM and
+rotate over enough sets (> 2 x 256 MB) that the Infinity Cache cannot serve them.
+
+Prints ONE JSON line.  Extra legs:
+  roofline      attention call (HBM-bound here): algorithmic bytes / mean call time (HIP events
+                on the launch stream); the accept call's figure is reported beside it;
+  cpu_baseline  the oracle (numpy fp64) on a bounded sample of the same workload, host cores.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--copy-probe]
+--copy-probe only runs a device-to-device copy of known size (to calibrate HBM byte counters).
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np
+
+METRIC = "draft positions verified/s (B=32,V=32k,K=5) + % of MI355X HBM roofline"
+HBM_PEAK_GBS = 8000.0
+B, K, V, T = 32, 5, 32000, 1.0
+HQ, HKV, D, CTX = 32, 8, 128, 2048
+ACCEPT_SETS = 24          # 24 x 22.5 MB of logits
+ATTN_SETS = 3             # 3 x 269 MB of KV cache
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline leg")
+    ap.add_argument("--copy-probe", action="store_true")
+    return ap.parse_args()
+
+
+def copy_probe(torch):
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_each_way": n, "launches": 10}))
+
+
+def accept_bytes(n1, n_internal, V, elem):
+    """Algorithmic HBM bytes of one accept call: every target row and the draft rows of internal
+    nodes once, plus the tiny per-node inputs and outputs."""
+    return B * (n1 + n_internal) * V * elem + B * n1 * 4 * 6 + B * 4
+
+
+def attn_bytes(ctx, n1):
+    """K and V of the context and of the tree entries once, Q in and O out (bf16), LSE out."""
+    kv = 2 * B * HKV * (ctx + n1) * D * 2
+    qo = 2 * B * n1 * HQ * D * 2 + B * n1 * HQ * 4
+    return kv + qo
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the verify step shards by sequence and KV head with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import draft_verify_sampling_specv_amd as specv
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe(torch)
+        return
+
+    n1 = K + 1
+    # ---- inputs (seeded, synthetic) resident in HBM
+    t0 = time.time()
+    acc_sets = []
+    for s in range(ACCEPT_SETS):
+        w = workloads.chain_config(T=T, seed_base=2000 + 17 * s)
+        acc_sets.append(dict(
+            target=torch.from_numpy(w.target_logits).cuda().to(torch.bfloat16),
+            draft=torch.from_numpy(w.draft_logits).cuda().to(torch.bfloat16),
+            tokens=torch.from_numpy(w.tokens).cuda(), parent=torch.from_numpy(w.parent).cuda(),
+            w=w if s == 0 else None))
+    greedy = workloads.chain_config(T=0.0)
+    g_target = torch.from_numpy(greedy.target_logits).cuda().to(torch.bfloat16)
+    g_tokens = torch.from_numpy(greedy.tokens).cuda()
+    a0 = workloads.chain_attention(B=B)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    attn_sets = []
+    for s in range(ATTN_SETS):
+        if s == 0:
+            q = torch.from_numpy(a0.q).cuda().to(torch.bfloat16)
+            kc = torch.from_numpy(a0.k_cache).cuda().to(torch.bfloat16)
+            vc = torch.from_numpy(a0.v_cache).cuda().to(torch.bfloat16)
+        else:
+            shape = tuple(a0.k_cache.shape)
+            q = torch.randn(a0.q.shape, generator=gen, device="cuda").to(torch.bfloat16)
+            kc = torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16)
+            vc = torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16)
+        attn_sets.append((q, kc, vc))
+    ctx_len = torch.full((B,), CTX, dtype=torch.int32, device="cuda")
+    parent = acc_sets[0]["parent"]
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f} s")
+
+    # ---- preallocated outputs and workspaces (nothing is allocated inside the timed region)
+    mask_out = (torch.empty((B, n1, 1), dtype=torch.int32, device="cuda"),
+                torch.empty((B, n1), dtype=torch.int32, device="cuda"),
+                torch.empty((B,), dtype=torch.int32, device="cuda"))
+    abuf = specv.AttnBuffers.allocate(attn_sets[0][0], attn_sets[0][1])
+    cbuf = specv.AcceptBuffers.allocate(B, n1, V, torch.bfloat16, "cuda")
+    gbuf = specv.AcceptBuffers.allocate(B, n1, V, torch.bfloat16, "cuda")
+
+    def step(i):
+        a = acc_sets[i % ACCEPT_SETS]
+        q, kc, vc = attn_sets[i % ATTN_SETS]
+        mask, _, _ = specv.build_tree_mask(parent, out=mask_out)
+        specv.tree_attn_verify(q, kc, vc, ctx_len, mask, buffers=abuf)
+        specv.accept_resample(a["target"], a["draft"], a["tokens"], a["parent"], T, seed=1234, offset=i,
+                              buffers=cbuf)
+
+    def timed(fn, n):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(n):
+            fn(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n   # ms per call
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = timed(step, args.steps)
+
+    # ---- per-call times (same stream, same rotation), for the rooflines
+    mask_now = specv.build_tree_mask(parent, out=mask_out)[0]
+    ms_attn = timed(lambda i: specv.tree_attn_verify(*attn_sets[i % ATTN_SETS], ctx_len, mask_now,
+                                                     buffers=abuf), args.steps)
+    ms_accept = timed(lambda i: specv.accept_resample(
+        acc_sets[i % ACCEPT_SETS]["target"], acc_sets[i % ACCEPT_SETS]["draft"], acc_sets[i % ACCEPT_SETS]["tokens"],
+        parent, T, seed=1234, offset=i, buffers=cbuf), args.steps)
+    ms_greedy = timed(lambda i: specv.accept_resample(g_target, None, g_tokens, parent, 0.0, buffers=gbuf),
+                      args.steps)
+    ms_mask = timed(lambda i: specv.build_tree_mask(parent, out=mask_out), args.steps)
+
+    # acceptance statistics of the timed configuration (set 0)
+    res = specv.accept_resample(acc_sets[0]["target"], acc_sets[0]["draft"], acc_sets[0]["tokens"], parent, T,
+                                seed=1234, offset=0)
+    mean_len = float(res.accept_len.float().mean().item())
+
+    positions = B * K
+    n_internal = K
+    ab = attn_bytes(CTX, n1)
+    cb = accept_bytes(n1, n_internal, V, 2)
+    attn_gbs = ab / (ms_attn * 1e-3) / 1e9
+    acc_gbs = cb / (ms_accept * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": positions / (ms_step * 1e-3),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "chain verify: B=32, K=5 (6 target positions), V=32000 bf16 logits "
+                               "N(0,3), draft noise 0.5285 (alpha~0.8), T=1; attention over ctx 2048 "
+                               "(+6 tree keys), 32 q / 8 kv heads, D=128, bf16",
+                   "global_batch": B, "seq_len": CTX, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": attn_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "specv_tree_attn_verify (attn_partial + attn_combine)",
+                     "bytes_per_call": ab, "ms_per_call": ms_attn},
+        "roofline_accept": {"bound": "hbm", "achieved": acc_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": acc_gbs / HBM_PEAK_GBS, "bytes_per_call": cb, "ms_per_call": ms_accept,
+                            "kernel": "specv_accept_resample (stats + walk + draw)"},
+        "accept_only_positions_per_s": positions / (ms_accept * 1e-3),
+        "ms_mask": ms_mask,
+        "ms_greedy_accept": ms_greedy,
+        "mean_accept_len": mean_len,
+    }
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(acc_sets[0]["w"], a0)
+    print(json.dumps(out))
+
+
+def cpu_baseline(w, a):
+    """Oracle (numpy fp64) on a bounded sample of the same workload: the whole verify step
+    (mask, attention, accept) for as many sequences as fit in about 15 s."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import accept as o_accept, attention as o_attn, philox as o_philox, tree as o_tree
+
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    t0 = time.time()
+    done = 0
+    while time.time() - t0 < 15.0:
+        b = done % w.B
+        mask, _, _ = o_tree.build_tree_mask_batch(a.parent[b:b + 1])
+        o_attn.tree_attention(a.q[b:b + 1], a.k_cache[b:b + 1], a.v_cache[b:b + 1], a.ctx_len[b:b + 1], mask,
+                              a.scale)
+        ua, ur = o_philox.uniforms(1234, 0, 1, w.N1)
+        o_accept.accept_batch(np.asarray(w.target_logits[b:b + 1], np.float64),
+                              np.asarray(w.draft_logits[b:b + 1], np.float64),
+                              w.tokens[b:b + 1], w.parent[b:b + 1], w.T, ua, ur)
+        done += 1
+    dt = time.time() - t0
+    return {"value": done * K / dt, "unit": "positions/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} sequences (cycling over the {w.B} of the timed workload), whole verify "
+                      f"step (mask, attention, accept) in numpy fp64, {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,25 @@
+"""Python binding of libspecv: the verify step of speculative decoding on MI355X.
+
+Argument marshalling only.  Every step runs in the HIP kernels of libspecv.so
+(see include/specv.h for the C ABI and the contract of each call); PyTorch
+provides device memory and the current stream.  There is no fallback: if the
+library has not been built this import fails.
+
+  build_tree_mask(parent)                                  -> mask, depth, status
+  tree_attn_verify(q, k_cache, v_cache, ctx_len, mask)     -> out, lse
+  accept_resample(target, draft, tokens, parent, T, seed, offset) -> AcceptResult
+"""
+
+from ._lib import (  # noqa: F401
+    SpecvError,
+    AcceptResult,
+    AcceptBuffers,
+    AttnBuffers,
+    lib,
+    library_path,
+    build_tree_mask,
+    tree_attn_verify,
+    accept_resample,
+    accept_workspace_bytes,
+    attn_workspace_bytes,
+)

@@ -1,0 +1,133 @@
+// C ABI of libspecv (declarations and full contract in include/specv.h).  Host-side argument
+// validation happens here, before any launch; nothing is allocated, nothing synchronises.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/specv.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+specv_status fail(specv_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+specv_status fail(specv_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+specv_status ok() {
+    g_last_error[0] = '\0';
+    return SPECV_OK;
+}
+
+specv_status hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(SPECV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* specv_status_string(specv_status s) {
+    switch (s) {
+        case SPECV_OK: return "ok";
+        case SPECV_ERR_INVALID_ARG: return "invalid argument";
+        case SPECV_ERR_UNSUPPORTED: return "unsupported configuration";
+        case SPECV_ERR_WORKSPACE: return "workspace missing or too small";
+        case SPECV_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+const char* specv_last_error(void) { return g_last_error; }
+
+specv_status specv_build_tree_mask(const int32_t* parent, int32_t B, int32_t K, uint32_t* mask,
+                                   int32_t* depth, int32_t* tree_status, hipStream_t stream) {
+    if (B < 0) return fail(SPECV_ERR_INVALID_ARG, "B = %d < 0", B);
+    if (K < 0 || K + 1 > SPECV_MAX_NODES)
+        return fail(SPECV_ERR_INVALID_ARG, "K = %d outside [0, %d]", K, SPECV_MAX_NODES - 1);
+    if (B == 0) return ok();
+    if (!parent || !mask || !depth || !tree_status)
+        return fail(SPECV_ERR_INVALID_ARG, "NULL pointer argument");
+    return hip_status(specv::launch_build_tree_mask(parent, B, K + 1, mask, depth, tree_status, stream),
+                      "build_tree_mask");
+}
+
+size_t specv_attn_workspace_bytes(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
+                                  int32_t Lmax) {
+    if (B <= 0 || K < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || (D != 64 && D != 128) || Lmax <= 0)
+        return 0;
+    return specv::attn_workspace_bytes(B, K + 1, Hq, Hkv, D, Lmax);
+}
+
+specv_status specv_tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* ctx_len, const uint32_t* mask, int32_t B,
+                                    int32_t K, int32_t Hq, int32_t Hkv, int32_t D, int32_t Lmax,
+                                    float scale, specv_dtype dtype, void* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (B < 0) return fail(SPECV_ERR_INVALID_ARG, "B = %d < 0", B);
+    if (K < 0 || K + 1 > SPECV_MAX_NODES)
+        return fail(SPECV_ERR_INVALID_ARG, "K = %d outside [0, %d]", K, SPECV_MAX_NODES - 1);
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+        return fail(SPECV_ERR_INVALID_ARG, "Hq = %d, Hkv = %d: need Hq a positive multiple of Hkv", Hq, Hkv);
+    if (Lmax < K + 1) return fail(SPECV_ERR_INVALID_ARG, "Lmax = %d < K + 1 = %d", Lmax, K + 1);
+    if (!(std::isfinite(scale) && scale > 0.f))
+        return fail(SPECV_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (dtype != SPECV_F32 && dtype != SPECV_BF16)
+        return fail(SPECV_ERR_UNSUPPORTED, "dtype %d not supported", static_cast<int>(dtype));
+    if (D != 64 && D != 128) return fail(SPECV_ERR_UNSUPPORTED, "head size D = %d not in {64, 128}", D);
+    if (B == 0) return ok();
+    if (!q || !k_cache || !v_cache || !ctx_len || !mask || !out)
+        return fail(SPECV_ERR_INVALID_ARG, "NULL pointer argument");
+    const size_t need = (dtype == SPECV_BF16) ? specv::attn_workspace_bytes(B, K + 1, Hq, Hkv, D, Lmax) : 0;
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(SPECV_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    specv::AttnArgs a{q, k_cache, v_cache, ctx_len, mask, B, K + 1, Hq, Hkv, D, Lmax, scale,
+                      dtype == SPECV_BF16, out, lse, workspace};
+    return hip_status(specv::launch_attention(a, stream), "tree_attn_verify");
+}
+
+size_t specv_accept_workspace_bytes(int32_t B, int32_t K, int32_t V, specv_dtype logits_dtype) {
+    if (B <= 0 || K < 0 || K + 1 > SPECV_MAX_NODES || V < 1 || V > SPECV_MAX_VOCAB) return 0;
+    return specv::accept_workspace_bytes(B, K + 1, V, logits_dtype == SPECV_BF16);
+}
+
+specv_status specv_accept_resample(const void* target_logits, const void* draft_logits,
+                                   specv_dtype logits_dtype, const int32_t* tokens,
+                                   const int32_t* parent, int32_t B, int32_t K, int32_t V,
+                                   float temperature, uint64_t seed, uint64_t offset,
+                                   int32_t* accept_len, int32_t* out_tokens, int32_t* out_nodes,
+                                   float* p_tok, float* q_tok, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+    if (B < 0) return fail(SPECV_ERR_INVALID_ARG, "B = %d < 0", B);
+    if (K < 0 || K + 1 > SPECV_MAX_NODES)
+        return fail(SPECV_ERR_INVALID_ARG, "K = %d outside [0, %d]", K, SPECV_MAX_NODES - 1);
+    if (V < 1 || V > SPECV_MAX_VOCAB)
+        return fail(SPECV_ERR_INVALID_ARG, "V = %d outside [1, %d]", V, SPECV_MAX_VOCAB);
+    if (!std::isfinite(temperature) || temperature < 0.f)
+        return fail(SPECV_ERR_INVALID_ARG, "temperature must be finite and >= 0");
+    if (logits_dtype != SPECV_F32 && logits_dtype != SPECV_BF16)
+        return fail(SPECV_ERR_UNSUPPORTED, "dtype %d not supported", static_cast<int>(logits_dtype));
+    if (B == 0) return ok();
+    if (!target_logits || !tokens || !parent || !accept_len || !out_tokens || !out_nodes)
+        return fail(SPECV_ERR_INVALID_ARG, "NULL pointer argument");
+    if (temperature > 0.f && !draft_logits)
+        return fail(SPECV_ERR_INVALID_ARG, "draft_logits may be NULL only at temperature 0");
+    const size_t need = specv::accept_workspace_bytes(B, K + 1, V, logits_dtype == SPECV_BF16);
+    if (!workspace || workspace_bytes < need)
+        return fail(SPECV_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    specv::AcceptArgs a{target_logits, temperature > 0.f ? draft_logits : nullptr,
+                        logits_dtype == SPECV_BF16, tokens, parent, B, K + 1, V, temperature,
+                        seed, offset, accept_len, out_tokens, out_nodes, p_tok, q_tok, workspace};
+    return hip_status(specv::launch_accept(a, stream), "accept_resample");
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Internal launchers behind the C ABI (include/specv.h).  Host code only calls these after the
+// arguments have been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace specv {
+
+constexpr int kMaxNodes = 1024;
+
+hipError_t launch_build_tree_mask(const int32_t* parent, int B, int n1, uint32_t* mask,
+                                  int32_t* depth, int32_t* tree_status, hipStream_t stream);
+
+// ------------------------------------------------------------------------------------ accept
+struct AcceptArgs {
+    const void* target;
+    const void* draft;     // NULL iff greedy
+    bool bf16;
+    const int32_t* tokens;
+    const int32_t* parent;
+    int B, n1, V;
+    float temperature;     // 0 -> greedy
+    uint64_t seed, offset;
+    int32_t* accept_len;
+    int32_t* out_tokens;
+    int32_t* out_nodes;
+    float* p_tok;          // may be NULL
+    float* q_tok;          // may be NULL
+    void* workspace;
+};
+
+size_t accept_workspace_bytes(int B, int n1, int V, bool bf16);
+hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
+
+// ------------------------------------------------------------------------------------ attention
+struct AttnArgs {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* ctx_len;
+    const uint32_t* mask;
+    int B, n1, Hq, Hkv, D, Lmax;
+    float scale;
+    bool bf16;
+    void* out;
+    float* lse;            // may be NULL
+    void* workspace;
+};
+
+size_t attn_workspace_bytes(int B, int n1, int Hq, int Hkv, int D, int Lmax);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace specv

@@ -1,0 +1,201 @@
+/*
+ * specv -- the verify step of speculative decoding on AMD MI355X (gfx950).
+ *
+ * Three operations, each asynchronous on the caller's HIP stream:
+ *
+ *   specv_build_tree_mask   ancestor mask and depth of every draft node, from
+ *                           a parent array;
+ *   specv_tree_attn_verify  the target's attention for all draft nodes in one
+ *                           pass over the KV cache, each node seeing the
+ *                           committed context plus its own ancestors;
+ *   specv_accept_resample   the exact accept / reject / resample rule over the
+ *                           vocabulary, for chains and for trees, greedy at
+ *                           temperature 0.
+ *
+ * Sources (web pages on speculative decoding):
+ *   [SD-review] paper review of Leviathan, Kalman, Matias, "Fast Inference
+ *               from Transformers via Speculative Decoding" (ICML 2023);
+ *   [PTD]       technical summary of "Progressive Tree Drafting (PTD)";
+ *   [SD-EAGLE]  lesson "Speculative Decoding and EAGLE".
+ *
+ * Conventions shared by all calls
+ *   - K is the number of draft nodes; every per-node array has K + 1 rows,
+ *     row 0 being the root (the last committed token), rows 1..K the drafts.
+ *     A chain of K drafts is the parent array {-1, 0, 1, ..., K-1}.
+ *   - Parent arrays are topological: parent[0] = -1 and 0 <= parent[i] < i.
+ *   - All pointers are DEVICE pointers unless stated otherwise, contiguous,
+ *     row-major, 16-byte aligned for the logits / q / k / v / out buffers.
+ *   - The caller owns every buffer, including the workspace (size from the
+ *     *_workspace_bytes queries).  The library allocates nothing, frees
+ *     nothing and never synchronises the stream; it keeps no state between
+ *     calls except the text of the last error of the calling thread.
+ *   - Argument errors are detected on the host and returned before any
+ *     launch; nothing is written then.  Errors that depend on device data
+ *     (a bad parent array, an out-of-range token or context length) are
+ *     reported per sequence in the outputs, as described per call.
+ *   - B == 0 is a valid empty call: SPECV_OK, no launch.
+ *   - Outputs are a pure function of the inputs (and of seed and offset for
+ *     the accept rule): calls replay bit-exactly.
+ */
+#ifndef SPECV_H
+#define SPECV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SPECV_OK = 0,
+    SPECV_ERR_INVALID_ARG = 1,   /* NULL pointer, size out of range, bad temperature, ... */
+    SPECV_ERR_UNSUPPORTED = 2,   /* a head size, dtype or size the kernels do not cover */
+    SPECV_ERR_WORKSPACE = 3,     /* workspace NULL or smaller than the query returns */
+    SPECV_ERR_HIP = 4            /* a kernel launch failed; see specv_last_error() */
+} specv_status;
+
+typedef enum {
+    SPECV_F32 = 0,
+    SPECV_BF16 = 1
+} specv_dtype;
+
+/* Largest supported K + 1 and vocabulary size. */
+#define SPECV_MAX_NODES 1024
+#define SPECV_MAX_VOCAB (1 << 21)
+
+/*
+ * Ancestor mask of a draft tree.
+ *
+ * [SD-EAGLE] "Tree Attention Verification": the verify pass uses a causal
+ * mask that encodes the tree, each node attending only to its ancestors;
+ * [PTD] Method 1, "Attention Masking".  Bit j of row i is set iff j == i or
+ * j is an ancestor of i (the causal diagonal is kept, so a chain gives the
+ * lower-triangular mask).
+ *
+ *   parent       [B][K+1] int32
+ *   mask         [B][K+1][W] uint32, W = (K + 32) / 32 words per row; bit
+ *                (j % 32) of word j / 32 of row i  <=>  j in ancestors(i) u {i}
+ *   depth        [B][K+1] int32, number of ancestors (root 0); position of a
+ *                node in the sequence is ctx_len + depth
+ *   tree_status  [B] int32: 0 if the parent array is valid, else the index of
+ *                the first invalid entry + 1; an invalid sequence gets an
+ *                all-zero mask and depth -1 everywhere.
+ *
+ * Errors: SPECV_ERR_INVALID_ARG for a NULL pointer, B < 0, K < 0 or
+ * K + 1 > SPECV_MAX_NODES.
+ */
+specv_status specv_build_tree_mask(const int32_t* parent, int32_t B, int32_t K,
+                                   uint32_t* mask, int32_t* depth, int32_t* tree_status,
+                                   hipStream_t stream);
+
+/*
+ * Tree-attention verify: one layer's attention for all K + 1 node rows.
+ *
+ * [SD-EAGLE] "Tree Attention Verification": all nodes are verified in one
+ * forward pass with the tree mask; [PTD] Method 4, "Verification";
+ * [SD-review] §2 step 2: the target sees the context and all drafts at once.
+ * For sequence b, node i, query head h (KV head h / (Hq / Hkv)):
+ *   keys  = the context entries 0 .. ctx_len[b]-1 (all visible) and the tree
+ *           entries ctx_len[b] + j for every j with mask bit (i, j) set;
+ *   out   = softmax(scale * q . k) . v over those keys;
+ *   lse   = natural log of the softmax denominator (sum of exp of the scaled
+ *           scores), optional.
+ *
+ *   q        [B][K+1][Hq][D]       dtype
+ *   k_cache  [B][Hkv][Lmax][D]     dtype; node j's own K/V row is at ctx_len[b] + j
+ *   v_cache  [B][Hkv][Lmax][D]     dtype
+ *   ctx_len  [B] int32             committed context length of each sequence
+ *   mask     [B][K+1][W] uint32    from specv_build_tree_mask
+ *   scale    score scale (pass 1/sqrt(D) for the usual attention)
+ *   dtype    SPECV_BF16 (bf16 in, fp32 accumulation, bf16 out) or SPECV_F32
+ *   out      [B][K+1][Hq][D]       dtype
+ *   lse      [B][K+1][Hq] float32, or NULL
+ *   workspace / workspace_bytes: at least specv_attn_workspace_bytes(...)
+ *
+ * A sequence with ctx_len[b] < 0 or ctx_len[b] + K + 1 > Lmax gets NaN in
+ * out and lse (nothing outside the cache is read).
+ * Errors: SPECV_ERR_INVALID_ARG (NULL pointer, sizes <= 0, Hq % Hkv != 0,
+ * K + 1 > SPECV_MAX_NODES, Lmax < K + 1, non-finite scale),
+ * SPECV_ERR_UNSUPPORTED (D not 64 or 128, unknown dtype),
+ * SPECV_ERR_WORKSPACE, SPECV_ERR_HIP.
+ */
+specv_status specv_tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* ctx_len, const uint32_t* mask,
+                                    int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
+                                    int32_t Lmax, float scale, specv_dtype dtype,
+                                    void* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+size_t specv_attn_workspace_bytes(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
+                                  int32_t Lmax);
+
+/*
+ * Exact accept / reject / resample over the vocabulary.
+ *
+ * [SD-EAGLE] "The Exactness Rule" and [SD-review] §2: p = softmax(target / T),
+ * q = softmax(draft / T); a draft x is accepted if u < p(x) / q(x); at the
+ * first rejection a replacement is drawn from (p - q)+ / ||(p - q)+||_1 and the
+ * step stops; if every draft on the path is accepted a bonus token is drawn
+ * from p of the last node.  T == 0 is the greedy rule: accept iff the draft
+ * equals argmax p (lowest token id on ties), otherwise emit argmax p.
+ * Trees ([PTD] Method 4, "Acceptance Logic"): at node v the children are
+ * tested in increasing node index as draws without replacement from q_v; after
+ * a rejection the target becomes the residual and the draft loses the
+ * rejected token (renormalised).  Equivalently, after i rejections the target
+ * is (p - c_i q)+ / R_i with c_0 = 0, R_0 = Q_0 = 1, c_{i+1} = c_i + R_i / Q_i,
+ * Q the draft mass not yet rejected.  A child repeating an earlier sibling's
+ * token is skipped.
+ *
+ *   target_logits [B][K+1][V]  row v is the target's next-token logits after node v
+ *   draft_logits  [B][K+1][V]  row v is the draft distribution that proposed v's
+ *                              children (rows of leaves are not read); may be NULL
+ *                              iff temperature == 0
+ *   logits_dtype  SPECV_F32 or SPECV_BF16 (both logits tensors)
+ *   tokens        [B][K+1] int32; tokens[b][0] is the root token (not read)
+ *   parent        [B][K+1] int32
+ *   temperature   T >= 0, finite
+ *   seed, offset  uniforms: Philox4x64-10 (Salmon et al., SC'11) with key
+ *                 (seed, 0) and counter (node, b, offset, 0); word 0 is the
+ *                 acceptance uniform of that node, word 1 the resampling
+ *                 uniform if the walk ends there; a word w maps to
+ *                 (2 * (w >> 12) + 1) * 2^-53.  Advance offset once per call.
+ *   accept_len    [B] int32: number of accepted draft nodes; -1 if the parent
+ *                 array is invalid or a draft token is outside [0, V)
+ *   out_nodes     [B][K+1] int32: accepted node ids from the first level down,
+ *                 then -1
+ *   out_tokens    [B][K+1] int32: the accepted tokens, then the resampled /
+ *                 bonus / greedy token (accept_len + 1 valid entries), then -1
+ *   p_tok, q_tok  [B][K+1] float32 or NULL: p_parent(v)(tokens[v]) and
+ *                 q_parent(v)(tokens[v]) for every v >= 1; NaN at v == 0, at
+ *                 T == 0 and for invalid sequences
+ *   workspace / workspace_bytes: at least specv_accept_workspace_bytes(...)
+ *
+ * Errors: SPECV_ERR_INVALID_ARG (NULL pointer, B < 0, K < 0,
+ * K + 1 > SPECV_MAX_NODES, V < 1 or V > SPECV_MAX_VOCAB, T < 0 or not finite,
+ * draft NULL with T > 0), SPECV_ERR_UNSUPPORTED (dtype), SPECV_ERR_WORKSPACE,
+ * SPECV_ERR_HIP.
+ */
+specv_status specv_accept_resample(const void* target_logits, const void* draft_logits,
+                                   specv_dtype logits_dtype,
+                                   const int32_t* tokens, const int32_t* parent,
+                                   int32_t B, int32_t K, int32_t V, float temperature,
+                                   uint64_t seed, uint64_t offset,
+                                   int32_t* accept_len, int32_t* out_tokens, int32_t* out_nodes,
+                                   float* p_tok, float* q_tok,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+size_t specv_accept_workspace_bytes(int32_t B, int32_t K, int32_t V, specv_dtype logits_dtype);
+
+/* Static description of a status code. */
+const char* specv_status_string(specv_status s);
+
+/* Text of the last error returned to the calling thread ("" if none). */
+const char* specv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECV_H */

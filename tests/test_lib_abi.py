@@ -1,0 +1,112 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function the header declares,
+and rejects bad arguments on the host before any launch (no GPU needed for these calls)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specv.h")
+LIB = os.path.join(ROOT, "draft_verify_sampling_specv_amd", "libspecv.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libspecv.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(specv_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_operations():
+    names = declared_functions()
+    for n in ("specv_build_tree_mask", "specv_tree_attn_verify", "specv_accept_resample",
+              "specv_accept_workspace_bytes", "specv_attn_workspace_bytes", "specv_status_string",
+              "specv_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(LIB)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+@pytest.fixture(scope="module")
+def specv():
+    import draft_verify_sampling_specv_amd as m
+    return m
+
+
+def test_status_strings(specv):
+    lib = specv.lib
+    assert lib.specv_status_string(0) == b"ok"
+    assert b"invalid" in lib.specv_status_string(1)
+    assert lib.specv_status_string(99) == b"unknown status"
+
+
+def _accept(lib, **kw):
+    args = dict(t=1, d=1, dtype=1, tok=1, par=1, B=2, K=3, V=100, T=1.0, seed=0, off=0,
+                al=1, ot=1, on=1, pt=None, qt=None, ws=1, wsb=1 << 30, stream=None)
+    args.update(kw)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.specv_accept_resample(p(args["t"]), p(args["d"]), args["dtype"], p(args["tok"]), p(args["par"]),
+                                     args["B"], args["K"], args["V"], args["T"], args["seed"], args["off"],
+                                     p(args["al"]), p(args["ot"]), p(args["on"]), p(args["pt"]), p(args["qt"]),
+                                     p(args["ws"]), args["wsb"], args["stream"])
+
+
+def test_accept_host_validation(specv):
+    lib = specv.lib
+    assert _accept(lib, B=-1) == 1
+    assert _accept(lib, K=-1) == 1
+    assert _accept(lib, K=1024) == 1
+    assert _accept(lib, V=0) == 1
+    assert _accept(lib, V=(1 << 21) + 1) == 1
+    assert _accept(lib, T=-0.5) == 1
+    assert _accept(lib, T=float("nan")) == 1
+    assert _accept(lib, T=float("inf")) == 1
+    assert _accept(lib, dtype=7) == 2
+    assert _accept(lib, t=None) == 1
+    assert _accept(lib, d=None, T=1.0) == 1
+    assert _accept(lib, ws=None) == 3
+    assert _accept(lib, wsb=16) == 3
+    assert b"workspace" in lib.specv_last_error()
+    assert _accept(lib, B=0) == 0                      # empty call, no launch
+    assert lib.specv_last_error() == b""
+
+
+def test_workspace_queries(specv):
+    assert specv.accept_workspace_bytes(32, 5, 32000, None) > 0
+    assert specv.lib.specv_accept_workspace_bytes(0, 5, 100, 0) == 0
+    assert specv.attn_workspace_bytes(32, 5, 32, 8, 128, 2054) > 0
+    assert specv.attn_workspace_bytes(32, 5, 32, 8, 96, 2054) == 0
+    assert specv.attn_workspace_bytes(32, 5, 30, 8, 128, 2054) == 0
+
+
+def test_attention_and_mask_host_validation(specv):
+    lib = specv.lib
+    v = ctypes.c_void_p(1)
+
+    def attn(**kw):
+        a = dict(B=2, K=5, Hq=8, Hkv=2, D=128, Lmax=100, scale=0.1, dtype=1, ws=v, wsb=1 << 30)
+        a.update(kw)
+        return lib.specv_tree_attn_verify(v, v, v, v, v, a["B"], a["K"], a["Hq"], a["Hkv"], a["D"], a["Lmax"],
+                                          a["scale"], a["dtype"], v, None, a["ws"], a["wsb"], None)
+
+    assert attn(Hq=7) == 1
+    assert attn(Hkv=0) == 1
+    assert attn(D=96) == 2
+    assert attn(dtype=5) == 2
+    assert attn(Lmax=3) == 1
+    assert attn(scale=float("nan")) == 1
+    assert attn(scale=-1.0) == 1
+    assert attn(K=1024) == 1
+    assert attn(wsb=8) == 3
+    assert attn(B=0) == 0
+    assert lib.specv_build_tree_mask(None, 2, 3, None, None, None, None) == 1
+    assert lib.specv_build_tree_mask(v, -2, 3, v, v, v, None) == 1
+    assert lib.specv_build_tree_mask(v, 2, 1024, v, v, v, None) == 1
+    assert lib.specv_build_tree_mask(None, 0, 3, None, None, None, None) == 0
