@@ -7,19 +7,18 @@
 // replacement from q; after i rejections the target is (p - c_i q)+ / R_i (scalar form, see the
 // walk below).
 //
-// Three launches on the caller's stream:
-//   1. stats  grid (chunk, node, sequence): streams every target row and the draft rows of
-//             internal nodes once, coalesced 16-byte loads, and writes per-chunk softmax
-//             statistics (max, sum of exp) -- or (max, argmax) at T = 0.  This is the HBM-bound
-//             pass; one exp per element.
-//   2. walk   one 1024-thread workgroup per sequence: combines the chunk statistics, computes
-//             p_tok / q_tok, runs the accept walk (all threads execute it in lock-step so that
-//             the rare sibling-rejection passes over a row pair can use the whole workgroup),
-//             and records the end node, the residual coefficient c and the draw uniform.
-//   3. draw   grid (chunk, sequence): sums of the draw weights w(x) = (p(x) - c q(x))+ (c = 0 for
-//             a bonus) per chunk of the end row; the last workgroup of a sequence to finish
-//             (device-scope counter) scans the chunk sums, finds the chunk where the CDF crosses
-//             u * W, and searches it.  Skipped at T = 0.
+// Two launches on the caller's stream:
+//   1. stats   grid (chunk, node, sequence): streams every target row and the draft rows of
+//              internal nodes once, coalesced 16-byte loads, and writes per-chunk softmax
+//              statistics (max, sum of exp) -- or (max, argmax) at T = 0.  This is the HBM-bound
+//              pass; one exp per element.
+//   2. finish  one 1024-thread workgroup per sequence: combines the chunk statistics; computes,
+//              for every draft node in parallel, p and q of its token under its parent's rows,
+//              the ratio p/q and its acceptance uniform; one wave then runs the walk (scalar, from
+//              those tables); the rare sibling-rejection passes R(c) = sum (p - c q)+ over a row
+//              pair and the final draw pass use the whole workgroup.  The draw pass records the
+//              sum of every 64*kVec-element segment in LDS; the segment holding the CDF crossing
+//              is found by a block scan and searched by one wave.
 //
 // Precision: per-element exponentials in fp32 (v_exp_f32), chunk sums in fp32, everything above
 // chunk level (row normalisers, ratios, c, Q, R, the CDF threshold and the chunk prefix) in fp64.
@@ -35,32 +34,20 @@ constexpr int kStatThreads = 256;
 constexpr int kUnroll = 4;
 constexpr int kWalkThreads = 1024;
 constexpr int kWalkWaves = kWalkThreads / kWave;
+constexpr int kMaxVocab = 1 << 21;
 
 template <typename T>
 constexpr int chunk_elems() {
     return kStatThreads * Elem<T>::kVec * kUnroll;   // bf16: 8192, fp32: 4096 (16 KB per row)
 }
 
-struct WalkResult {        // per sequence: what the draw kernel must sample
-    int32_t mode;          // 0: nothing to draw (greedy or invalid sequence); 1: draw
-    int32_t row;           // end node
-    float m_t, m_d;        // raw-logit maxima of the end node's target / draft rows
-    float p_scale;         // 1 / S_t
-    float q_scale;         // c / S_d   (0: bonus, weights are p itself)
-    double u;              // draw uniform
-};
-static_assert(sizeof(WalkResult) == 32, "WalkResult layout");
-
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct AcceptLayout {
-    size_t stats, res, sums, counters, total;
+    size_t stats, total;
     AcceptLayout(int B, int n1, int nchunk) {
         stats = 0;
-        res = align256(stats + sizeof(float4) * size_t(B) * n1 * nchunk);
-        sums = align256(res + sizeof(WalkResult) * size_t(B));
-        counters = align256(sums + sizeof(float) * size_t(B) * nchunk);
-        total = align256(counters + sizeof(uint32_t) * size_t(B));
+        total = align256(stats + sizeof(float4) * size_t(B) * n1 * nchunk);
     }
 };
 
@@ -89,19 +76,6 @@ __device__ __forceinline__ float draw_weight(float zt, float zd, float mt, float
     float p = __builtin_amdgcn_exp2f((zt - mt) * k) * p_scale;
     float q = __builtin_amdgcn_exp2f((zd - md) * k) * q_scale;
     return fmaxf(p - q, 0.0f);
-}
-
-template <int kThreads>
-__device__ double block_sum(double x, double* red) {
-    x = wave_sum(x);
-    const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    __syncthreads();
-    if (lane == 0) red[w] = x;
-    __syncthreads();
-    double s = 0.0;
-#pragma unroll
-    for (int i = 0; i < kThreads / kWave; ++i) s += red[i];
-    return s;
 }
 
 // ------------------------------------------------------------------------------------ 1. stats
@@ -187,44 +161,64 @@ accept_stats_kernel(const T* __restrict__ target, const T* __restrict__ draft,
     }
 }
 
-// ------------------------------------------------------------------------------------ 2. walk
+// ------------------------------------------------------------------------------------ 2. finish
 
-// Sum over the vocabulary of (p(x) - c q(x))+ for row v: the residual mass R(c).  Whole workgroup.
+// Streaming pass over one row pair with the draw weights w(x) = (p(x) - c q(x))+ (c = q_scale S_d;
+// q_scale == 0: w = p).  Tile i covers kWalkThreads * kVec consecutive elements; within a tile
+// wave ww owns the contiguous segment of 64 * kVec elements starting at (ww * 64) * kVec.  The
+// segment sums are written to seg[i * kWalkWaves + ww] (index order) if seg != nullptr.
+// Returns the total (fp64, all threads).
 template <typename T, bool kVecOK>
-__device__ double residual_mass(const T* __restrict__ trow, const T* __restrict__ drow, int V,
-                                float mt, float md, float k, float p_scale, float q_scale,
-                                double* red) {
+__device__ double row_pass(const T* __restrict__ trow, const T* __restrict__ drow, int V, float mt,
+                           float md, float k, float p_scale, float q_scale, float* seg, double* red) {
     constexpr int kVec = Elem<T>::kVec;
-    float acc = 0.f;
-    float zt[kVec], zd[kVec];
-    for (int base = threadIdx.x * kVec; base < V; base += kWalkThreads * kVec) {
-        if (kVecOK) {
+    constexpr int kTile = kWalkThreads * kVec;
+    const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const bool use_q = q_scale != 0.f;
+    double acc = 0.0;
+    const int ntile = (V + kTile - 1) / kTile;
+    for (int i = 0; i < ntile; ++i) {
+        const int base = i * kTile + threadIdx.x * kVec;
+        float zt[kVec], zd[kVec];
+        if (kVecOK && base + kVec <= V) {
             Elem<T>::load_vec(trow, base, zt);
-            Elem<T>::load_vec(drow, base, zd);
+            if (use_q) Elem<T>::load_vec(drow, base, zd);
         } else {
 #pragma unroll
             for (int e = 0; e < kVec; ++e) {
                 zt[e] = (base + e < V) ? Elem<T>::load(trow, base + e) : -INFINITY;
-                zd[e] = (base + e < V) ? Elem<T>::load(drow, base + e) : 0.f;
+                zd[e] = (use_q && base + e < V) ? Elem<T>::load(drow, base + e) : -INFINITY;
             }
         }
+        float sum = 0.f;
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) acc += draw_weight(zt[e], zd[e], mt, md, k, p_scale, q_scale);
+        for (int e = 0; e < kVec; ++e) sum += draw_weight(zt[e], use_q ? zd[e] : -INFINITY, mt, md, k, p_scale, q_scale);
+        sum = wave_sum(sum);
+        if (seg && lane == 0) seg[i * kWalkWaves + w] = sum;
+        acc += sum;
     }
-    return block_sum<kWalkThreads>(static_cast<double>(acc), red);
+    // every lane of a wave holds the same acc: add the wave totals
+    __syncthreads();
+    if (lane == 0) red[w] = acc;
+    __syncthreads();
+    double tot = 0.0;
+#pragma unroll
+    for (int i = 0; i < kWalkWaves; ++i) tot += red[i];
+    return tot;
 }
 
-// Is there a child of v with index in (after, n1)?  Uniform over the wave.
-__device__ __forceinline__ bool has_child_after(const int32_t* par, int n1, int v, int after) {
+// Is there a child of v with index in (after, n1)?  Returns the smallest, or -1.  Wave-uniform.
+__device__ __forceinline__ int next_child(const int32_t* par, int n1, int v, int after) {
     const int lane = threadIdx.x % kWave;
     for (int base = (after + 1) & ~(kWave - 1); base < n1; base += kWave) {
         const int i = base + lane;
-        if (__ballot(i > after && i < n1 && par[i] == v)) return true;
+        const uint64_t m = __ballot(i > after && i < n1 && par[i] == v);
+        if (m) return base + __ffsll(static_cast<unsigned long long>(m)) - 1;
     }
-    return false;
+    return -1;
 }
 
-// Does an earlier sibling (index < ch) of ch carry token x?
+// Does an earlier sibling (index < ch) of ch carry token x?  Wave-uniform.
 __device__ __forceinline__ bool earlier_sibling_has(const int32_t* par, const int32_t* tok, int v,
                                                     int ch, int x) {
     const int lane = threadIdx.x % kWave;
@@ -235,23 +229,47 @@ __device__ __forceinline__ bool earlier_sibling_has(const int32_t* par, const in
     return false;
 }
 
+// Block-wide inclusive scan of one double per thread (thread order); returns the inclusive value.
+__device__ double block_scan(double x, double* red) {
+    const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const double y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    __syncthreads();
+    if (lane == kWave - 1) red[w] = x;
+    __syncthreads();
+    double before = 0.0;
+    for (int i = 0; i < w; ++i) before += red[i];
+    return x + before;
+}
+
 template <typename T, bool kGreedy, bool kVecOK>
 __global__ void __launch_bounds__(kWalkThreads)
-accept_walk_kernel(const T* __restrict__ target, const T* __restrict__ draft,
-                   const int32_t* __restrict__ tokens, const int32_t* __restrict__ parent, int n1,
-                   int V, int nchunk, float k, double invT, uint64_t seed, uint64_t offset,
-                   const float4* __restrict__ stats, WalkResult* __restrict__ res,
-                   uint32_t* __restrict__ counters, int32_t* __restrict__ accept_len,
-                   int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_nodes,
-                   float* __restrict__ p_tok, float* __restrict__ q_tok) {
+accept_finish_kernel(const T* __restrict__ target, const T* __restrict__ draft,
+                     const int32_t* __restrict__ tokens, const int32_t* __restrict__ parent, int n1,
+                     int V, int nchunk, float k, double invT, uint64_t seed, uint64_t offset,
+                     const float4* __restrict__ stats, int32_t* __restrict__ accept_len,
+                     int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_nodes,
+                     float* __restrict__ p_tok, float* __restrict__ q_tok) {
+    constexpr int kVec = Elem<T>::kVec;
+    constexpr int kTile = kWalkThreads * kVec;
+    constexpr int kMaxSeg = (kMaxVocab + kTile - 1) / kTile * kWalkWaves;
     __shared__ int32_t par[kMaxNodes];
     __shared__ int32_t tok[kMaxNodes];
-    __shared__ int32_t haskid[kMaxNodes];
+    __shared__ int32_t haskid[kMaxNodes];   // greedy: argmax token of the row
     __shared__ float Mt[kMaxNodes], Md[kMaxNodes];
     __shared__ double St[kMaxNodes], Sd[kMaxNodes];
-    __shared__ int32_t amax[kMaxNodes];
+    __shared__ double pq[kMaxNodes];        // p(x)/q(x) of node x under its parent's rows
+    __shared__ float qx[kMaxNodes];         // q(x)
+    __shared__ double uacc[kMaxNodes];      // acceptance uniforms
+    __shared__ int32_t path[kMaxNodes];
+    __shared__ float seg[kMaxSeg];
     __shared__ double red[kWalkWaves];
-    __shared__ int bad;
+    __shared__ int s_bad, s_cmd, s_row, s_n, s_sel, s_found;
+    __shared__ float s_ps, s_qs;
+    __shared__ double s_R, s_base, s_thr;
 
     const int b = blockIdx.x;
     const int t = threadIdx.x;
@@ -259,7 +277,7 @@ accept_walk_kernel(const T* __restrict__ target, const T* __restrict__ draft,
     const int64_t seq = static_cast<int64_t>(b) * n1;
 
     // -- stage and validate the parent array and the draft tokens
-    if (t == 0) bad = 0;
+    if (t == 0) s_bad = 0;
     for (int i = t; i < n1; i += kWalkThreads) haskid[i] = 0;
     __syncthreads();
     for (int i = t; i < n1; i += kWalkThreads) {
@@ -268,24 +286,23 @@ accept_walk_kernel(const T* __restrict__ target, const T* __restrict__ draft,
         par[i] = p;
         tok[i] = x;
         const bool ok = (i == 0) ? (p == -1) : (p >= 0 && p < i && x >= 0 && x < V);
-        if (!ok) bad = 1;
+        if (!ok) s_bad = 1;
     }
     __syncthreads();
-    if (bad) {
+    if (s_bad) {
         for (int i = t; i < n1; i += kWalkThreads) {
             out_tokens[seq + i] = -1;
             out_nodes[seq + i] = -1;
             if (p_tok) p_tok[seq + i] = NAN;
             if (q_tok) q_tok[seq + i] = NAN;
         }
-        if (t == 0) {
-            accept_len[b] = -1;
-            res[b].mode = 0;
-        }
+        if (t == 0) accept_len[b] = -1;
         return;
     }
-    for (int i = 1 + t; i < n1; i += kWalkThreads) haskid[par[i]] = 1;
-    __syncthreads();
+    if (!kGreedy) {
+        for (int i = 1 + t; i < n1; i += kWalkThreads) haskid[par[i]] = 1;
+        __syncthreads();
+    }
 
     // -- combine chunk statistics per row (one wave per row, lanes over chunks)
     for (int v = w; v < n1; v += kWalkWaves) {
@@ -294,26 +311,26 @@ accept_walk_kernel(const T* __restrict__ target, const T* __restrict__ draft,
             float bv = -INFINITY;
             int bi = INT_MAX;
             for (int c = lane; c < nchunk; c += kWave) {
-                float4 s = sv[c];
-                argmax_merge(bv, bi, s.x, __float_as_int(s.y));
+                const float4 s4 = sv[c];
+                argmax_merge(bv, bi, s4.x, __float_as_int(s4.y));
             }
             wave_argmax(bv, bi);
-            if (lane == 0) amax[v] = (bi >= 0 && bi < V) ? bi : 0;
+            if (lane == 0) haskid[v] = (bi >= 0 && bi < V) ? bi : 0;
         } else {
             const bool dr = haskid[v] != 0;
             float mt = -INFINITY, md = -INFINITY;
             for (int c = lane; c < nchunk; c += kWave) {
-                float4 s = sv[c];
-                mt = fmaxf(mt, s.x);
-                if (dr) md = fmaxf(md, s.z);
+                const float4 s4 = sv[c];
+                mt = fmaxf(mt, s4.x);
+                if (dr) md = fmaxf(md, s4.z);
             }
             mt = wave_max(mt);
             md = wave_max(md);
             double st = 0.0, sd = 0.0;
             for (int c = lane; c < nchunk; c += kWave) {
-                float4 s = sv[c];
-                if (s.x != -INFINITY) st += static_cast<double>(s.y) * exp2(static_cast<double>((s.x - mt) * k));
-                if (dr && s.z != -INFINITY) sd += static_cast<double>(s.w) * exp2(static_cast<double>((s.z - md) * k));
+                const float4 s4 = sv[c];
+                if (s4.x != -INFINITY) st += static_cast<double>(s4.y) * __builtin_amdgcn_exp2f((s4.x - mt) * k);
+                if (dr && s4.z != -INFINITY) sd += static_cast<double>(s4.w) * __builtin_amdgcn_exp2f((s4.z - md) * k);
             }
             st = wave_sum(st);
             sd = wave_sum(sd);
@@ -325,295 +342,243 @@ accept_walk_kernel(const T* __restrict__ target, const T* __restrict__ draft,
     }
     __syncthreads();
 
-    // -- p_tok / q_tok: target and draft probability of every draft token under its parent's row
-    if (p_tok || q_tok) {
-        for (int v = t; v < n1; v += kWalkThreads) {
-            float pv = NAN, qv = NAN;
-            if (!kGreedy && v > 0) {
-                const int pa = par[v], x = tok[v];
-                const double zt = Elem<T>::load(target + (seq + pa) * V, x);
-                const double zd = Elem<T>::load(draft + (seq + pa) * V, x);
-                pv = static_cast<float>(exp((zt - Mt[pa]) * invT) / St[pa]);
-                qv = static_cast<float>(exp((zd - Md[pa]) * invT) / Sd[pa]);
-            }
-            if (p_tok) p_tok[seq + v] = pv;
-            if (q_tok) q_tok[seq + v] = qv;
+    // -- per draft node: p, q of its token under its parent's rows, the ratio, its uniform
+    for (int v = t; v < n1; v += kWalkThreads) {
+        float pv = NAN, qv = NAN;
+        if (!kGreedy && v > 0) {
+            const int pa = par[v], x = tok[v];
+            const double zt = Elem<T>::load(target + (seq + pa) * V, x);
+            const double zd = Elem<T>::load(draft + (seq + pa) * V, x);
+            const double lp = (zt - Mt[pa]) * invT;
+            const double lq = (zd - Md[pa]) * invT;
+            const double pd = exp(lp) / St[pa];
+            const double qd = exp(lq) / Sd[pa];
+            pq[v] = exp(lp - lq) * (Sd[pa] / St[pa]);
+            qx[v] = static_cast<float>(qd);
+            pv = static_cast<float>(pd);
+            qv = static_cast<float>(qd);
+            const U64x4 rnd = philox4x64_10(static_cast<uint64_t>(v), static_cast<uint64_t>(b), offset, 0, seed, 0);
+            uacc[v] = word_to_uniform(rnd.w[0]);
         }
-    }
-
-    // -- the walk: executed identically by every thread (uniform control flow)
-    int v = 0, n = 0;
-    double cs = 0.0;
-    while (true) {
-        int accepted = -1;
-        if (kGreedy) {
-            const int y = amax[v];
-            for (int base = (v + 1) & ~(kWave - 1); base < n1 && accepted < 0; base += kWave) {
-                const int i = base + lane;
-                const uint64_t m = __ballot(i > v && i < n1 && par[i] == v && tok[i] == y);
-                if (m) accepted = base + __ffsll(static_cast<unsigned long long>(m)) - 1;
-            }
-        } else {
-            cs = 0.0;
-            double R = 1.0, Q = 1.0;
-            const int64_t rv = (seq + v) * V;
-            for (int base = (v + 1) & ~(kWave - 1); base < n1 && accepted < 0; base += kWave) {
-                const int i = base + lane;
-                uint64_t m = __ballot(i > v && i < n1 && par[i] == v);
-                while (m && accepted < 0) {
-                    const int ch = base + __ffsll(static_cast<unsigned long long>(m)) - 1;
-                    m &= m - 1;
-                    const int x = tok[ch];
-                    if (earlier_sibling_has(par, tok, v, ch, x)) continue;
-                    const double zt = Elem<T>::load(target + rv, x);
-                    const double zd = Elem<T>::load(draft + rv, x);
-                    const double lp = (zt - Mt[v]) * invT;
-                    const double lq = (zd - Md[v]) * invT;
-                    const double pq = exp(lp - lq) * (Sd[v] / St[v]);
-                    const double qx = exp(lq) / Sd[v];
-                    const double ratio = fmax(0.0, pq - cs) * Q / R;
-                    const U64x4 rnd = philox4x64_10(static_cast<uint64_t>(ch), static_cast<uint64_t>(b),
-                                                    offset, 0, seed, 0);
-                    if (word_to_uniform(rnd.w[0]) < ratio) {
-                        accepted = ch;
-                        break;
-                    }
-                    // rejection: c <- c + R/Q, Q <- Q - q(x), R <- R(c) if another sibling follows
-                    const double cn = cs + R / Q;
-                    Q -= qx;
-                    if (has_child_after(par, n1, v, ch)) {
-                        const double Rn = residual_mass<T, kVecOK>(
-                            target + rv, draft + rv, V, Mt[v], Md[v], k,
-                            static_cast<float>(1.0 / St[v]), static_cast<float>(cn / Sd[v]), red);
-                        if (Rn > 0.0) {
-                            cs = cn;
-                            R = Rn;
-                        }
-                    } else {
-                        cs = cn;
-                    }
-                }
-            }
-        }
-        if (accepted < 0) break;
-        if (t == 0) {
-            out_nodes[seq + n] = accepted;
-            out_tokens[seq + n] = tok[accepted];
-        }
-        ++n;
-        v = accepted;
-    }
-
-    // -- record the outcome
-    for (int i = n + t; i < n1; i += kWalkThreads) {
-        out_nodes[seq + i] = -1;
-        if (i > n) out_tokens[seq + i] = -1;
-    }
-    if (t == 0) {
-        accept_len[b] = n;
-        if (kGreedy) {
-            out_tokens[seq + n] = amax[v];
-            res[b].mode = 0;
-        } else {
-            const U64x4 rnd = philox4x64_10(static_cast<uint64_t>(v), static_cast<uint64_t>(b),
-                                            offset, 0, seed, 0);
-            WalkResult r;
-            r.mode = 1;
-            r.row = v;
-            r.m_t = Mt[v];
-            r.m_d = (cs > 0.0) ? Md[v] : 0.f;
-            r.p_scale = static_cast<float>(1.0 / St[v]);
-            r.q_scale = (cs > 0.0) ? static_cast<float>(cs / Sd[v]) : 0.f;
-            r.u = word_to_uniform(rnd.w[1]);
-            res[b] = r;
-            counters[b] = 0;
-        }
-    }
-}
-
-// ------------------------------------------------------------------------------------ 3. draw
-
-template <typename T, bool kVecOK>
-__global__ void __launch_bounds__(kStatThreads)
-accept_draw_kernel(const T* __restrict__ target, const T* __restrict__ draft, int n1, int V,
-                   int nchunk, float k, const WalkResult* __restrict__ res,
-                   float* __restrict__ chunk_sums, uint32_t* __restrict__ counters,
-                   const int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tokens) {
-    constexpr int kVec = Elem<T>::kVec;
-    constexpr int CH = chunk_elems<T>();
-    constexpr int kPer = kUnroll * kVec;
-    constexpr int kWaves = kStatThreads / kWave;
-    const int c = blockIdx.x, b = blockIdx.y;
-    const int t = threadIdx.x;
-    const int w = t / kWave, lane = t % kWave;
-    const WalkResult r = res[b];
-    if (r.mode == 0) return;
-
-    const int64_t row = (static_cast<int64_t>(b) * n1 + r.row) * V;
-    const bool use_q = r.q_scale != 0.f;
-    __shared__ double red[kWaves];
-    __shared__ int last;
-
-    {
-        const int lo = c * CH, hi = min(V, lo + CH);
-        float zt[kPer], zd[kPer];
-        load_chunk<T, kVecOK>(target + row, lo, hi, t, zt);
-        if (use_q) load_chunk<T, kVecOK>(draft + row, lo, hi, t, zd);
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < kPer; ++e)
-            acc += draw_weight(zt[e], use_q ? zd[e] : 0.f, r.m_t, r.m_d, k, r.p_scale, r.q_scale);
-        const double s = block_sum<kStatThreads>(static_cast<double>(acc), red);
-        if (t == 0) {
-            chunk_sums[static_cast<int64_t>(b) * nchunk + c] = static_cast<float>(s);
-            __threadfence();
-            last = (atomicAdd(&counters[b], 1u) == static_cast<uint32_t>(nchunk - 1));
-        }
-        __syncthreads();
-        if (!last) return;
-        __threadfence();
-    }
-
-    // ---- the last workgroup of this sequence samples
-    __shared__ float wbuf[CH];
-    __shared__ int sel_chunk;
-    __shared__ double sel_base, thresh;
-    __shared__ int found;
-    const float* sums = chunk_sums + static_cast<int64_t>(b) * nchunk;
-
-    if (w == 0) {
-        // chunk totals: lane l owns a contiguous group of chunks; fp64 inclusive scan over lanes
-        const int g = (nchunk + kWave - 1) / kWave;
-        const int c0 = min(nchunk, lane * g), c1 = min(nchunk, c0 + g);
-        double gs = 0.0;
-        for (int i = c0; i < c1; ++i) gs += __hip_atomic_load(&sums[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        double incl = gs;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const double y = __shfl_up(incl, o);
-            if (lane >= o) incl += y;
-        }
-        const double total = __shfl(incl, kWave - 1);
-        const double tt = r.u * total;
-        const uint64_t m = __ballot(c1 > c0 && incl > tt);
-        int chosen = -1;
-        double base = 0.0;
-        if (total > 0.0) {
-            int L;
-            if (m) {
-                L = __ffsll(static_cast<unsigned long long>(m)) - 1;
-            } else {   // rounding put u*W at or above the total: take the last group with mass
-                const uint64_t nz = __ballot(gs > 0.0);
-                L = 63 - __clzll(static_cast<long long>(nz));
-            }
-            if (lane == L) {
-                double acc = incl - gs;
-                int lastpos = -1;
-                double lastbase = acc;
-                for (int i = c0; i < c1; ++i) {
-                    const double s = __hip_atomic_load(&sums[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    if (s > 0.0) { lastpos = i; lastbase = acc; }
-                    if (acc + s > tt) { chosen = i; base = acc; break; }
-                    acc += s;
-                }
-                if (chosen < 0) { chosen = lastpos; base = lastbase; }
-            }
-            chosen = __shfl(chosen, L);
-            base = __shfl(base, L);
-        }
-        if (lane == 0) {
-            sel_chunk = chosen;
-            sel_base = base;
-            thresh = tt;
-            found = INT_MAX;
-        }
+        if (p_tok) p_tok[seq + v] = pv;
+        if (q_tok) q_tok[seq + v] = qv;
     }
     __syncthreads();
 
-    int y = -1;
-    if (sel_chunk >= 0) {
-        // recompute the weights of the chosen chunk in index order and search it
-        const int lo = sel_chunk * CH, hi = min(V, lo + CH);
-        float zt[kPer], zd[kPer];
-        load_chunk<T, kVecOK>(target + row, lo, hi, t, zt);
-        if (use_q) load_chunk<T, kVecOK>(draft + row, lo, hi, t, zd);
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-            for (int e = 0; e < kVec; ++e) {
-                const int off = (u * kStatThreads + t) * kVec + e;
-                wbuf[off] = draw_weight(zt[u * kVec + e], use_q ? zd[u * kVec + e] : 0.f, r.m_t,
-                                        r.m_d, k, r.p_scale, r.q_scale);
+    // -- the walk, run by wave 0; residual-mass passes (sibling rejections) use the whole block
+    int v = 0, n = 0;
+    double cs = 0.0, R = 1.0, Q = 1.0, pend = 0.0;
+    bool pending = false;
+    int nxt = (w == 0) ? next_child(par, n1, 0, 0) : -1;
+    while (true) {
+        if (w == 0) {
+            if (pending) {
+                const double Rn = s_R;
+                if (Rn > 0.0) { cs = pend; R = Rn; }
+                pending = false;
             }
-        __syncthreads();
-        // thread t scans the contiguous segment [t*kPer, (t+1)*kPer)
-        float seg[kPer];
-        float ssum = 0.f;
-#pragma unroll
-        for (int e = 0; e < kPer; ++e) {
-            seg[e] = wbuf[t * kPer + e];
-            ssum += seg[e];
+            int cmd = -1;   // 0: residual-mass pass, 1: draw at v, 2: greedy end at v
+            while (cmd < 0) {
+                if (kGreedy) {
+                    const int y = haskid[v];
+                    int c = -1;
+                    for (int base = (v + 1) & ~(kWave - 1); base < n1 && c < 0; base += kWave) {
+                        const int i = base + lane;
+                        const uint64_t m = __ballot(i > v && i < n1 && par[i] == v && tok[i] == y);
+                        if (m) c = base + __ffsll(static_cast<unsigned long long>(m)) - 1;
+                    }
+                    if (c < 0) { cmd = 2; break; }
+                    if (lane == 0) path[n] = c;
+                    ++n;
+                    v = c;
+                    continue;
+                }
+                if (nxt < 0) { cmd = 1; break; }
+                const int c = nxt;
+                nxt = next_child(par, n1, v, c);
+                if (earlier_sibling_has(par, tok, v, c, tok[c])) continue;
+                const double ratio = fmax(0.0, pq[c] - cs) * Q / R;
+                if (uacc[c] < ratio) {
+                    if (lane == 0) path[n] = c;
+                    ++n;
+                    v = c;
+                    cs = 0.0; R = 1.0; Q = 1.0;
+                    nxt = next_child(par, n1, v, v);
+                    continue;
+                }
+                const double cn = cs + R / Q;
+                Q -= static_cast<double>(qx[c]);
+                if (nxt >= 0) {
+                    pending = true;
+                    pend = cn;
+                    if (lane == 0) {
+                        s_ps = static_cast<float>(1.0 / St[v]);
+                        s_qs = static_cast<float>(cn / Sd[v]);
+                    }
+                    cmd = 0;
+                } else {
+                    cs = cn;
+                    cmd = 1;
+                }
+            }
+            if (lane == 0) {
+                s_cmd = cmd;
+                s_row = v;
+                s_n = n;
+                if (cmd == 1) {
+                    s_ps = static_cast<float>(1.0 / St[v]);
+                    s_qs = (cs > 0.0) ? static_cast<float>(cs / Sd[v]) : 0.f;
+                }
+            }
         }
-        // exclusive scan of segment sums in thread order (fp64)
-        double incl = ssum;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const double yv = __shfl_up(incl, o);
-            if (lane >= o) incl += yv;
+        __syncthreads();
+        if (s_cmd != 0) break;
+        const int64_t rr = (seq + s_row) * V;
+        const double Rn = row_pass<T, kVecOK>(target + rr, draft + rr, V, Mt[s_row], Md[s_row], k, s_ps,
+                                              s_qs, nullptr, red);
+        if (t == 0) s_R = Rn;
+        __syncthreads();
+    }
+
+    // -- outputs of the walk
+    const int cmd = s_cmd, e = s_row, na = s_n;
+    for (int i = t; i < n1; i += kWalkThreads) {
+        out_nodes[seq + i] = (i < na) ? path[i] : -1;
+        if (i < na) out_tokens[seq + i] = tok[path[i]];
+        else if (i > na) out_tokens[seq + i] = -1;
+    }
+    if (t == 0) accept_len[b] = na;
+    if (cmd == 2) {
+        if (t == 0) out_tokens[seq + na] = haskid[e];
+        return;
+    }
+
+    // -- the draw at node e: w(x) = (p(x) - c q(x))+, smallest x whose CDF exceeds u * W
+    const int64_t rr = (seq + e) * V;
+    const float mt = Mt[e], ps = s_ps, qs = s_qs;
+    const float md = (qs != 0.f) ? Md[e] : 0.f;
+    const double W = row_pass<T, kVecOK>(target + rr, draft + rr, V, mt, md, k, ps, qs, seg, red);
+    const int ntile = (V + kTile - 1) / kTile;
+    const int nseg = ntile * kWalkWaves;
+    if (t == 0) {
+        const U64x4 rnd = philox4x64_10(static_cast<uint64_t>(e), static_cast<uint64_t>(b), offset, 0, seed, 0);
+        s_thr = word_to_uniform(rnd.w[1]) * W;
+        s_sel = -1;
+        s_found = INT_MAX;
+    }
+    __syncthreads();
+    const double thr = s_thr;
+    int y = -1;
+    if (W > 0.0) {
+        // segment search: thread j owns a contiguous group of segments; block scan of group sums
+        const int g = (nseg + kWalkThreads - 1) / kWalkThreads;
+        const int s0 = min(nseg, t * g), s1 = min(nseg, s0 + g);
+        double gs = 0.0;
+        for (int i = s0; i < s1; ++i) gs += seg[i];
+        const double incl = block_scan(gs, red);
+        // the first thread whose running sum passes the threshold owns the crossing
+        if (s1 > s0 && incl > thr) atomicMin(&s_found, t);
+        __syncthreads();
+        if (t == s_found) {
+            double acc = incl - gs;
+            int sel = -1, lastpos = -1;
+            double sb = acc, lastbase = acc;
+            for (int i = s0; i < s1; ++i) {
+                if (seg[i] > 0.f) { lastpos = i; lastbase = acc; }
+                if (acc + seg[i] > thr) { sel = i; sb = acc; break; }
+                acc += seg[i];
+            }
+            if (sel < 0) { sel = lastpos; sb = lastbase; }
+            s_sel = sel;
+            s_base = sb;
         }
         __syncthreads();
-        if (lane == kWave - 1) red[w] = incl;
-        __syncthreads();
-        double before = 0.0;
-        for (int i = 0; i < w; ++i) before += red[i];
-        double acc = sel_base + before + (incl - ssum);
-        int cand = INT_MAX;
-#pragma unroll
-        for (int e = 0; e < kPer; ++e) {
-            acc += seg[e];
-            if (cand == INT_MAX && seg[e] > 0.f && acc > thresh) cand = lo + t * kPer + e;
-        }
-        if (cand != INT_MAX) atomicMin(&found, cand);
-        __syncthreads();
-        y = found;
-        if (y == INT_MAX || y >= hi) {
-            // rounding kept the threshold above this chunk's running sum: last positive element
-            int lastpos = -1;
-            for (int e = kPer - 1; e >= 0; --e)
-                if (seg[e] > 0.f) { lastpos = lo + t * kPer + e; break; }
+        if (t == 0) s_found = INT_MAX;
+        if (s_sel < 0) {
+            // rounding left u * W at or above every running sum: the last segment with mass
+            if (t == 0) {
+                double acc = 0.0;
+                for (int i = 0; i < nseg; ++i) {
+                    if (seg[i] > 0.f) { s_sel = i; s_base = acc; }
+                    acc += seg[i];
+                }
+            }
             __syncthreads();
-            if (t == 0) found = -1;
-            __syncthreads();
-            if (lastpos >= 0 && lastpos < hi) atomicMax(&found, lastpos);
-            __syncthreads();
-            y = found;
         }
+        if (w == 0 && s_sel >= 0) {
+            // re-read the selected segment (same layout and arithmetic as the pass) and search it
+            const int sel = s_sel;
+            const int base = (sel / kWalkWaves) * kTile + ((sel % kWalkWaves) * kWave + lane) * kVec;
+            float zt[kVec], zd[kVec], wt[kVec];
+            if (kVecOK && base + kVec <= V) {
+                Elem<T>::load_vec(target + rr, base, zt);
+                if (qs != 0.f) Elem<T>::load_vec(draft + rr, base, zd);
+            } else {
+#pragma unroll
+                for (int i = 0; i < kVec; ++i) {
+                    zt[i] = (base + i < V) ? Elem<T>::load(target + rr, base + i) : -INFINITY;
+                    zd[i] = (qs != 0.f && base + i < V) ? Elem<T>::load(draft + rr, base + i) : -INFINITY;
+                }
+            }
+            float ls = 0.f;
+#pragma unroll
+            for (int i = 0; i < kVec; ++i) {
+                wt[i] = draw_weight(zt[i], qs != 0.f ? zd[i] : -INFINITY, mt, md, k, ps, qs);
+                ls += wt[i];
+            }
+            double incl2 = ls;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const double yv = __shfl_up(incl2, o);
+                if (lane >= o) incl2 += yv;
+            }
+            double acc = s_base + incl2 - ls;
+            int cand = INT_MAX, lastpos = -1;
+#pragma unroll
+            for (int i = 0; i < kVec; ++i) {
+                acc += wt[i];
+                if (wt[i] > 0.f) {
+                    lastpos = base + i;
+                    if (cand == INT_MAX && acc > thr) cand = base + i;
+                }
+            }
+            const uint64_t hit = __ballot(cand != INT_MAX);
+            if (hit) {
+                const int L = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+                y = __shfl(cand, L);
+            } else {
+                const uint64_t pos = __ballot(lastpos >= 0);
+                if (pos) y = __shfl(lastpos, 63 - __clzll(static_cast<long long>(pos)));
+            }
+            if (lane == 0) s_found = y;
+        }
+        __syncthreads();
+        y = (s_found == INT_MAX) ? -1 : s_found;
     }
     if (y < 0) {
-        // no residual mass at all (a zero-probability event in exact arithmetic): emit the token
-        // with the largest p(x) - c q(x), lowest index on ties
+        // no residual mass at all (a zero-probability event in exact arithmetic): the token with
+        // the largest p(x) - c q(x), lowest index on ties
         float bv = -INFINITY;
         int bi = INT_MAX;
-        for (int base = t; base < V; base += kStatThreads) {
-            const float zt = Elem<T>::load(target + row, base);
-            const float zd = use_q ? Elem<T>::load(draft + row, base) : 0.f;
-            const float d = __builtin_amdgcn_exp2f((zt - r.m_t) * k) * r.p_scale -
-                            __builtin_amdgcn_exp2f((zd - r.m_d) * k) * r.q_scale;
-            argmax_merge(bv, bi, d, base);
+        for (int x = t; x < V; x += kWalkThreads) {
+            const float zt = Elem<T>::load(target + rr, x);
+            const float zd = (qs != 0.f) ? Elem<T>::load(draft + rr, x) : -INFINITY;
+            const float d = __builtin_amdgcn_exp2f((zt - mt) * k) * ps - __builtin_amdgcn_exp2f((zd - md) * k) * qs;
+            argmax_merge(bv, bi, d, x);
         }
         wave_argmax(bv, bi);
-        __shared__ float pv[kWaves];
-        __shared__ int pi[kWaves];
+        __shared__ float pv[kWalkWaves];
+        __shared__ int pi[kWalkWaves];
         if (lane == 0) { pv[w] = bv; pi[w] = bi; }
         __syncthreads();
         if (t == 0) {
-            for (int i = 1; i < kWaves; ++i) argmax_merge(pv[0], pi[0], pv[i], pi[i]);
-            found = (pi[0] >= 0 && pi[0] < V) ? pi[0] : 0;
+            for (int i = 1; i < kWalkWaves; ++i) argmax_merge(pv[0], pi[0], pv[i], pi[i]);
+            s_found = (pi[0] >= 0 && pi[0] < V) ? pi[0] : 0;
         }
         __syncthreads();
-        y = found;
+        y = s_found;
     }
-    if (t == 0) out_tokens[static_cast<int64_t>(b) * n1 + accept_len[b]] = y;
+    if (t == 0) out_tokens[seq + na] = y;
 }
 
 template <typename T, bool kVecOK>
@@ -621,35 +586,26 @@ hipError_t launch_typed(const AcceptArgs& a, hipStream_t stream) {
     constexpr int CH = chunk_elems<T>();
     const int nchunk = (a.V + CH - 1) / CH;
     const AcceptLayout lay(a.B, a.n1, nchunk);
-    char* ws = static_cast<char*>(a.workspace);
-    float4* stats = reinterpret_cast<float4*>(ws + lay.stats);
-    WalkResult* res = reinterpret_cast<WalkResult*>(ws + lay.res);
-    float* sums = reinterpret_cast<float*>(ws + lay.sums);
-    uint32_t* counters = reinterpret_cast<uint32_t*>(ws + lay.counters);
+    float4* stats = reinterpret_cast<float4*>(static_cast<char*>(a.workspace) + lay.stats);
     const T* target = static_cast<const T*>(a.target);
     const T* draft = static_cast<const T*>(a.draft);
     const bool greedy = a.temperature == 0.f;
     const double invT = greedy ? 0.0 : 1.0 / static_cast<double>(a.temperature);
     const float k = greedy ? 0.f : static_cast<float>(1.4426950408889634 * invT);   // log2(e) / T
-
     const dim3 sgrid(nchunk, a.n1, a.B);
     if (greedy) {
         hipLaunchKernelGGL((accept_stats_kernel<T, true, kVecOK>), sgrid, dim3(kStatThreads), 0, stream,
                            target, draft, a.parent, a.n1, a.V, nchunk, k, stats);
-        hipLaunchKernelGGL((accept_walk_kernel<T, true, kVecOK>), dim3(a.B), dim3(kWalkThreads), 0, stream,
-                           target, draft, a.tokens, a.parent, a.n1, a.V, nchunk, k, invT, a.seed,
-                           a.offset, stats, res, counters, a.accept_len, a.out_tokens, a.out_nodes,
-                           a.p_tok, a.q_tok);
-        return hipGetLastError();
+        hipLaunchKernelGGL((accept_finish_kernel<T, true, kVecOK>), dim3(a.B), dim3(kWalkThreads), 0, stream,
+                           target, draft, a.tokens, a.parent, a.n1, a.V, nchunk, k, invT, a.seed, a.offset,
+                           stats, a.accept_len, a.out_tokens, a.out_nodes, a.p_tok, a.q_tok);
+    } else {
+        hipLaunchKernelGGL((accept_stats_kernel<T, false, kVecOK>), sgrid, dim3(kStatThreads), 0, stream,
+                           target, draft, a.parent, a.n1, a.V, nchunk, k, stats);
+        hipLaunchKernelGGL((accept_finish_kernel<T, false, kVecOK>), dim3(a.B), dim3(kWalkThreads), 0, stream,
+                           target, draft, a.tokens, a.parent, a.n1, a.V, nchunk, k, invT, a.seed, a.offset,
+                           stats, a.accept_len, a.out_tokens, a.out_nodes, a.p_tok, a.q_tok);
     }
-    hipLaunchKernelGGL((accept_stats_kernel<T, false, kVecOK>), sgrid, dim3(kStatThreads), 0, stream,
-                       target, draft, a.parent, a.n1, a.V, nchunk, k, stats);
-    hipLaunchKernelGGL((accept_walk_kernel<T, false, kVecOK>), dim3(a.B), dim3(kWalkThreads), 0, stream,
-                       target, draft, a.tokens, a.parent, a.n1, a.V, nchunk, k, invT, a.seed, a.offset,
-                       stats, res, counters, a.accept_len, a.out_tokens, a.out_nodes, a.p_tok, a.q_tok);
-    hipLaunchKernelGGL((accept_draw_kernel<T, kVecOK>), dim3(nchunk, a.B), dim3(kStatThreads), 0, stream,
-                       target, draft, a.n1, a.V, nchunk, k, res, sums, counters, a.accept_len,
-                       a.out_tokens);
     return hipGetLastError();
 }
 
