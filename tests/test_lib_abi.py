@@ -81,7 +81,10 @@ def test_accept_host_validation(specv):
 def test_workspace_queries(specv):
     assert specv.accept_workspace_bytes(32, 5, 32000, None) > 0
     assert specv.lib.specv_accept_workspace_bytes(0, 5, 100, 0) == 0
-    assert specv.attn_workspace_bytes(32, 5, 32, 8, 128, 2054) > 0
+    # many query rows per KV head (tree x GQA group) use split partials and need a workspace;
+    # decode-shaped calls (at most 64 rows per KV head) need none
+    assert specv.attn_workspace_bytes(16, 60, 64, 8, 128, 4157) > 0
+    assert specv.attn_workspace_bytes(32, 5, 32, 8, 128, 2054) == 0
     assert specv.attn_workspace_bytes(32, 5, 32, 8, 96, 2054) == 0
     assert specv.attn_workspace_bytes(32, 5, 30, 8, 128, 2054) == 0
 
@@ -90,8 +93,9 @@ def test_attention_and_mask_host_validation(specv):
     lib = specv.lib
     v = ctypes.c_void_p(1)
 
+    # every call below must be rejected on the host: the pointers are not device memory
     def attn(**kw):
-        a = dict(B=2, K=5, Hq=8, Hkv=2, D=128, Lmax=100, scale=0.1, dtype=1, ws=v, wsb=1 << 30)
+        a = dict(B=2, K=60, Hq=64, Hkv=8, D=128, Lmax=100, scale=0.1, dtype=1, ws=v, wsb=8)
         a.update(kw)
         return lib.specv_tree_attn_verify(v, v, v, v, v, a["B"], a["K"], a["Hq"], a["Hkv"], a["D"], a["Lmax"],
                                           a["scale"], a["dtype"], v, None, a["ws"], a["wsb"], None)
@@ -104,7 +108,8 @@ def test_attention_and_mask_host_validation(specv):
     assert attn(scale=float("nan")) == 1
     assert attn(scale=-1.0) == 1
     assert attn(K=1024) == 1
-    assert attn(wsb=8) == 3
+    assert attn() == 3                                  # workspace too small
+    assert attn(ws=None) == 3
     assert attn(B=0) == 0
     assert lib.specv_build_tree_mask(None, 2, 3, None, None, None, None) == 1
     assert lib.specv_build_tree_mask(v, -2, 3, v, v, v, None) == 1
