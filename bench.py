@@ -36,6 +36,43 @@ ACCEPT_SETS = 24          # 24 x 22.5 MB of logits
 ATTN_SETS = 3             # 3 x 269 MB of KV cache
 
 
+# configurations: accept generator, attention generator, draft positions per sequence, description
+CONFIGS = {
+    "tiny": "tiny oracle case: chain K=4, V=1000 fp32, 10^4 trials; six-node tree attention, 4 heads, D=64, ctx 128, fp32",
+    "chain": "chain B=32, K=5, V=32000 bf16, T=1; attention ctx 2048, 32/8 heads, D=128 bf16",
+    "chain-greedy": "chain B=32, K=5, V=32000 bf16, T=0 (greedy)",
+    "eagle": "EAGLE-style tree B=16, 60 nodes (top-3, depth 6), V=128256 bf16, T=0.7; attention ctx 4096, 64/8 heads, D=128",
+    "stress": "low-acceptance chain B=64, K=8, V=151936 fp32, T=1.5; attention ctx 1024, 40/8 heads, D=128 bf16",
+    "ptd": "PTD-style tree B=4, 64 nodes (<=4 children, depth <=8), V=128256 bf16, T=1; attention ctx 32768, 64/8 heads",
+}
+MFMA_PEAK_TFLOPS = 2500.0
+
+# HBM traffic of the dominant kernel (attn_decode_kernel<128, 8, 1>) per call on this workload, from
+# two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), each scaled by what the same
+# counter reads for a 256 MiB device-to-device copy (FETCH_SIZE 131084.0 KiB -> x1.99982,
+# WRITE_SIZE 262144.0 KiB -> x1.0).  Summaries and commands: profiles/attn_decode_chain_pmc.md.
+# Valid only for the kernel sources it was measured on (their SHA-256 below); null otherwise.
+ATTN_TRAFFIC = {
+    "sources": ["draft_verify_sampling_specv_amd/csrc/attn_decode.hip",
+                "draft_verify_sampling_specv_amd/csrc/attn_common.h",
+                "draft_verify_sampling_specv_amd/csrc/common.h"],
+    "sha256": "3b59d703509c165447b46260e69a4279a854121482dc61a0b13069377b65a6a3",
+    "fetch_kib": 132343.7, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131084.0, "write_scale": 1.0,
+}
+
+
+def attn_traffic_bytes():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_TRAFFIC["sources"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != ATTN_TRAFFIC["sha256"]:
+        return None
+    t = ATTN_TRAFFIC
+    return (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024.0
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -47,6 +84,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline leg")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--config", default=None, choices=sorted(CONFIGS),
+                    help="measure every kernel on one configuration (prints a per-config JSON line "
+                         "instead of the headline line)")
     return ap.parse_args()
 
 
@@ -92,6 +132,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe(torch)
+        return
+    if args.config:
+        measure_config(args.config, args, torch, specv, workloads)
         return
 
     n1 = K + 1
@@ -170,6 +213,14 @@ def main():
                       args.steps)
     ms_mask = timed(lambda i: specv.build_tree_mask(parent, out=mask_out), args.steps)
 
+    # measured streaming ceiling on this machine: device-to-device copy of 1 GiB (read + write bytes)
+    big = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    big2 = torch.empty_like(big)
+    big2.copy_(big)
+    ms_copy = timed(lambda i: big2.copy_(big), 5)
+    copy_gbs = 2 * (1 << 30) / (ms_copy * 1e-3) / 1e9
+    del big, big2
+
     # acceptance statistics of the timed configuration (set 0)
     res = specv.accept_resample(acc_sets[0]["target"], acc_sets[0]["draft"], acc_sets[0]["tokens"], parent, T,
                                 seed=1234, offset=0)
@@ -199,20 +250,126 @@ def main():
                                "(+6 tree keys), 32 q / 8 kv heads, D=128, bf16",
                    "global_batch": B, "seq_len": CTX, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": attn_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "specv_tree_attn_verify (attn_partial + attn_combine)",
+                     "frac": attn_gbs / HBM_PEAK_GBS, "traffic": attn_traffic_bytes(),
+                     "kernel": "attn_decode_kernel<128,8,1> (specv_tree_attn_verify, one launch)",
                      "bytes_per_call": ab, "ms_per_call": ms_attn},
         "roofline_accept": {"bound": "hbm", "achieved": acc_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": acc_gbs / HBM_PEAK_GBS, "bytes_per_call": cb, "ms_per_call": ms_accept,
-                            "kernel": "specv_accept_resample (stats + walk + draw)"},
+                            "kernel": "specv_accept_resample (accept_stats + accept_finish)"},
         "accept_only_positions_per_s": positions / (ms_accept * 1e-3),
         "ms_mask": ms_mask,
         "ms_greedy_accept": ms_greedy,
         "mean_accept_len": mean_len,
+        "hbm_copy_gbs": copy_gbs,
     }
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(acc_sets[0]["w"], a0)
+    print(json.dumps(out))
+
+
+def measure_config(name, args, torch, specv, workloads):
+    """Per-kernel times and roofline fractions of one configuration (inputs resident in HBM)."""
+    t0 = time.time()
+    if name == "tiny":
+        w = workloads.tiny_chain_trials(10_000)
+        a = workloads.tiny_tree_attention()
+    elif name in ("chain", "chain-greedy"):
+        w = workloads.chain_config(T=0.0 if name == "chain-greedy" else 1.0)
+        a = workloads.chain_attention()
+    elif name == "eagle":
+        w = workloads.eagle_config()
+        a = workloads.eagle_attention(w.parent)
+    elif name == "stress":
+        w = workloads.stress_config()
+        a = workloads.stress_attention()
+    else:
+        w = workloads.ptd_config()
+        a = workloads.ptd_attention(w.parent)
+    ldt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    adt = torch.bfloat16 if a.dtype == "bf16" else torch.float32
+    tl = torch.from_numpy(np.ascontiguousarray(w.target_logits)).cuda().to(ldt)
+    dl = torch.from_numpy(np.ascontiguousarray(w.draft_logits)).cuda().to(ldt) if w.T > 0 else None
+    tok = torch.from_numpy(w.tokens).cuda()
+    par = torch.from_numpy(w.parent).cuda()
+    q = torch.from_numpy(a.q).cuda().to(adt)
+    kc = torch.from_numpy(a.k_cache).cuda().to(adt)
+    vc = torch.from_numpy(a.v_cache).cuda().to(adt)
+    cl = torch.from_numpy(a.ctx_len).cuda()
+    apar = torch.from_numpy(a.parent).cuda()
+    # a second resident copy (sequences permuted) when one set fits in the 256 MB Infinity Cache
+    sets_acc = [(tl, dl, tok, par)]
+    acc_bytes = tl.numel() * tl.element_size()
+    if acc_bytes < (512 << 20):
+        for r in range(1, max(2, int((512 << 20) // max(acc_bytes, 1)) + 1)):
+            if r > 24:
+                break
+            perm = torch.roll(torch.arange(w.B, device="cuda"), r)
+            sets_acc.append((tl[perm].contiguous(), None if dl is None else dl[perm].contiguous(), tok[perm].contiguous(),
+                             par[perm].contiguous()))
+    sets_att = [(q, kc, vc)]
+    att_bytes = kc.numel() * kc.element_size() * 2
+    if att_bytes < (512 << 20):
+        for r in range(1, min(24, int((512 << 20) // att_bytes) + 2)):
+            perm = torch.roll(torch.arange(a.q.shape[0], device="cuda"), r)
+            sets_att.append((q[perm].contiguous(), kc[perm].contiguous(), vc[perm].contiguous()))
+    torch.cuda.synchronize()
+    log(f"{name}: inputs ready in {time.time() - t0:.1f} s ({len(sets_acc)} accept sets, {len(sets_att)} attention sets)")
+
+    B, n1 = w.tokens.shape
+    V = w.V
+    mask, _, _ = specv.build_tree_mask(apar)
+    abuf = specv.AttnBuffers.allocate(q, kc)
+    cbuf = specv.AcceptBuffers.allocate(B, n1, V, ldt, "cuda")
+
+    def timed(fn, n):
+        for i in range(3):
+            fn(i)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(n):
+            fn(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n
+
+    steps = max(20, min(args.steps, 200))
+    ms_mask = timed(lambda i: specv.build_tree_mask(apar), steps)
+    ms_attn = timed(lambda i: specv.tree_attn_verify(*sets_att[i % len(sets_att)], cl, mask, a.scale, buffers=abuf),
+                    steps)
+    ms_acc = timed(lambda i: specv.accept_resample(*sets_acc[i % len(sets_acc)], w.T, seed=1, offset=i,
+                                                   buffers=cbuf), steps)
+    r = specv.accept_resample(tl, dl, tok, par, w.T, seed=1, offset=0, buffers=cbuf)
+    accept_len = r.accept_len.cpu().numpy()
+
+    # algorithmic work
+    pa = w.parent
+    internal = sum(len(set(int(x) for x in pa[b, 1:])) for b in range(B))
+    elem = 2 if w.dtype == "bf16" else 4
+    acc_b = (B * n1 + (internal if w.T > 0 else 0)) * V * elem
+    Bq, _, Hq, D = a.q.shape
+    Hkv = a.k_cache.shape[1]
+    esz = 2 if a.dtype == "bf16" else 4
+    keys = int(a.ctx_len.sum()) + Bq * n1
+    att_b = 2 * Hkv * keys * D * esz + 2 * Bq * n1 * Hq * D * esz
+    att_f = 4.0 * Hq * D * sum(int(a.ctx_len[b]) + n1 for b in range(Bq)) * n1
+    positions = B * (n1 - 1)
+    out = {
+        "config": name, "description": CONFIGS[name], "B": B, "nodes": n1, "V": V, "T": w.T,
+        "internal_nodes": internal,
+        "ms_mask": ms_mask, "ms_attention": ms_attn, "ms_accept": ms_acc,
+        "attention": {"bytes": att_b, "flops": att_f, "GBps": att_b / (ms_attn * 1e-3) / 1e9,
+                      "hbm_frac": att_b / (ms_attn * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "TFLOPs": att_f / (ms_attn * 1e-3) / 1e12,
+                      "mfma_frac": att_f / (ms_attn * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS,
+                      "arith_intensity": att_f / att_b},
+        "accept": {"bytes": acc_b, "GBps": acc_b / (ms_acc * 1e-3) / 1e9,
+                   "hbm_frac": acc_b / (ms_acc * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "positions_per_s_accept_only": positions / (ms_acc * 1e-3),
+        "positions_per_s_verify": positions / ((ms_mask + ms_attn + ms_acc) * 1e-3),
+        "mean_tokens_per_step": float(np.mean(accept_len + 1)),
+    }
     print(json.dumps(out))
 
 

@@ -35,6 +35,7 @@ constexpr int kUnroll = 4;
 constexpr int kWalkThreads = 1024;
 constexpr int kWalkWaves = kWalkThreads / kWave;
 constexpr int kMaxVocab = 1 << 21;
+constexpr double kAllDraftBytes = 32.0 * (1 << 20);   // target logits of a call
 
 template <typename T>
 constexpr int chunk_elems() {
@@ -80,7 +81,7 @@ __device__ __forceinline__ float draw_weight(float zt, float zd, float mt, float
 
 // ------------------------------------------------------------------------------------ 1. stats
 
-template <typename T, bool kGreedy, bool kVecOK>
+template <typename T, bool kGreedy, bool kVecOK, bool kAllDraft>
 __global__ void __launch_bounds__(kStatThreads)
 accept_stats_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                     const int32_t* __restrict__ parent, int n1, int V, int nchunk, float k,
@@ -122,11 +123,16 @@ accept_stats_kernel(const T* __restrict__ target, const T* __restrict__ draft,
         return;
     }
 
-    // Draft rows are read only for internal nodes (a leaf's draft row proposes nothing).
-    int found = 0;
-    const int32_t* pb = parent + static_cast<int64_t>(b) * n1;
-    for (int i = v + 1 + t; i < n1; i += kStatThreads) found |= (pb[i] == v);
-    const bool want_draft = __syncthreads_or(found) != 0;
+    // Draft rows are needed only for internal nodes (a leaf's draft row proposes nothing).  Small
+    // calls (kAllDraft) read every draft row instead: one dependent round trip to the parent
+    // array costs more there than the leaf rows' bytes.
+    bool want_draft = true;
+    if (!kAllDraft) {
+        int found = 0;
+        const int32_t* pb = parent + static_cast<int64_t>(b) * n1;
+        for (int i = v + 1 + t; i < n1; i += kStatThreads) found |= (pb[i] == v);
+        want_draft = __syncthreads_or(found) != 0;
+    }
 
     float zd[kUnroll * kVec];
     if (want_draft) load_chunk<T, kVecOK>(draft + row, lo, hi, t, zd);
@@ -166,36 +172,94 @@ accept_stats_kernel(const T* __restrict__ target, const T* __restrict__ draft,
 // Streaming pass over one row pair with the draw weights w(x) = (p(x) - c q(x))+ (c = q_scale S_d;
 // q_scale == 0: w = p).  Tile i covers kWalkThreads * kVec consecutive elements; within a tile
 // wave ww owns the contiguous segment of 64 * kVec elements starting at (ww * 64) * kVec.  The
-// segment sums are written to seg[i * kWalkWaves + ww] (index order) if seg != nullptr.
-// Returns the total (fp64, all threads).
+// segment sums are written to seg[i * kWalkWaves + ww] (index order) if seg != nullptr.  Loads of
+// up to kPassBatch tiles are issued together so that their latencies overlap.
+// Returns the total (fp64, identical in all threads).
+constexpr int kPassBatch = 4;
+
+template <typename T>
+__device__ __forceinline__ void cvt_vec(const uint4& r, float* out);
+template <>
+__device__ __forceinline__ void cvt_vec<float>(const uint4& r, float* out) {
+    out[0] = __uint_as_float(r.x); out[1] = __uint_as_float(r.y);
+    out[2] = __uint_as_float(r.z); out[3] = __uint_as_float(r.w);
+}
+template <>
+__device__ __forceinline__ void cvt_vec<uint16_t>(const uint4& r, float* out) {
+    out[0] = bf16_lo(r.x); out[1] = bf16_hi(r.x); out[2] = bf16_lo(r.y); out[3] = bf16_hi(r.y);
+    out[4] = bf16_lo(r.z); out[5] = bf16_hi(r.z); out[6] = bf16_lo(r.w); out[7] = bf16_hi(r.w);
+}
+
+template <typename T, bool kVecOK>
+__device__ __forceinline__ void load_pair(const T* __restrict__ trow, const T* __restrict__ drow, int V,
+                                          int base, bool use_q, float* zt, float* zd) {
+    constexpr int kVec = Elem<T>::kVec;
+    if (kVecOK && base + kVec <= V) {
+        Elem<T>::load_vec(trow, base, zt);
+        if (use_q) Elem<T>::load_vec(drow, base, zd);
+    } else {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            zt[e] = (base + e < V) ? Elem<T>::load(trow, base + e) : -INFINITY;
+            zd[e] = (use_q && base + e < V) ? Elem<T>::load(drow, base + e) : -INFINITY;
+        }
+    }
+    if (!use_q) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) zd[e] = -INFINITY;
+    }
+}
+
 template <typename T, bool kVecOK>
 __device__ double row_pass(const T* __restrict__ trow, const T* __restrict__ drow, int V, float mt,
-                           float md, float k, float p_scale, float q_scale, float* seg, double* red) {
+                           float md, float k, float p_scale, float q_scale, float* seg, double* red,
+                           uint4 (&rt)[kPassBatch], uint4 (&rd)[kPassBatch]) {
     constexpr int kVec = Elem<T>::kVec;
     constexpr int kTile = kWalkThreads * kVec;
     const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const bool use_q = q_scale != 0.f;
     double acc = 0.0;
     const int ntile = (V + kTile - 1) / kTile;
-    for (int i = 0; i < ntile; ++i) {
-        const int base = i * kTile + threadIdx.x * kVec;
-        float zt[kVec], zd[kVec];
-        if (kVecOK && base + kVec <= V) {
-            Elem<T>::load_vec(trow, base, zt);
-            if (use_q) Elem<T>::load_vec(drow, base, zd);
-        } else {
+    for (int i0 = 0; i0 < ntile; i0 += kPassBatch) {
+        if (kVecOK) {
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) {
-                zt[e] = (base + e < V) ? Elem<T>::load(trow, base + e) : -INFINITY;
-                zd[e] = (use_q && base + e < V) ? Elem<T>::load(drow, base + e) : -INFINITY;
+            for (int j = 0; j < kPassBatch; ++j) {
+                const int base = (i0 + j) * kTile + threadIdx.x * kVec;
+                rt[j] = make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
+                rd[j] = rt[j];
+                if (i0 + j < ntile && base < V) {
+                    rt[j] = *reinterpret_cast<const uint4*>(trow + base);
+                    if (use_q) rd[j] = *reinterpret_cast<const uint4*>(drow + base);
+                }
             }
         }
-        float sum = 0.f;
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) sum += draw_weight(zt[e], use_q ? zd[e] : -INFINITY, mt, md, k, p_scale, q_scale);
-        sum = wave_sum(sum);
-        if (seg && lane == 0) seg[i * kWalkWaves + w] = sum;
-        acc += sum;
+        for (int j = 0; j < kPassBatch; ++j) {
+            if (i0 + j >= ntile) break;
+            const int base = (i0 + j) * kTile + threadIdx.x * kVec;
+            float zt[kVec], zd[kVec];
+            if (kVecOK) {
+                if (base < V) {
+                    cvt_vec<T>(rt[j], zt);
+                    if (use_q) cvt_vec<T>(rd[j], zd);
+                }
+                if (!(base < V) || !use_q) {
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) {
+                        zd[e] = -INFINITY;
+                        if (!(base < V)) zt[e] = -INFINITY;
+                    }
+                }
+            } else {
+                load_pair<T, false>(trow, drow, V, base, use_q, zt, zd);
+            }
+            float sum = 0.f;
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) sum += draw_weight(zt[e], zd[e], mt, md, k, p_scale, q_scale);
+            sum = wave_sum(sum);
+            if (seg && lane == 0) seg[(i0 + j) * kWalkWaves + w] = sum;
+            acc += sum;
+        }
     }
     // every lane of a wave holds the same acc: add the wave totals
     __syncthreads();
@@ -205,44 +269,6 @@ __device__ double row_pass(const T* __restrict__ trow, const T* __restrict__ dro
 #pragma unroll
     for (int i = 0; i < kWalkWaves; ++i) tot += red[i];
     return tot;
-}
-
-// Is there a child of v with index in (after, n1)?  Returns the smallest, or -1.  Wave-uniform.
-__device__ __forceinline__ int next_child(const int32_t* par, int n1, int v, int after) {
-    const int lane = threadIdx.x % kWave;
-    for (int base = (after + 1) & ~(kWave - 1); base < n1; base += kWave) {
-        const int i = base + lane;
-        const uint64_t m = __ballot(i > after && i < n1 && par[i] == v);
-        if (m) return base + __ffsll(static_cast<unsigned long long>(m)) - 1;
-    }
-    return -1;
-}
-
-// Does an earlier sibling (index < ch) of ch carry token x?  Wave-uniform.
-__device__ __forceinline__ bool earlier_sibling_has(const int32_t* par, const int32_t* tok, int v,
-                                                    int ch, int x) {
-    const int lane = threadIdx.x % kWave;
-    for (int base = (v + 1) & ~(kWave - 1); base < ch; base += kWave) {
-        const int i = base + lane;
-        if (__ballot(i > v && i < ch && par[i] == v && tok[i] == x)) return true;
-    }
-    return false;
-}
-
-// Block-wide inclusive scan of one double per thread (thread order); returns the inclusive value.
-__device__ double block_scan(double x, double* red) {
-    const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const double y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
-    __syncthreads();
-    if (lane == kWave - 1) red[w] = x;
-    __syncthreads();
-    double before = 0.0;
-    for (int i = 0; i < w; ++i) before += red[i];
-    return x + before;
 }
 
 template <typename T, bool kGreedy, bool kVecOK>
@@ -258,27 +284,39 @@ accept_finish_kernel(const T* __restrict__ target, const T* __restrict__ draft,
     constexpr int kMaxSeg = (kMaxVocab + kTile - 1) / kTile * kWalkWaves;
     __shared__ int32_t par[kMaxNodes];
     __shared__ int32_t tok[kMaxNodes];
-    __shared__ int32_t haskid[kMaxNodes];   // greedy: argmax token of the row
+    __shared__ int32_t info[kMaxNodes];     // greedy: argmax token of the row; else: has children
+    __shared__ int32_t fch[kMaxNodes];      // first child (n1 if none)
+    __shared__ int32_t nsib[kMaxNodes];     // next sibling (-1 if none)
+    __shared__ int32_t dup[kMaxNodes];      // token repeats an earlier sibling's
     __shared__ float Mt[kMaxNodes], Md[kMaxNodes];
     __shared__ double St[kMaxNodes], Sd[kMaxNodes];
     __shared__ double pq[kMaxNodes];        // p(x)/q(x) of node x under its parent's rows
     __shared__ float qx[kMaxNodes];         // q(x)
     __shared__ double uacc[kMaxNodes];      // acceptance uniforms
+    __shared__ double ures[kMaxNodes];      // draw uniforms
     __shared__ int32_t path[kMaxNodes];
     __shared__ float seg[kMaxSeg];
     __shared__ double red[kWalkWaves];
     __shared__ int s_bad, s_cmd, s_row, s_n, s_sel, s_found;
     __shared__ float s_ps, s_qs;
-    __shared__ double s_R, s_base, s_thr;
+    __shared__ double s_R, s_base;
 
     const int b = blockIdx.x;
     const int t = threadIdx.x;
     const int w = t / kWave, lane = t % kWave;
     const int64_t seq = static_cast<int64_t>(b) * n1;
 
-    // -- stage and validate the parent array and the draft tokens
+    // -- A. issue the independent loads first: the sequence's chunk statistics (staged in LDS when
+    //       they fit), the parent array and the draft tokens; validate
+    __shared__ float4 sst[kWalkThreads];
+    const bool stage = n1 * nchunk <= kWalkThreads;
+    float4 mystat = make_float4(-INFINITY, 0.f, -INFINITY, 0.f);
+    if (stage && t < n1 * nchunk) mystat = stats[seq * nchunk + t];
     if (t == 0) s_bad = 0;
-    for (int i = t; i < n1; i += kWalkThreads) haskid[i] = 0;
+    for (int i = t; i < n1; i += kWalkThreads) {
+        info[i] = 0;
+        fch[i] = n1;
+    }
     __syncthreads();
     for (int i = t; i < n1; i += kWalkThreads) {
         const int p = parent[seq + i];
@@ -288,6 +326,7 @@ accept_finish_kernel(const T* __restrict__ target, const T* __restrict__ draft,
         const bool ok = (i == 0) ? (p == -1) : (p >= 0 && p < i && x >= 0 && x < V);
         if (!ok) s_bad = 1;
     }
+    if (stage) sst[t] = mystat;
     __syncthreads();
     if (s_bad) {
         for (int i = t; i < n1; i += kWalkThreads) {
@@ -299,14 +338,33 @@ accept_finish_kernel(const T* __restrict__ target, const T* __restrict__ draft,
         if (t == 0) accept_len[b] = -1;
         return;
     }
-    if (!kGreedy) {
-        for (int i = 1 + t; i < n1; i += kWalkThreads) haskid[par[i]] = 1;
-        __syncthreads();
-    }
 
-    // -- combine chunk statistics per row (one wave per row, lanes over chunks)
+    // -- B. gather every draft token's logits under its parent's rows (in flight during the
+    //       combine); tree links: first child, next sibling, repeated sibling tokens
+    float gzt = 0.f, gzd = 0.f;
+    if (!kGreedy && t > 0 && t < n1) {
+        const int pa = par[t], x = tok[t];
+        gzt = Elem<T>::load(target + (seq + pa) * V, x);
+        gzd = Elem<T>::load(draft + (seq + pa) * V, x);
+    }
+    for (int c = 1 + t; c < n1; c += kWalkThreads) {
+        const int pa = par[c], x = tok[c];
+        if (!kGreedy) info[pa] = 1;
+        atomicMin(&fch[pa], c);
+        int nx = -1;
+        for (int i = c + 1; i < n1; ++i)
+            if (par[i] == pa) { nx = i; break; }
+        nsib[c] = nx;
+        int d = 0;
+        for (int i = c - 1; i > pa; --i)
+            if (par[i] == pa && tok[i] == x) { d = 1; break; }
+        dup[c] = d;
+    }
+    __syncthreads();
+
+    // -- C. combine chunk statistics per row (one wave per row, lanes over chunks)
     for (int v = w; v < n1; v += kWalkWaves) {
-        const float4* sv = stats + (seq + v) * nchunk;
+        const float4* sv = stage ? sst + v * nchunk : stats + (seq + v) * nchunk;
         if (kGreedy) {
             float bv = -INFINITY;
             int bi = INT_MAX;
@@ -315,9 +373,9 @@ accept_finish_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                 argmax_merge(bv, bi, s4.x, __float_as_int(s4.y));
             }
             wave_argmax(bv, bi);
-            if (lane == 0) haskid[v] = (bi >= 0 && bi < V) ? bi : 0;
+            if (lane == 0) info[v] = (bi >= 0 && bi < V) ? bi : 0;
         } else {
-            const bool dr = haskid[v] != 0;
+            const bool dr = info[v] != 0;
             float mt = -INFINITY, md = -INFINITY;
             for (int c = lane; c < nchunk; c += kWave) {
                 const float4 s4 = sv[c];
@@ -342,105 +400,106 @@ accept_finish_kernel(const T* __restrict__ target, const T* __restrict__ draft,
     }
     __syncthreads();
 
-    // -- per draft node: p, q of its token under its parent's rows, the ratio, its uniform
+    // -- D. per node: p, q of its token under its parent's rows, the ratio, its two uniforms
     for (int v = t; v < n1; v += kWalkThreads) {
         float pv = NAN, qv = NAN;
-        if (!kGreedy && v > 0) {
-            const int pa = par[v], x = tok[v];
-            const double zt = Elem<T>::load(target + (seq + pa) * V, x);
-            const double zd = Elem<T>::load(draft + (seq + pa) * V, x);
-            const double lp = (zt - Mt[pa]) * invT;
-            const double lq = (zd - Md[pa]) * invT;
-            const double pd = exp(lp) / St[pa];
-            const double qd = exp(lq) / Sd[pa];
-            pq[v] = exp(lp - lq) * (Sd[pa] / St[pa]);
-            qx[v] = static_cast<float>(qd);
-            pv = static_cast<float>(pd);
-            qv = static_cast<float>(qd);
+        if (!kGreedy) {
             const U64x4 rnd = philox4x64_10(static_cast<uint64_t>(v), static_cast<uint64_t>(b), offset, 0, seed, 0);
             uacc[v] = word_to_uniform(rnd.w[0]);
+            ures[v] = word_to_uniform(rnd.w[1]);
+            if (v > 0) {
+                const int pa = par[v];
+                const double zt = gzt, zd = gzd;
+                const double lp = (zt - Mt[pa]) * invT;
+                const double lq = (zd - Md[pa]) * invT;
+                const double pd = exp(lp) / St[pa];
+                const double qd = exp(lq) / Sd[pa];
+                pq[v] = exp(lp - lq) * (Sd[pa] / St[pa]);
+                qx[v] = static_cast<float>(qd);
+                pv = static_cast<float>(pd);
+                qv = static_cast<float>(qd);
+            }
         }
         if (p_tok) p_tok[seq + v] = pv;
         if (q_tok) q_tok[seq + v] = qv;
     }
     __syncthreads();
 
-    // -- the walk, run by wave 0; residual-mass passes (sibling rejections) use the whole block
-    int v = 0, n = 0;
-    double cs = 0.0, R = 1.0, Q = 1.0, pend = 0.0;
-    bool pending = false;
-    int nxt = (w == 0) ? next_child(par, n1, 0, 0) : -1;
-    while (true) {
-        if (w == 0) {
-            if (pending) {
-                const double Rn = s_R;
-                if (Rn > 0.0) { cs = pend; R = Rn; }
-                pending = false;
-            }
-            int cmd = -1;   // 0: residual-mass pass, 1: draw at v, 2: greedy end at v
-            while (cmd < 0) {
-                if (kGreedy) {
-                    const int y = haskid[v];
-                    int c = -1;
-                    for (int base = (v + 1) & ~(kWave - 1); base < n1 && c < 0; base += kWave) {
-                        const int i = base + lane;
-                        const uint64_t m = __ballot(i > v && i < n1 && par[i] == v && tok[i] == y);
-                        if (m) c = base + __ffsll(static_cast<unsigned long long>(m)) - 1;
+    // -- E. the walk, run by wave 0; residual-mass passes (sibling rejections) use the whole block
+    uint4 rt[kPassBatch], rd[kPassBatch];
+    {
+        int v = 0, n = 0;
+        double cs = 0.0, R = 1.0, Q = 1.0, pend = 0.0;
+        bool pending = false;
+        int nxt = fch[0] < n1 ? fch[0] : -1;
+        while (true) {
+            if (w == 0) {
+                if (pending) {
+                    const double Rn = s_R;
+                    if (Rn > 0.0) { cs = pend; R = Rn; }
+                    pending = false;
+                }
+                int cmd = -1;   // 0: residual-mass pass, 1: draw at v, 2: greedy end at v
+                while (cmd < 0) {
+                    if (kGreedy) {
+                        const int y = info[v];
+                        int c = fch[v] < n1 ? fch[v] : -1;
+                        while (c >= 0 && tok[c] != y) c = nsib[c];
+                        if (c < 0) { cmd = 2; break; }
+                        if (lane == 0) path[n] = c;
+                        ++n;
+                        v = c;
+                        continue;
                     }
-                    if (c < 0) { cmd = 2; break; }
-                    if (lane == 0) path[n] = c;
-                    ++n;
-                    v = c;
-                    continue;
+                    if (nxt < 0) { cmd = 1; break; }
+                    const int c = nxt;
+                    nxt = nsib[c];
+                    if (dup[c]) continue;
+                    const double ratio = fmax(0.0, pq[c] - cs) * Q / R;
+                    if (uacc[c] < ratio) {
+                        if (lane == 0) path[n] = c;
+                        ++n;
+                        v = c;
+                        cs = 0.0; R = 1.0; Q = 1.0;
+                        nxt = fch[v] < n1 ? fch[v] : -1;
+                        continue;
+                    }
+                    const double cn = cs + R / Q;
+                    Q -= static_cast<double>(qx[c]);
+                    if (nxt >= 0) {
+                        pending = true;
+                        pend = cn;
+                        if (lane == 0) {
+                            s_ps = static_cast<float>(1.0 / St[v]);
+                            s_qs = static_cast<float>(cn / Sd[v]);
+                        }
+                        cmd = 0;
+                    } else {
+                        cs = cn;
+                        cmd = 1;
+                    }
                 }
-                if (nxt < 0) { cmd = 1; break; }
-                const int c = nxt;
-                nxt = next_child(par, n1, v, c);
-                if (earlier_sibling_has(par, tok, v, c, tok[c])) continue;
-                const double ratio = fmax(0.0, pq[c] - cs) * Q / R;
-                if (uacc[c] < ratio) {
-                    if (lane == 0) path[n] = c;
-                    ++n;
-                    v = c;
-                    cs = 0.0; R = 1.0; Q = 1.0;
-                    nxt = next_child(par, n1, v, v);
-                    continue;
-                }
-                const double cn = cs + R / Q;
-                Q -= static_cast<double>(qx[c]);
-                if (nxt >= 0) {
-                    pending = true;
-                    pend = cn;
-                    if (lane == 0) {
+                if (lane == 0) {
+                    s_cmd = cmd;
+                    s_row = v;
+                    s_n = n;
+                    if (cmd == 1) {
                         s_ps = static_cast<float>(1.0 / St[v]);
-                        s_qs = static_cast<float>(cn / Sd[v]);
+                        s_qs = (cs > 0.0) ? static_cast<float>(cs / Sd[v]) : 0.f;
                     }
-                    cmd = 0;
-                } else {
-                    cs = cn;
-                    cmd = 1;
                 }
             }
-            if (lane == 0) {
-                s_cmd = cmd;
-                s_row = v;
-                s_n = n;
-                if (cmd == 1) {
-                    s_ps = static_cast<float>(1.0 / St[v]);
-                    s_qs = (cs > 0.0) ? static_cast<float>(cs / Sd[v]) : 0.f;
-                }
-            }
+            __syncthreads();
+            if (s_cmd != 0) break;
+            const int64_t rr = (seq + s_row) * V;
+            const double Rn = row_pass<T, kVecOK>(target + rr, draft + rr, V, Mt[s_row], Md[s_row], k,
+                                                  s_ps, s_qs, nullptr, red, rt, rd);
+            if (t == 0) s_R = Rn;
+            __syncthreads();
         }
-        __syncthreads();
-        if (s_cmd != 0) break;
-        const int64_t rr = (seq + s_row) * V;
-        const double Rn = row_pass<T, kVecOK>(target + rr, draft + rr, V, Mt[s_row], Md[s_row], k, s_ps,
-                                              s_qs, nullptr, red);
-        if (t == 0) s_R = Rn;
-        __syncthreads();
     }
 
-    // -- outputs of the walk
+    // -- F. outputs of the walk
     const int cmd = s_cmd, e = s_row, na = s_n;
     for (int i = t; i < n1; i += kWalkThreads) {
         out_nodes[seq + i] = (i < na) ? path[i] : -1;
@@ -449,112 +508,128 @@ accept_finish_kernel(const T* __restrict__ target, const T* __restrict__ draft,
     }
     if (t == 0) accept_len[b] = na;
     if (cmd == 2) {
-        if (t == 0) out_tokens[seq + na] = haskid[e];
+        if (t == 0) out_tokens[seq + na] = info[e];
         return;
     }
 
-    // -- the draw at node e: w(x) = (p(x) - c q(x))+, smallest x whose CDF exceeds u * W
+    // -- G. the draw at node e: w(x) = (p(x) - c q(x))+, smallest x whose CDF exceeds u * W
     const int64_t rr = (seq + e) * V;
     const float mt = Mt[e], ps = s_ps, qs = s_qs;
     const float md = (qs != 0.f) ? Md[e] : 0.f;
-    const double W = row_pass<T, kVecOK>(target + rr, draft + rr, V, mt, md, k, ps, qs, seg, red);
+    const double W = row_pass<T, kVecOK>(target + rr, draft + rr, V, mt, md, k, ps, qs, seg, red, rt, rd);
     const int ntile = (V + kTile - 1) / kTile;
     const int nseg = ntile * kWalkWaves;
-    if (t == 0) {
-        const U64x4 rnd = philox4x64_10(static_cast<uint64_t>(e), static_cast<uint64_t>(b), offset, 0, seed, 0);
-        s_thr = word_to_uniform(rnd.w[1]) * W;
-        s_sel = -1;
-        s_found = INT_MAX;
-    }
-    __syncthreads();
-    const double thr = s_thr;
-    int y = -1;
-    if (W > 0.0) {
-        // segment search: thread j owns a contiguous group of segments; block scan of group sums
-        const int g = (nseg + kWalkThreads - 1) / kWalkThreads;
-        const int s0 = min(nseg, t * g), s1 = min(nseg, s0 + g);
-        double gs = 0.0;
-        for (int i = s0; i < s1; ++i) gs += seg[i];
-        const double incl = block_scan(gs, red);
-        // the first thread whose running sum passes the threshold owns the crossing
-        if (s1 > s0 && incl > thr) atomicMin(&s_found, t);
-        __syncthreads();
-        if (t == s_found) {
-            double acc = incl - gs;
-            int sel = -1, lastpos = -1;
-            double sb = acc, lastbase = acc;
-            for (int i = s0; i < s1; ++i) {
-                if (seg[i] > 0.f) { lastpos = i; lastbase = acc; }
-                if (acc + seg[i] > thr) { sel = i; sb = acc; break; }
-                acc += seg[i];
-            }
-            if (sel < 0) { sel = lastpos; sb = lastbase; }
-            s_sel = sel;
-            s_base = sb;
-        }
-        __syncthreads();
-        if (t == 0) s_found = INT_MAX;
-        if (s_sel < 0) {
-            // rounding left u * W at or above every running sum: the last segment with mass
-            if (t == 0) {
-                double acc = 0.0;
-                for (int i = 0; i < nseg; ++i) {
-                    if (seg[i] > 0.f) { s_sel = i; s_base = acc; }
-                    acc += seg[i];
-                }
-            }
-            __syncthreads();
-        }
-        if (w == 0 && s_sel >= 0) {
-            // re-read the selected segment (same layout and arithmetic as the pass) and search it
-            const int sel = s_sel;
-            const int base = (sel / kWalkWaves) * kTile + ((sel % kWalkWaves) * kWave + lane) * kVec;
-            float zt[kVec], zd[kVec], wt[kVec];
-            if (kVecOK && base + kVec <= V) {
-                Elem<T>::load_vec(target + rr, base, zt);
-                if (qs != 0.f) Elem<T>::load_vec(draft + rr, base, zd);
-            } else {
-#pragma unroll
-                for (int i = 0; i < kVec; ++i) {
-                    zt[i] = (base + i < V) ? Elem<T>::load(target + rr, base + i) : -INFINITY;
-                    zd[i] = (qs != 0.f && base + i < V) ? Elem<T>::load(draft + rr, base + i) : -INFINITY;
-                }
-            }
-            float ls = 0.f;
-#pragma unroll
-            for (int i = 0; i < kVec; ++i) {
-                wt[i] = draw_weight(zt[i], qs != 0.f ? zd[i] : -INFINITY, mt, md, k, ps, qs);
-                ls += wt[i];
-            }
-            double incl2 = ls;
+    const double thr = ures[e] * W;
+
+    // -- H. wave 0 finds the segment holding the crossing (lane l owns a contiguous group)
+    if (w == 0) {
+        int sel = -1;
+        double base = 0.0;
+        if (W > 0.0) {
+            const int g = (nseg + kWave - 1) / kWave;
+            const int s0 = min(nseg, lane * g), s1 = min(nseg, s0 + g);
+            double gs = 0.0;
+            for (int i = s0; i < s1; ++i) gs += seg[i];
+            double incl = gs;
 #pragma unroll
             for (int o = 1; o < kWave; o <<= 1) {
-                const double yv = __shfl_up(incl2, o);
-                if (lane >= o) incl2 += yv;
+                const double yv = __shfl_up(incl, o);
+                if (lane >= o) incl += yv;
             }
-            double acc = s_base + incl2 - ls;
-            int cand = INT_MAX, lastpos = -1;
+            const uint64_t hit = __ballot(s1 > s0 && incl > thr);
+            int L;
+            bool crossing;
+            if (hit) {
+                L = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+                crossing = true;
+            } else {   // rounding left u * W at or above every running sum: last group with mass
+                const uint64_t nz = __ballot(gs > 0.0);
+                L = nz ? 63 - __clzll(static_cast<long long>(nz)) : -1;
+                crossing = false;
+            }
+            if (L >= 0 && lane == L) {
+                double acc = incl - gs;
+                int lastpos = -1;
+                double lastbase = acc;
+                for (int i = s0; i < s1; ++i) {
+                    if (seg[i] > 0.f) { lastpos = i; lastbase = acc; }
+                    if (crossing && acc + seg[i] > thr) { sel = i; base = acc; break; }
+                    acc += seg[i];
+                }
+                if (sel < 0) { sel = lastpos; base = lastbase; }
+            }
+            if (L >= 0) {
+                sel = __shfl(sel, L);
+                base = __shfl(base, L);
+            }
+        }
+        if (lane == 0) {
+            s_sel = sel;
+            s_base = base;
+            s_found = -1;
+        }
+    }
+    __syncthreads();
+
+    // -- I. the wave owning the segment searches it, from registers when the whole row was held
+    const int sel = s_sel;
+    if (sel >= 0 && w == sel % kWalkWaves) {
+        const int tile = sel / kWalkWaves;
+        const int base = tile * kTile + (w * kWave + lane) * kVec;
+        float zt[kVec], zd[kVec], wt[kVec];
+        if (kVecOK && ntile <= kPassBatch) {
+            uint4 a = rt[0], c = rd[0];
 #pragma unroll
-            for (int i = 0; i < kVec; ++i) {
-                acc += wt[i];
-                if (wt[i] > 0.f) {
-                    lastpos = base + i;
-                    if (cand == INT_MAX && acc > thr) cand = base + i;
+            for (int j = 1; j < kPassBatch; ++j)
+                if (j == tile) { a = rt[j]; c = rd[j]; }
+            if (base < V) {
+                cvt_vec<T>(a, zt);
+                cvt_vec<T>(c, zd);
+            }
+            if (!(base < V) || qs == 0.f) {
+#pragma unroll
+                for (int i = 0; i < kVec; ++i) {
+                    zd[i] = -INFINITY;
+                    if (!(base < V)) zt[i] = -INFINITY;
                 }
             }
-            const uint64_t hit = __ballot(cand != INT_MAX);
-            if (hit) {
-                const int L = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-                y = __shfl(cand, L);
-            } else {
-                const uint64_t pos = __ballot(lastpos >= 0);
-                if (pos) y = __shfl(lastpos, 63 - __clzll(static_cast<long long>(pos)));
-            }
-            if (lane == 0) s_found = y;
+        } else {
+            load_pair<T, kVecOK>(target + rr, draft + rr, V, base, qs != 0.f, zt, zd);
         }
-        __syncthreads();
-        y = (s_found == INT_MAX) ? -1 : s_found;
+        float ls = 0.f;
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) {
+            wt[i] = draw_weight(zt[i], zd[i], mt, md, k, ps, qs);
+            ls += wt[i];
+        }
+        double incl2 = ls;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const double yv = __shfl_up(incl2, o);
+            if (lane >= o) incl2 += yv;
+        }
+        double acc = s_base + incl2 - ls;
+        int cand = INT_MAX, lastpos = -1;
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) {
+            acc += wt[i];
+            if (wt[i] > 0.f) {
+                lastpos = base + i;
+                if (cand == INT_MAX && acc > thr) cand = base + i;
+            }
+        }
+        int y = -1;
+        const uint64_t hit = __ballot(cand != INT_MAX);
+        if (hit) {
+            y = __shfl(cand, __ffsll(static_cast<unsigned long long>(hit)) - 1);
+        } else {
+            const uint64_t pos = __ballot(lastpos >= 0);
+            if (pos) y = __shfl(lastpos, 63 - __clzll(static_cast<long long>(pos)));
+        }
+        if (lane == 0) s_found = y;
     }
+    __syncthreads();
+    int y = s_found;
     if (y < 0) {
         // no residual mass at all (a zero-probability event in exact arithmetic): the token with
         // the largest p(x) - c q(x), lowest index on ties
@@ -593,15 +668,20 @@ hipError_t launch_typed(const AcceptArgs& a, hipStream_t stream) {
     const double invT = greedy ? 0.0 : 1.0 / static_cast<double>(a.temperature);
     const float k = greedy ? 0.f : static_cast<float>(1.4426950408889634 * invT);   // log2(e) / T
     const dim3 sgrid(nchunk, a.n1, a.B);
+    const bool all_draft = static_cast<double>(a.B) * a.n1 * a.V * sizeof(T) <= kAllDraftBytes;
     if (greedy) {
-        hipLaunchKernelGGL((accept_stats_kernel<T, true, kVecOK>), sgrid, dim3(kStatThreads), 0, stream,
+        hipLaunchKernelGGL((accept_stats_kernel<T, true, kVecOK, false>), sgrid, dim3(kStatThreads), 0, stream,
                            target, draft, a.parent, a.n1, a.V, nchunk, k, stats);
         hipLaunchKernelGGL((accept_finish_kernel<T, true, kVecOK>), dim3(a.B), dim3(kWalkThreads), 0, stream,
                            target, draft, a.tokens, a.parent, a.n1, a.V, nchunk, k, invT, a.seed, a.offset,
                            stats, a.accept_len, a.out_tokens, a.out_nodes, a.p_tok, a.q_tok);
     } else {
-        hipLaunchKernelGGL((accept_stats_kernel<T, false, kVecOK>), sgrid, dim3(kStatThreads), 0, stream,
-                           target, draft, a.parent, a.n1, a.V, nchunk, k, stats);
+        if (all_draft)
+            hipLaunchKernelGGL((accept_stats_kernel<T, false, kVecOK, true>), sgrid, dim3(kStatThreads), 0,
+                               stream, target, draft, a.parent, a.n1, a.V, nchunk, k, stats);
+        else
+            hipLaunchKernelGGL((accept_stats_kernel<T, false, kVecOK, false>), sgrid, dim3(kStatThreads), 0,
+                               stream, target, draft, a.parent, a.n1, a.V, nchunk, k, stats);
         hipLaunchKernelGGL((accept_finish_kernel<T, false, kVecOK>), dim3(a.B), dim3(kWalkThreads), 0, stream,
                            target, draft, a.tokens, a.parent, a.n1, a.V, nchunk, k, invT, a.seed, a.offset,
                            stats, a.accept_len, a.out_tokens, a.out_nodes, a.p_tok, a.q_tok);

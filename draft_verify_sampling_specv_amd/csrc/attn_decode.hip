@@ -1,0 +1,276 @@
+// Tree-attention verify, decode-shaped case: at most two 32-row blocks of queries per KV head
+// ([SD-EAGLE] "Tree Attention Verification"; [PTD] Method 4, "Verification").  See the comment
+// on attn_decode_kernel for the design.
+
+#include "attn_common.h"
+#include "kernels.h"
+
+namespace specv {
+namespace {
+using namespace attn;
+
+// ------------------------------------------------------------------------------------------
+// Decode-shaped case (at most two 32-row blocks per KV head, e.g. chains with small G): the
+// workgroup owns one (sequence, KV head); its KS waves split the key tiles round-robin, each wave
+// computing all RBW row blocks for its tiles, and the waves' partial softmax states are merged
+// through LDS at the end, so the final output is written directly (no partials in HBM).
+//   * K goes straight from HBM into MFMA A-operand registers (16-byte loads; lane (c, h) reads key
+//     c of the tile, features 16 ks + 8 h .. +8).
+//   * V^T operands are built without a transpose: the O^T rows (feature index) are permuted so that
+//     MFMA block 2 dh holds the even features 64 dh + 2 i and block 2 dh + 1 the odd ones; a lane's
+//     4-byte load of V[key][64 dh + 2 c .. +2] then feeds both blocks (low / high halves).
+//   * The next tile's K and V words are prefetched into registers while the current tile runs.
+
+template <int D, int KS, int RBW>
+__global__ void __launch_bounds__(KS * kWave)
+attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+                   const uint16_t* __restrict__ vc, const int32_t* __restrict__ ctx_len,
+                   const uint32_t* __restrict__ mask, int n1, int Hq, int Hkv, int Lmax, float c2,
+                   uint16_t* __restrict__ out, float* __restrict__ lse) {
+    constexpr int kKS = D / 16;        // k-steps of S^T = K Q^T
+    constexpr int kDH = D / 64;        // 64-feature halves: MFMA blocks 2 dh (even) and 2 dh + 1 (odd)
+    constexpr int kDB = D / 32;
+    extern __shared__ float xs[];      // merge buffer: (KS / 2) x RBW x kDB x 16 x 64 floats + m, l
+    __shared__ uint4 sq[RBW][kKS][kWave];   // Q^T operands of the workgroup's row blocks
+
+    const int kv = blockIdx.y, b = blockIdx.z;
+    const int G = Hq / Hkv, R = G * n1;
+    const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int h = lane / 32, col = lane % 32;
+    const int words = (n1 + 31) >> 5;
+    const int L = ctx_len[b];
+    const bool seq_ok = L >= 0 && L + n1 <= Lmax;
+    const int Ltot = L + n1;
+    const int ntiles = seq_ok ? (Ltot + kTileKeys - 1) / kTileKeys : 0;
+
+    int rows[RBW];
+    bool rok[RBW];
+    const uint32_t* mrow[RBW];
+#pragma unroll
+    for (int j = 0; j < RBW; ++j) {
+        rows[j] = (blockIdx.x * RBW + j) * 32 + col;
+        rok[j] = rows[j] < R;
+        const int node = rok[j] ? rows[j] / G : 0;
+        mrow[j] = mask + (static_cast<int64_t>(b) * n1 + node) * words;
+    }
+    // stage Q^T operands: entry (j, s, lane) = Q[row j*32 + col][16 s + 8 h .. +8]
+    for (int e = threadIdx.x; e < RBW * kKS * kWave; e += KS * kWave) {
+        const int j = e / (kKS * kWave), s2 = (e / kWave) % kKS, ln = e % kWave;
+        const int row = (blockIdx.x * RBW + j) * 32 + ln % 32;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (row < R) {
+            const int node = row / G, g = row - node * G;
+            v = *reinterpret_cast<const uint4*>(q + ((static_cast<int64_t>(b) * n1 + node) * Hq + kv * G + g) * D +
+                                                16 * s2 + 8 * (ln / 32));
+        }
+        sq[j][s2][ln] = v;
+    }
+    __syncthreads();
+
+    const uint16_t* kbase = kc + (static_cast<int64_t>(b) * Hkv + kv) * Lmax * D;
+    const uint16_t* vbase = vc + (static_cast<int64_t>(b) * Hkv + kv) * Lmax * D;
+
+    uint4 kn[kKS];
+    auto load_k = [&](int t) {
+        const int kkey = t * kTileKeys + col;
+#pragma unroll
+        for (int s2 = 0; s2 < kKS; ++s2)
+            kn[s2] = (kkey < Ltot) ? *reinterpret_cast<const uint4*>(kbase + static_cast<int64_t>(kkey) * D + 16 * s2 + 8 * h)
+                                   : make_uint4(0, 0, 0, 0);
+    };
+
+    f32x16_t o[RBW][kDB];
+    float m[RBW], l[RBW];
+#pragma unroll
+    for (int j = 0; j < RBW; ++j) {
+        m[j] = -INFINITY;
+        l[j] = 0.f;
+#pragma unroll
+        for (int i = 0; i < kDB; ++i) o[j][i] = f32x16_t{};
+    }
+
+    if (w < ntiles) load_k(w);
+    for (int t = w; t < ntiles; t += KS) {
+        const int kb = t * kTileKeys;
+        uint4 kcur[kKS];
+#pragma unroll
+        for (int s2 = 0; s2 < kKS; ++s2) kcur[s2] = kn[s2];
+        // this tile's V words (consumed after the softmax), then the next tile's K
+        uint32_t vr[2][kDH][8];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int key = kb + 16 * ks + 8 * (e / 4) + 4 * h + (e % 4);
+#pragma unroll
+                for (int dh = 0; dh < kDH; ++dh)
+                    vr[ks][dh][e] = (key < Ltot)
+                        ? *reinterpret_cast<const uint32_t*>(vbase + static_cast<int64_t>(key) * D + 64 * dh + 2 * col)
+                        : 0u;
+            }
+        if (t + KS < ntiles) load_k(t + KS);
+
+        bf16x8_t pb[RBW][2];
+#pragma unroll
+        for (int j = 0; j < RBW; ++j) {
+            f32x16_t s = f32x16_t{};
+#pragma unroll
+            for (int ks = 0; ks < kKS; ++ks)
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kcur[ks]), as_bf16x8(sq[j][ks][lane]), s, 0, 0, 0);
+            if (kb + kTileKeys > L) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kb + 8 * (r / 4) + 4 * h + (r % 4);
+                    bool vis = key < L;
+                    if (!vis && key < Ltot) {
+                        const int jj = key - L;
+                        vis = (mrow[j][jj >> 5] >> (jj & 31)) & 1u;
+                    }
+                    if (!vis) s[r] = -INFINITY;
+                }
+            }
+            float mx = s[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mnew = fmaxf(m[j], mx * c2);
+            const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+            const float alpha = __builtin_amdgcn_exp2f(m[j] - mref);
+            float rs = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -mref));
+                rs += s[r];
+            }
+            rs += __shfl_xor(rs, 32);
+            l[j] = l[j] * alpha + rs;
+            m[j] = mnew;
+            if (__ballot(alpha != 1.f)) {
+#pragma unroll
+                for (int i = 0; i < kDB; ++i) o[j][i] *= alpha;
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                uint4 pw;
+                pw.x = pack_bf16x2(s[8 * ks + 0], s[8 * ks + 1]);
+                pw.y = pack_bf16x2(s[8 * ks + 2], s[8 * ks + 3]);
+                pw.z = pack_bf16x2(s[8 * ks + 4], s[8 * ks + 5]);
+                pw.w = pack_bf16x2(s[8 * ks + 6], s[8 * ks + 7]);
+                pb[j][ks] = as_bf16x8(pw);
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int dh = 0; dh < kDH; ++dh) {
+                const uint32_t* x = vr[ks][dh];
+                uint4 ev, od;
+                ev.x = (x[0] & 0xffffu) | (x[1] << 16);
+                ev.y = (x[2] & 0xffffu) | (x[3] << 16);
+                ev.z = (x[4] & 0xffffu) | (x[5] << 16);
+                ev.w = (x[6] & 0xffffu) | (x[7] << 16);
+                od.x = (x[0] >> 16) | (x[1] & 0xffff0000u);
+                od.y = (x[2] >> 16) | (x[3] & 0xffff0000u);
+                od.z = (x[4] >> 16) | (x[5] & 0xffff0000u);
+                od.w = (x[6] >> 16) | (x[7] & 0xffff0000u);
+#pragma unroll
+                for (int j = 0; j < RBW; ++j) {
+                    o[j][2 * dh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ev), pb[j][ks], o[j][2 * dh], 0, 0, 0);
+                    o[j][2 * dh + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(od), pb[j][ks], o[j][2 * dh + 1], 0, 0, 0);
+                }
+            }
+    }
+
+    // ---- merge the KS waves' states: halving tree through LDS
+    constexpr int kRegs = RBW * kDB * 16;
+    float* ml = xs + (KS / 2) * kRegs * kWave;
+    for (int half = KS / 2; half >= 1; half /= 2) {
+        if (w >= half && w < 2 * half) {
+            float* dst = xs + (w - half) * kRegs * kWave;
+#pragma unroll
+            for (int j = 0; j < RBW; ++j) {
+#pragma unroll
+                for (int i = 0; i < kDB; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) dst[((j * kDB + i) * 16 + r) * kWave + lane] = o[j][i][r];
+                ml[((w - half) * RBW + j) * 2 * kWave + lane] = m[j];
+                ml[((w - half) * RBW + j) * 2 * kWave + kWave + lane] = l[j];
+            }
+        }
+        __syncthreads();
+        if (w < half) {
+            const float* src = xs + w * kRegs * kWave;
+#pragma unroll
+            for (int j = 0; j < RBW; ++j) {
+                const float m2 = ml[(w * RBW + j) * 2 * kWave + lane];
+                const float l2 = ml[(w * RBW + j) * 2 * kWave + kWave + lane];
+                const float M = fmaxf(m[j], m2);
+                const float a1 = (m[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[j] - M);
+                const float a2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
+#pragma unroll
+                for (int i = 0; i < kDB; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        o[j][i][r] = a1 * o[j][i][r] + a2 * src[((j * kDB + i) * 16 + r) * kWave + lane];
+                l[j] = a1 * l[j] + a2 * l2;
+                m[j] = M;
+            }
+        }
+        __syncthreads();
+    }
+
+    if (w == 0) {
+#pragma unroll
+        for (int j = 0; j < RBW; ++j) {
+            if (!rok[j]) continue;
+            const int node = rows[j] / G, g = rows[j] - (rows[j] / G) * G;
+            const int64_t orow = (static_cast<int64_t>(b) * n1 + node) * Hq + kv * G + g;
+            uint16_t* op = out + orow * D;
+            const float inv = seq_ok ? 1.f / l[j] : NAN;
+#pragma unroll
+            for (int dh = 0; dh < kDH; ++dh)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    // registers 4 rr .. 4 rr + 3 hold feature slots i = 8 rr + 4 h + 0..3, i.e.
+                    // features 64 dh + 2 i (even block) and 64 dh + 2 i + 1 (odd block)
+                    uint4 st;
+                    st.x = pack_bf16x2(o[j][2 * dh][4 * rr + 0] * inv, o[j][2 * dh + 1][4 * rr + 0] * inv);
+                    st.y = pack_bf16x2(o[j][2 * dh][4 * rr + 1] * inv, o[j][2 * dh + 1][4 * rr + 1] * inv);
+                    st.z = pack_bf16x2(o[j][2 * dh][4 * rr + 2] * inv, o[j][2 * dh + 1][4 * rr + 2] * inv);
+                    st.w = pack_bf16x2(o[j][2 * dh][4 * rr + 3] * inv, o[j][2 * dh + 1][4 * rr + 3] * inv);
+                    *reinterpret_cast<uint4*>(op + 64 * dh + 2 * (8 * rr + 4 * h)) = st;
+                }
+            if (lse && h == 0) lse[orow] = seq_ok ? (m[j] + log2f(l[j])) * kLn2 : NAN;
+        }
+    }
+}
+
+template <int D, int KS, int RBW>
+void launch_decode(const AttnArgs& a, dim3 grid, hipStream_t stream) {
+    const size_t lds = sizeof(float) * (size_t(KS / 2) * RBW * (D / 32) * 16 * kWave + size_t(KS / 2) * RBW * 2 * kWave);
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&attn_decode_kernel<D, KS, RBW>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    (void)attr;
+    hipLaunchKernelGGL((attn_decode_kernel<D, KS, RBW>), grid, dim3(KS * kWave), lds, stream,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_cache),
+                       static_cast<const uint16_t*>(a.v_cache), a.ctx_len, a.mask, a.n1, a.Hq, a.Hkv,
+                       a.Lmax, a.scale * kLog2e, static_cast<uint16_t*>(a.out), a.lse);
+}
+
+}  // namespace
+
+hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t stream) {
+    const int RB = ((a.Hq / a.Hkv) * a.n1 + 31) / 32;
+    const dim3 grid(1, a.Hkv, a.B);
+    if (a.D == 64) {
+        if (RB == 1) launch_decode<64, 8, 1>(a, grid, stream);
+        else launch_decode<64, 4, 2>(a, grid, stream);
+    } else {
+        if (RB == 1) launch_decode<128, 8, 1>(a, grid, stream);
+        else launch_decode<128, 4, 2>(a, grid, stream);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace specv

@@ -52,4 +52,10 @@ struct AttnArgs {
 size_t attn_workspace_bytes(int B, int n1, int Hq, int Hkv, int D, int Lmax);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
 
+// the three paths behind launch_attention
+size_t attn_tree_workspace_bytes(int B, int n1, int Hq, int Hkv, int D, int Lmax);
+hipError_t launch_attn_tree(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
+
 }  // namespace specv
