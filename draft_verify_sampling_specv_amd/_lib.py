@@ -12,7 +12,7 @@ library_path = os.path.join(_HERE, "libspecv.so")
 
 if not os.path.exists(library_path):
     raise ImportError(
-        f"{library_path} is missing: build it with `python -m draft_verify_sampling_specv_amd.build` "
+        f"{library_path} is missing: build it with `python draft_verify_sampling_specv_amd/build.py` "
         "(the verify step has no CPU fallback)")
 
 lib = ctypes.CDLL(library_path)

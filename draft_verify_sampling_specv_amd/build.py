@@ -1,6 +1,6 @@
 """Build libspecv.so (HIP, gfx950) in-tree.
 
-    python -m draft_verify_sampling_specv_amd.build
+    python draft_verify_sampling_specv_amd/build.py      (or __graft_entry__.build())
 
 Every .hip file under csrc/ is compiled to an object with hipcc and the objects
 are linked into draft_verify_sampling_specv_amd/libspecv.so.  Packed-fp32 ops
