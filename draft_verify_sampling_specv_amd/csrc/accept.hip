@@ -4,24 +4,38 @@
 // accept x if u < p(x)/q(x); at the first rejection draw from (p - q)+ and stop; if the whole path
 // is accepted draw a bonus token from p of the last node; greedy at T = 0.  [PTD] Method 4,
 // "Acceptance Logic": on a tree the children of a node are tested in index order as draws without
-// replacement from q; after i rejections the target is (p - c_i q)+ / R_i (scalar form, see the
-// walk below).
+// replacement from q; after i rejections the target is (p - c_i q)+ / R_i with c_0 = 0,
+// R_0 = Q_0 = 1, c_{i+1} = c_i + R_i / Q_i (Q: draft mass not yet rejected).
 //
-// Two launches on the caller's stream:
-//   1. stats   grid (chunk, node, sequence): streams every target row and the draft rows of
-//              internal nodes once, coalesced 16-byte loads, and writes per-chunk softmax
-//              statistics (max, sum of exp) -- or (max, argmax) at T = 0.  This is the HBM-bound
-//              pass; one exp per element.
-//   2. finish  one 1024-thread workgroup per sequence: combines the chunk statistics; computes,
-//              for every draft node in parallel, p and q of its token under its parent's rows,
-//              the ratio p/q and its acceptance uniform; one wave then runs the walk (scalar, from
-//              those tables); the rare sibling-rejection passes R(c) = sum (p - c q)+ over a row
-//              pair and the final draw pass use the whole workgroup.  The draw pass records the
-//              sum of every 64*kVec-element segment in LDS; the segment holding the CDF crossing
-//              is found by a block scan and searched by one wave.
+// One launch whose grid never exceeds the number of workgroups the device holds at once (one per
+// CU here: the LDS tables need about 100 KB), so on a device running this kernel alone every
+// workgroup is resident together.  (A cooperative launch would guarantee that, but costs about
+// 20 us per call on this machine.)  Workgroups form teams of P; a team owns
+// one sequence at a time (sequences are dealt to teams round-robin) and every phase that streams
+// the vocabulary is split over the P workgroups of the team:
+//   1. statistics: items (row, chunk of 64 * kVec * kWaveLoads elements), one wave per item, over
+//      every target row and the draft rows of internal nodes, coalesced 16-byte loads, one exp per
+//      element: per-chunk (max, sum of exp2((z - max) log2e / T)), or (max, argmax) at T = 0.
+//   2. every workgroup of the team combines the chunk statistics (fp64 above chunk level) and
+//      builds per-node tables in LDS (p, q of each draft token under its parent's rows, p/q, both
+//      Philox uniforms, first child / next sibling / repeated-token links);
+//   3. one wave per workgroup runs the walk from those tables -- all workgroups of a team run the
+//      same walk on the same data, so they take the same decisions;
+//   4. residual-mass passes R(c) = sum (p - c q)+ (a rejection followed by another sibling) and the
+//      final draw pass are split into P contiguous ranges; partial sums are exchanged and added in
+//      rank order (fp64), so every workgroup sees the same totals.  The workgroup whose range holds
+//      the CDF crossing searches it (per-segment sums in LDS, then one wave) and writes the token.
+// Workgroups exchange values through 64-bit words (32-bit value, 32-bit tag of the launch) written
+// and read with device-scope atomic stores / loads: a word carries its own validity, so no fence
+// is needed.  Every wait is bounded by a wall-clock timeout, sticky per workgroup, so a launch ends
+// within about one timeout even if a teammate were never scheduled (e.g. CUs held by another
+// process); the sequences of a workgroup that timed out report accept_len = -2.
 //
-// Precision: per-element exponentials in fp32 (v_exp_f32), chunk sums in fp32, everything above
-// chunk level (row normalisers, ratios, c, Q, R, the CDF threshold and the chunk prefix) in fp64.
+// Precision: per-element exponentials in fp32 (v_exp_f32), chunk and segment sums in fp32,
+// everything above (row normalisers, ratios, c, Q, R, the CDF threshold and prefixes) in fp64.
+
+#include <algorithm>
+#include <atomic>
 
 #include "common.h"
 #include "kernels.h"
@@ -30,152 +44,30 @@ namespace specv {
 
 namespace {
 
-constexpr int kStatThreads = 256;
-constexpr int kUnroll = 4;
-constexpr int kWalkThreads = 1024;
-constexpr int kWalkWaves = kWalkThreads / kWave;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kWaveLoads = 16;              // 16-byte loads per lane per statistics item
 constexpr int kMaxVocab = 1 << 21;
-constexpr double kAllDraftBytes = 32.0 * (1 << 20);   // target logits of a call
+constexpr int kMaxTeam = 64;                // workgroups per sequence at most
+constexpr int kPassBatch = 4;               // tiles per batch of a range pass
+constexpr uint64_t kTimeoutTicks = 50000000ull;   // 0.5 s of the 100 MHz wall clock
 
 template <typename T>
-constexpr int chunk_elems() {
-    return kStatThreads * Elem<T>::kVec * kUnroll;   // bf16: 8192, fp32: 4096 (16 KB per row)
-}
+constexpr int item_elems() { return kWave * Elem<T>::kVec * kWaveLoads; }   // bf16 8192, fp32 4096
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct AcceptLayout {
-    size_t stats, total;
-    AcceptLayout(int B, int n1, int nchunk) {
-        stats = 0;
-        total = align256(stats + sizeof(float4) * size_t(B) * n1 * nchunk);
+    size_t stat, part, err, total;
+    AcceptLayout(int B, int n1, int nchunk, int P) {
+        stat = 0;
+        part = align256(stat + sizeof(uint64_t) * size_t(B) * n1 * nchunk * 4);
+        err = align256(part + sizeof(uint64_t) * size_t(B) * (n1 + 1) * P);
+        total = align256(err + sizeof(uint32_t));
     }
 };
 
-// Load this thread's share of [lo, hi) of one row: kUnroll vectors of kVec contiguous elements,
-// vector u at lo + (u * kStatThreads + t) * kVec.  Out-of-range elements read as -inf.
-template <typename T, bool kVecOK>
-__device__ __forceinline__ void load_chunk(const T* __restrict__ row, int lo, int hi, int t,
-                                           float* out) {
-    constexpr int kVec = Elem<T>::kVec;
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const int base = lo + (u * kStatThreads + t) * kVec;
-        if (kVecOK && base + kVec <= hi) {
-            Elem<T>::load_vec(row, base, out + u * kVec);
-        } else {
-#pragma unroll
-            for (int e = 0; e < kVec; ++e)
-                out[u * kVec + e] = (base + e < hi) ? Elem<T>::load(row, base + e) : -INFINITY;
-        }
-    }
-}
-
-// Draw weight of one element: (p(x) - c q(x))+ with p = exp2((zt - mt) k) / S_t etc.
-__device__ __forceinline__ float draw_weight(float zt, float zd, float mt, float md, float k,
-                                             float p_scale, float q_scale) {
-    float p = __builtin_amdgcn_exp2f((zt - mt) * k) * p_scale;
-    float q = __builtin_amdgcn_exp2f((zd - md) * k) * q_scale;
-    return fmaxf(p - q, 0.0f);
-}
-
-// ------------------------------------------------------------------------------------ 1. stats
-
-template <typename T, bool kGreedy, bool kVecOK, bool kAllDraft>
-__global__ void __launch_bounds__(kStatThreads)
-accept_stats_kernel(const T* __restrict__ target, const T* __restrict__ draft,
-                    const int32_t* __restrict__ parent, int n1, int V, int nchunk, float k,
-                    float4* __restrict__ stats) {
-    constexpr int kVec = Elem<T>::kVec;
-    constexpr int CH = chunk_elems<T>();
-    const int c = blockIdx.x, v = blockIdx.y, b = blockIdx.z;
-    const int t = threadIdx.x;
-    const int w = t / kWave, lane = t % kWave;
-    const int64_t row = (static_cast<int64_t>(b) * n1 + v) * V;
-    const int lo = c * CH;
-    const int hi = min(V, lo + CH);
-    __shared__ float4 part[kStatThreads / kWave];
-
-    float zt[kUnroll * kVec];
-    load_chunk<T, kVecOK>(target + row, lo, hi, t, zt);
-
-    if (kGreedy) {
-        float bv = -INFINITY;
-        int bi = INT_MAX;
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-            for (int e = 0; e < kVec; ++e) {
-                const int idx = lo + (u * kStatThreads + t) * kVec + e;
-                if (idx < hi) argmax_merge(bv, bi, zt[u * kVec + e], idx);
-            }
-        wave_argmax(bv, bi);
-        if (lane == 0) part[w] = make_float4(bv, __int_as_float(bi), 0.f, 0.f);
-        __syncthreads();
-        if (t == 0) {
-            float fv = part[0].x;
-            int fi = __float_as_int(part[0].y);
-            for (int i = 1; i < kStatThreads / kWave; ++i)
-                argmax_merge(fv, fi, part[i].x, __float_as_int(part[i].y));
-            stats[(static_cast<int64_t>(b) * n1 + v) * nchunk + c] =
-                make_float4(fv, __int_as_float(fi), 0.f, 0.f);
-        }
-        return;
-    }
-
-    // Draft rows are needed only for internal nodes (a leaf's draft row proposes nothing).  Small
-    // calls (kAllDraft) read every draft row instead: one dependent round trip to the parent
-    // array costs more there than the leaf rows' bytes.
-    bool want_draft = true;
-    if (!kAllDraft) {
-        int found = 0;
-        const int32_t* pb = parent + static_cast<int64_t>(b) * n1;
-        for (int i = v + 1 + t; i < n1; i += kStatThreads) found |= (pb[i] == v);
-        want_draft = __syncthreads_or(found) != 0;
-    }
-
-    float zd[kUnroll * kVec];
-    if (want_draft) load_chunk<T, kVecOK>(draft + row, lo, hi, t, zd);
-
-    float mt = -INFINITY, st = 0.f;
-#pragma unroll
-    for (int e = 0; e < kUnroll * kVec; ++e) mt = fmaxf(mt, zt[e]);
-    if (mt != -INFINITY) {
-#pragma unroll
-        for (int e = 0; e < kUnroll * kVec; ++e) st += __builtin_amdgcn_exp2f((zt[e] - mt) * k);
-    }
-    float md = -INFINITY, sd = 0.f;
-    if (want_draft) {
-#pragma unroll
-        for (int e = 0; e < kUnroll * kVec; ++e) md = fmaxf(md, zd[e]);
-        if (md != -INFINITY) {
-#pragma unroll
-            for (int e = 0; e < kUnroll * kVec; ++e) sd += __builtin_amdgcn_exp2f((zd[e] - md) * k);
-        }
-    }
-    wave_max_sum(mt, st, k);
-    if (want_draft) wave_max_sum(md, sd, k);
-    if (lane == 0) part[w] = make_float4(mt, st, md, sd);
-    __syncthreads();
-    if (t == 0) {
-        float4 r = part[0];
-        for (int i = 1; i < kStatThreads / kWave; ++i) {
-            merge_max_sum(r.x, r.y, part[i].x, part[i].y, k);
-            merge_max_sum(r.z, r.w, part[i].z, part[i].w, k);
-        }
-        stats[(static_cast<int64_t>(b) * n1 + v) * nchunk + c] = r;
-    }
-}
-
-// ------------------------------------------------------------------------------------ 2. finish
-
-// Streaming pass over one row pair with the draw weights w(x) = (p(x) - c q(x))+ (c = q_scale S_d;
-// q_scale == 0: w = p).  Tile i covers kWalkThreads * kVec consecutive elements; within a tile
-// wave ww owns the contiguous segment of 64 * kVec elements starting at (ww * 64) * kVec.  The
-// segment sums are written to seg[i * kWalkWaves + ww] (index order) if seg != nullptr.  Loads of
-// up to kPassBatch tiles are issued together so that their latencies overlap.
-// Returns the total (fp64, identical in all threads).
-constexpr int kPassBatch = 4;
+// ---------------------------------------------------------------------------------- helpers
 
 template <typename T>
 __device__ __forceinline__ void cvt_vec(const uint4& r, float* out);
@@ -190,44 +82,60 @@ __device__ __forceinline__ void cvt_vec<uint16_t>(const uint4& r, float* out) {
     out[4] = bf16_lo(r.z); out[5] = bf16_hi(r.z); out[6] = bf16_lo(r.w); out[7] = bf16_hi(r.w);
 }
 
-template <typename T, bool kVecOK>
-__device__ __forceinline__ void load_pair(const T* __restrict__ trow, const T* __restrict__ drow, int V,
-                                          int base, bool use_q, float* zt, float* zd) {
-    constexpr int kVec = Elem<T>::kVec;
-    if (kVecOK && base + kVec <= V) {
-        Elem<T>::load_vec(trow, base, zt);
-        if (use_q) Elem<T>::load_vec(drow, base, zd);
-    } else {
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) {
-            zt[e] = (base + e < V) ? Elem<T>::load(trow, base + e) : -INFINITY;
-            zd[e] = (use_q && base + e < V) ? Elem<T>::load(drow, base + e) : -INFINITY;
-        }
-    }
-    if (!use_q) {
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) zd[e] = -INFINITY;
-    }
+// Draw weight of one element: (p(x) - c q(x))+ with p = exp2((zt - mt) k) / S_t, q likewise.
+__device__ __forceinline__ float draw_weight(float zt, float zd, float mt, float md, float k,
+                                             float p_scale, float q_scale) {
+    const float p = __builtin_amdgcn_exp2f((zt - mt) * k) * p_scale;
+    const float q = __builtin_amdgcn_exp2f((zd - md) * k) * q_scale;
+    return fmaxf(p - q, 0.0f);
 }
 
+// Publish / read a tagged 64-bit word (value in the low half, launch tag in the high half).
+__device__ __forceinline__ void put_word(uint64_t* p, uint32_t bits, uint32_t tag) {
+    __hip_atomic_store(p, (static_cast<uint64_t>(tag) << 32) | bits, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Once a wait of this workgroup has timed out (*timed_out, sticky for the launch), later waits
+// return at once, so a launch ends within about one timeout whatever happens.
+__device__ uint32_t get_word(uint64_t* p, uint32_t tag, int* timed_out) {
+    uint64_t w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (static_cast<uint32_t>(w >> 32) != tag && !*timed_out) {
+        const uint64_t t0 = wall_clock64();
+        do {
+            __builtin_amdgcn_s_sleep(1);
+            w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (wall_clock64() - t0 > kTimeoutTicks) {
+                *timed_out = 1;
+                break;
+            }
+        } while (static_cast<uint32_t>(w >> 32) != tag);
+    }
+    return static_cast<uint32_t>(w);
+}
+
+// Streaming pass over tiles [t0, t1) of one row pair with the draw weights.  Tile i covers
+// kThreads * kVec consecutive elements; within a tile wave ww owns the contiguous segment of
+// 64 * kVec elements at (ww * 64) * kVec.  Segment sums go to seg[(i - t0) * kWaves + ww] if seg is
+// given.  Up to kPassBatch tiles are loaded together; the raw words of the last batch stay in rt /
+// rd.  Returns the block's total (fp64, identical in all threads).
 template <typename T, bool kVecOK>
-__device__ double row_pass(const T* __restrict__ trow, const T* __restrict__ drow, int V, float mt,
-                           float md, float k, float p_scale, float q_scale, float* seg, double* red,
-                           uint4 (&rt)[kPassBatch], uint4 (&rd)[kPassBatch]) {
+__device__ double range_pass(const T* __restrict__ trow, const T* __restrict__ drow, int V, int t0,
+                             int t1, float mt, float md, float k, float p_scale, float q_scale,
+                             float* seg, double* red, uint4 (&rt)[kPassBatch], uint4 (&rd)[kPassBatch]) {
     constexpr int kVec = Elem<T>::kVec;
-    constexpr int kTile = kWalkThreads * kVec;
+    constexpr int kTile = kThreads * kVec;
     const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const bool use_q = q_scale != 0.f;
     double acc = 0.0;
-    const int ntile = (V + kTile - 1) / kTile;
-    for (int i0 = 0; i0 < ntile; i0 += kPassBatch) {
+    for (int i0 = t0; i0 < t1; i0 += kPassBatch) {
         if (kVecOK) {
 #pragma unroll
             for (int j = 0; j < kPassBatch; ++j) {
                 const int base = (i0 + j) * kTile + threadIdx.x * kVec;
                 rt[j] = make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
                 rd[j] = rt[j];
-                if (i0 + j < ntile && base < V) {
+                if (i0 + j < t1 && base < V) {
                     rt[j] = *reinterpret_cast<const uint4*>(trow + base);
                     if (use_q) rd[j] = *reinterpret_cast<const uint4*>(drow + base);
                 }
@@ -235,59 +143,86 @@ __device__ double row_pass(const T* __restrict__ trow, const T* __restrict__ dro
         }
 #pragma unroll
         for (int j = 0; j < kPassBatch; ++j) {
-            if (i0 + j >= ntile) break;
+            if (i0 + j >= t1) break;
             const int base = (i0 + j) * kTile + threadIdx.x * kVec;
             float zt[kVec], zd[kVec];
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) { zt[e] = -INFINITY; zd[e] = -INFINITY; }
             if (kVecOK) {
                 if (base < V) {
                     cvt_vec<T>(rt[j], zt);
                     if (use_q) cvt_vec<T>(rd[j], zd);
                 }
-                if (!(base < V) || !use_q) {
+            } else {
 #pragma unroll
-                    for (int e = 0; e < kVec; ++e) {
-                        zd[e] = -INFINITY;
-                        if (!(base < V)) zt[e] = -INFINITY;
+                for (int e = 0; e < kVec; ++e) {
+                    if (base + e < V) {
+                        zt[e] = Elem<T>::load(trow, base + e);
+                        if (use_q) zd[e] = Elem<T>::load(drow, base + e);
                     }
                 }
-            } else {
-                load_pair<T, false>(trow, drow, V, base, use_q, zt, zd);
             }
             float sum = 0.f;
 #pragma unroll
             for (int e = 0; e < kVec; ++e) sum += draw_weight(zt[e], zd[e], mt, md, k, p_scale, q_scale);
             sum = wave_sum(sum);
-            if (seg && lane == 0) seg[(i0 + j) * kWalkWaves + w] = sum;
+            if (seg && lane == 0) seg[(i0 + j - t0) * kWaves + w] = sum;
             acc += sum;
         }
     }
-    // every lane of a wave holds the same acc: add the wave totals
     __syncthreads();
     if (lane == 0) red[w] = acc;
     __syncthreads();
     double tot = 0.0;
 #pragma unroll
-    for (int i = 0; i < kWalkWaves; ++i) tot += red[i];
+    for (int i = 0; i < kWaves; ++i) tot += red[i];
+    __syncthreads();
     return tot;
 }
 
+// Team exchange: publish this workgroup's partial, return the P partials' exclusive prefix before
+// `rank` and the total (fp64, rank order; identical in every workgroup of the team).  The partials
+// stay in s_vals for the caller.
+__device__ void team_exchange(uint64_t* slots, int P, int rank, float mine, uint32_t tag, double* s_vals,
+                              int* s_to, double& before, double& total) {
+    if (threadIdx.x == 0) put_word(slots + rank, __float_as_uint(mine), tag);
+    if (static_cast<int>(threadIdx.x) < P) {
+        const uint32_t bits = (static_cast<int>(threadIdx.x) == rank)
+                                  ? __float_as_uint(mine)
+                                  : get_word(slots + threadIdx.x, tag, s_to);
+        s_vals[threadIdx.x] = static_cast<double>(__uint_as_float(bits));
+    }
+    __syncthreads();
+    before = 0.0;
+    total = 0.0;
+    for (int r = 0; r < P; ++r) {
+        if (r < rank) before += s_vals[r];
+        total += s_vals[r];
+    }
+}
+
+// ---------------------------------------------------------------------------------- the kernel
+
 template <typename T, bool kGreedy, bool kVecOK>
-__global__ void __launch_bounds__(kWalkThreads)
-accept_finish_kernel(const T* __restrict__ target, const T* __restrict__ draft,
-                     const int32_t* __restrict__ tokens, const int32_t* __restrict__ parent, int n1,
-                     int V, int nchunk, float k, double invT, uint64_t seed, uint64_t offset,
-                     const float4* __restrict__ stats, int32_t* __restrict__ accept_len,
-                     int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_nodes,
-                     float* __restrict__ p_tok, float* __restrict__ q_tok) {
+__global__ void __launch_bounds__(kThreads)
+accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
+              const int32_t* __restrict__ tokens, const int32_t* __restrict__ parent, int B, int n1,
+              int V, int nchunk, int P, float k, double invT, uint64_t seed, uint64_t offset,
+              uint32_t tag, uint64_t* __restrict__ statw, uint64_t* __restrict__ partw,
+              uint32_t* __restrict__ err, int32_t* __restrict__ accept_len,
+              int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_nodes,
+              float* __restrict__ p_tok, float* __restrict__ q_tok) {
     constexpr int kVec = Elem<T>::kVec;
-    constexpr int kTile = kWalkThreads * kVec;
-    constexpr int kMaxSeg = (kMaxVocab + kTile - 1) / kTile * kWalkWaves;
+    constexpr int kTile = kThreads * kVec;
+    constexpr int kItem = item_elems<T>();
+    constexpr int kMaxSeg = (kMaxVocab + kTile - 1) / kTile * kWaves;
     __shared__ int32_t par[kMaxNodes];
     __shared__ int32_t tok[kMaxNodes];
     __shared__ int32_t info[kMaxNodes];     // greedy: argmax token of the row; else: has children
     __shared__ int32_t fch[kMaxNodes];      // first child (n1 if none)
     __shared__ int32_t nsib[kMaxNodes];     // next sibling (-1 if none)
     __shared__ int32_t dup[kMaxNodes];      // token repeats an earlier sibling's
+    __shared__ int32_t ilist[kMaxNodes];    // internal rows in index order
     __shared__ float Mt[kMaxNodes], Md[kMaxNodes];
     __shared__ double St[kMaxNodes], Sd[kMaxNodes];
     __shared__ double pq[kMaxNodes];        // p(x)/q(x) of node x under its parent's rows
@@ -296,397 +231,610 @@ accept_finish_kernel(const T* __restrict__ target, const T* __restrict__ draft,
     __shared__ double ures[kMaxNodes];      // draw uniforms
     __shared__ int32_t path[kMaxNodes];
     __shared__ float seg[kMaxSeg];
-    __shared__ double red[kWalkWaves];
-    __shared__ int s_bad, s_cmd, s_row, s_n, s_sel, s_found;
+    __shared__ double red[kWaves];
+    __shared__ double s_vals[kMaxTeam];
+    __shared__ int wcount[kWaves];
+    __shared__ float pv[kWaves];
+    __shared__ int pi[kWaves];
+    __shared__ int s_bad, s_ni, s_cmd, s_row, s_n, s_sel, s_found, s_to;
     __shared__ float s_ps, s_qs;
     __shared__ double s_R, s_base;
 
-    const int b = blockIdx.x;
     const int t = threadIdx.x;
     const int w = t / kWave, lane = t % kWave;
-    const int64_t seq = static_cast<int64_t>(b) * n1;
+    const int team = blockIdx.x / P, rank = blockIdx.x % P, nteams = gridDim.x / P;
+    const int ntile = (V + kTile - 1) / kTile;
+    const int tpb = (ntile + P - 1) / P;
+    const int my_t0 = min(ntile, rank * tpb), my_t1 = min(ntile, my_t0 + tpb);
 
-    // -- A. issue the independent loads first: the sequence's chunk statistics (staged in LDS when
-    //       they fit), the parent array and the draft tokens; validate
-    __shared__ float4 sst[kWalkThreads];
-    const bool stage = n1 * nchunk <= kWalkThreads;
-    float4 mystat = make_float4(-INFINITY, 0.f, -INFINITY, 0.f);
-    if (stage && t < n1 * nchunk) mystat = stats[seq * nchunk + t];
-    if (t == 0) s_bad = 0;
-    for (int i = t; i < n1; i += kWalkThreads) {
-        info[i] = 0;
-        fch[i] = n1;
-    }
-    __syncthreads();
-    for (int i = t; i < n1; i += kWalkThreads) {
-        const int p = parent[seq + i];
-        const int x = tokens[seq + i];
-        par[i] = p;
-        tok[i] = x;
-        const bool ok = (i == 0) ? (p == -1) : (p >= 0 && p < i && x >= 0 && x < V);
-        if (!ok) s_bad = 1;
-    }
-    if (stage) sst[t] = mystat;
-    __syncthreads();
-    if (s_bad) {
-        for (int i = t; i < n1; i += kWalkThreads) {
-            out_tokens[seq + i] = -1;
-            out_nodes[seq + i] = -1;
-            if (p_tok) p_tok[seq + i] = NAN;
-            if (q_tok) q_tok[seq + i] = NAN;
+    if (t == 0) s_to = 0;
+    for (int b = team; b < B; b += nteams) {
+        const int64_t seq = static_cast<int64_t>(b) * n1;
+        uint64_t* sw = statw + seq * nchunk * 4;
+        uint64_t* pw = partw + static_cast<int64_t>(b) * (n1 + 1) * P;
+
+        // -- A. stage and validate the parent array and the draft tokens
+        __syncthreads();
+        if (t == 0) s_bad = 0;
+        for (int i = t; i < n1; i += kThreads) {
+            info[i] = 0;
+            fch[i] = n1;
         }
-        if (t == 0) accept_len[b] = -1;
-        return;
-    }
-
-    // -- B. gather every draft token's logits under its parent's rows (in flight during the
-    //       combine); tree links: first child, next sibling, repeated sibling tokens
-    float gzt = 0.f, gzd = 0.f;
-    if (!kGreedy && t > 0 && t < n1) {
-        const int pa = par[t], x = tok[t];
-        gzt = Elem<T>::load(target + (seq + pa) * V, x);
-        gzd = Elem<T>::load(draft + (seq + pa) * V, x);
-    }
-    for (int c = 1 + t; c < n1; c += kWalkThreads) {
-        const int pa = par[c], x = tok[c];
-        if (!kGreedy) info[pa] = 1;
-        atomicMin(&fch[pa], c);
-        int nx = -1;
-        for (int i = c + 1; i < n1; ++i)
-            if (par[i] == pa) { nx = i; break; }
-        nsib[c] = nx;
-        int d = 0;
-        for (int i = c - 1; i > pa; --i)
-            if (par[i] == pa && tok[i] == x) { d = 1; break; }
-        dup[c] = d;
-    }
-    __syncthreads();
-
-    // -- C. combine chunk statistics per row (one wave per row, lanes over chunks)
-    for (int v = w; v < n1; v += kWalkWaves) {
-        const float4* sv = stage ? sst + v * nchunk : stats + (seq + v) * nchunk;
-        if (kGreedy) {
-            float bv = -INFINITY;
-            int bi = INT_MAX;
-            for (int c = lane; c < nchunk; c += kWave) {
-                const float4 s4 = sv[c];
-                argmax_merge(bv, bi, s4.x, __float_as_int(s4.y));
-            }
-            wave_argmax(bv, bi);
-            if (lane == 0) info[v] = (bi >= 0 && bi < V) ? bi : 0;
-        } else {
-            const bool dr = info[v] != 0;
-            float mt = -INFINITY, md = -INFINITY;
-            for (int c = lane; c < nchunk; c += kWave) {
-                const float4 s4 = sv[c];
-                mt = fmaxf(mt, s4.x);
-                if (dr) md = fmaxf(md, s4.z);
-            }
-            mt = wave_max(mt);
-            md = wave_max(md);
-            double st = 0.0, sd = 0.0;
-            for (int c = lane; c < nchunk; c += kWave) {
-                const float4 s4 = sv[c];
-                if (s4.x != -INFINITY) st += static_cast<double>(s4.y) * __builtin_amdgcn_exp2f((s4.x - mt) * k);
-                if (dr && s4.z != -INFINITY) sd += static_cast<double>(s4.w) * __builtin_amdgcn_exp2f((s4.z - md) * k);
-            }
-            st = wave_sum(st);
-            sd = wave_sum(sd);
-            if (lane == 0) {
-                Mt[v] = mt; St[v] = st;
-                Md[v] = md; Sd[v] = sd;
-            }
+        __syncthreads();
+        for (int i = t; i < n1; i += kThreads) {
+            const int p = parent[seq + i];
+            const int x = tokens[seq + i];
+            par[i] = p;
+            tok[i] = x;
+            const bool ok = (i == 0) ? (p == -1) : (p >= 0 && p < i && x >= 0 && x < V);
+            if (!ok) s_bad = 1;
         }
-    }
-    __syncthreads();
-
-    // -- D. per node: p, q of its token under its parent's rows, the ratio, its two uniforms
-    for (int v = t; v < n1; v += kWalkThreads) {
-        float pv = NAN, qv = NAN;
-        if (!kGreedy) {
-            const U64x4 rnd = philox4x64_10(static_cast<uint64_t>(v), static_cast<uint64_t>(b), offset, 0, seed, 0);
-            uacc[v] = word_to_uniform(rnd.w[0]);
-            ures[v] = word_to_uniform(rnd.w[1]);
-            if (v > 0) {
-                const int pa = par[v];
-                const double zt = gzt, zd = gzd;
-                const double lp = (zt - Mt[pa]) * invT;
-                const double lq = (zd - Md[pa]) * invT;
-                const double pd = exp(lp) / St[pa];
-                const double qd = exp(lq) / Sd[pa];
-                pq[v] = exp(lp - lq) * (Sd[pa] / St[pa]);
-                qx[v] = static_cast<float>(qd);
-                pv = static_cast<float>(pd);
-                qv = static_cast<float>(qd);
-            }
-        }
-        if (p_tok) p_tok[seq + v] = pv;
-        if (q_tok) q_tok[seq + v] = qv;
-    }
-    __syncthreads();
-
-    // -- E. the walk, run by wave 0; residual-mass passes (sibling rejections) use the whole block
-    uint4 rt[kPassBatch], rd[kPassBatch];
-    {
-        int v = 0, n = 0;
-        double cs = 0.0, R = 1.0, Q = 1.0, pend = 0.0;
-        bool pending = false;
-        int nxt = fch[0] < n1 ? fch[0] : -1;
-        while (true) {
-            if (w == 0) {
-                if (pending) {
-                    const double Rn = s_R;
-                    if (Rn > 0.0) { cs = pend; R = Rn; }
-                    pending = false;
+        __syncthreads();
+        if (s_bad) {
+            if (rank == 0) {
+                for (int i = t; i < n1; i += kThreads) {
+                    out_tokens[seq + i] = -1;
+                    out_nodes[seq + i] = -1;
+                    if (p_tok) p_tok[seq + i] = NAN;
+                    if (q_tok) q_tok[seq + i] = NAN;
                 }
-                int cmd = -1;   // 0: residual-mass pass, 1: draw at v, 2: greedy end at v
-                while (cmd < 0) {
-                    if (kGreedy) {
-                        const int y = info[v];
-                        int c = fch[v] < n1 ? fch[v] : -1;
-                        while (c >= 0 && tok[c] != y) c = nsib[c];
-                        if (c < 0) { cmd = 2; break; }
-                        if (lane == 0) path[n] = c;
-                        ++n;
-                        v = c;
-                        continue;
-                    }
-                    if (nxt < 0) { cmd = 1; break; }
-                    const int c = nxt;
-                    nxt = nsib[c];
-                    if (dup[c]) continue;
-                    const double ratio = fmax(0.0, pq[c] - cs) * Q / R;
-                    if (uacc[c] < ratio) {
-                        if (lane == 0) path[n] = c;
-                        ++n;
-                        v = c;
-                        cs = 0.0; R = 1.0; Q = 1.0;
-                        nxt = fch[v] < n1 ? fch[v] : -1;
-                        continue;
-                    }
-                    const double cn = cs + R / Q;
-                    Q -= static_cast<double>(qx[c]);
-                    if (nxt >= 0) {
-                        pending = true;
-                        pend = cn;
-                        if (lane == 0) {
-                            s_ps = static_cast<float>(1.0 / St[v]);
-                            s_qs = static_cast<float>(cn / Sd[v]);
-                        }
-                        cmd = 0;
+                if (t == 0) accept_len[b] = -1;
+            }
+            continue;
+        }
+
+        // -- B. tree links, internal rows; gather every draft token's logits under its parent's rows
+        float gzt = 0.f, gzd = 0.f;
+        if (!kGreedy && t > 0 && t < n1) {
+            const int pa = par[t], x = tok[t];
+            gzt = Elem<T>::load(target + (seq + pa) * V, x);
+            gzd = Elem<T>::load(draft + (seq + pa) * V, x);
+        }
+        for (int c = 1 + t; c < n1; c += kThreads) {
+            const int pa = par[c], x = tok[c];
+            info[pa] = 1;
+            atomicMin(&fch[pa], c);
+            int nx = -1;
+            for (int i = c + 1; i < n1; ++i)
+                if (par[i] == pa) { nx = i; break; }
+            nsib[c] = nx;
+            int d = 0;
+            for (int i = c - 1; i > pa; --i)
+                if (par[i] == pa && tok[i] == x) { d = 1; break; }
+            dup[c] = d;
+        }
+        __syncthreads();
+        {   // compact list of internal rows, in index order
+            int done = 0;
+            for (int base = 0; base < n1; base += kThreads) {
+                const int v = base + t;
+                const bool f = v < n1 && info[v] != 0;
+                const uint64_t m = __ballot(f);
+                if (lane == 0) wcount[w] = __popcll(m);
+                __syncthreads();
+                int before = 0, all = 0;
+                for (int i = 0; i < kWaves; ++i) {
+                    if (i < w) before += wcount[i];
+                    all += wcount[i];
+                }
+                if (f) ilist[done + before + __popcll(m & ((1ull << lane) - 1ull))] = v;
+                done += all;
+                __syncthreads();
+            }
+            if (t == 0) s_ni = done;
+            __syncthreads();
+        }
+        const int ni = kGreedy ? 0 : s_ni;
+
+        // -- C. chunk statistics: one wave per item, items split over the team
+        const int nitems = (n1 + ni) * nchunk;
+        for (int it = rank * kWaves + w; it < nitems; it += P * kWaves) {
+            const bool isd = it >= n1 * nchunk;
+            const int j = isd ? it - n1 * nchunk : it;
+            const int row = isd ? ilist[j / nchunk] : j / nchunk;
+            const int c = j % nchunk;
+            const T* src = (isd ? draft : target) + (seq + row) * V;
+            const int lo = c * kItem, hi = min(V, lo + kItem);
+            uint64_t* slot = sw + (static_cast<int64_t>(row) * nchunk + c) * 4 + (isd ? 2 : 0);
+            // values of load u are converted from the raw words when used (two passes: max, then
+            // sum of exp), so only the raw 16-byte words stay in registers
+            uint4 r[kWaveLoads];
+            if (kVecOK) {
+#pragma unroll
+                for (int u = 0; u < kWaveLoads; ++u) {
+                    const int base = lo + (u * kWave + lane) * kVec;
+                    r[u] = make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
+                    if (base < hi) r[u] = *reinterpret_cast<const uint4*>(src + base);
+                }
+            }
+            auto values = [&](int u, float* z) {
+                const int base = lo + (u * kWave + lane) * kVec;
+                if (kVecOK) {
+                    if (base < hi) {
+                        cvt_vec<T>(r[u], z);
                     } else {
-                        cs = cn;
-                        cmd = 1;
+#pragma unroll
+                        for (int e = 0; e < kVec; ++e) z[e] = -INFINITY;
                     }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) z[e] = (base + e < hi) ? Elem<T>::load(src, base + e) : -INFINITY;
+                }
+            };
+            if (kGreedy) {
+                float bv = -INFINITY;
+                int bi = INT_MAX;
+#pragma unroll
+                for (int u = 0; u < kWaveLoads; ++u) {
+                    float z[kVec];
+                    values(u, z);
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) {
+                        const int x = lo + (u * kWave + lane) * kVec + e;
+                        if (x < hi) argmax_merge(bv, bi, z[e], x);
+                    }
+                }
+                wave_argmax(bv, bi);
+                if (lane == 0) {
+                    put_word(slot, __float_as_uint(bv), tag);
+                    put_word(slot + 1, static_cast<uint32_t>(bi), tag);
+                }
+            } else {
+                // online over the 16-byte vectors: the running sum is rescaled once per vector
+                float m = -INFINITY, s = 0.f;
+#pragma unroll
+                for (int u = 0; u < kWaveLoads; ++u) {
+                    float z[kVec];
+                    values(u, z);
+                    float mu = m;
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) mu = fmaxf(mu, z[e]);
+                    if (mu != -INFINITY) {
+                        float add = 0.f;
+#pragma unroll
+                        for (int e = 0; e < kVec; ++e) add += __builtin_amdgcn_exp2f((z[e] - mu) * k);
+                        s = (m == -INFINITY ? 0.f : s * __builtin_amdgcn_exp2f((m - mu) * k)) + add;
+                        m = mu;
+                    }
+                }
+                wave_max_sum(m, s, k);
+                if (lane == 0) {
+                    put_word(slot, __float_as_uint(m), tag);
+                    put_word(slot + 1, __float_as_uint(s), tag);
+                }
+            }
+        }
+
+        // -- D. combine the chunk statistics of every row (one wave per row, lanes over chunks)
+        for (int v = w; v < n1; v += kWaves) {
+            uint64_t* sv = sw + static_cast<int64_t>(v) * nchunk * 4;
+            if (kGreedy) {
+                float bv = -INFINITY;
+                int bi = INT_MAX;
+                for (int c = lane; c < nchunk; c += kWave) {
+                    const float cv = __uint_as_float(get_word(sv + c * 4, tag, &s_to));
+                    const int ci = static_cast<int>(get_word(sv + c * 4 + 1, tag, &s_to));
+                    argmax_merge(bv, bi, cv, ci);
+                }
+                wave_argmax(bv, bi);
+                if (lane == 0) info[v] = (bi >= 0 && bi < V) ? bi : 0;
+            } else {
+                const bool dr = info[v] != 0;
+                float mt = -INFINITY, md = -INFINITY;
+                float a0[2], a1[2], b0[2], b1[2];   // up to 128 chunks per row held in registers
+                for (int q2 = 0; q2 < 2; ++q2) {
+                    const int c = lane + q2 * kWave;
+                    a0[q2] = -INFINITY; a1[q2] = 0.f; b0[q2] = -INFINITY; b1[q2] = 0.f;
+                    if (c < nchunk) {
+                        a0[q2] = __uint_as_float(get_word(sv + c * 4, tag, &s_to));
+                        a1[q2] = __uint_as_float(get_word(sv + c * 4 + 1, tag, &s_to));
+                        if (dr) {
+                            b0[q2] = __uint_as_float(get_word(sv + c * 4 + 2, tag, &s_to));
+                            b1[q2] = __uint_as_float(get_word(sv + c * 4 + 3, tag, &s_to));
+                        }
+                    }
+                    mt = fmaxf(mt, a0[q2]);
+                    md = fmaxf(md, b0[q2]);
+                }
+                for (int c = lane + 2 * kWave; c < nchunk; c += kWave) {
+                    mt = fmaxf(mt, __uint_as_float(get_word(sv + c * 4, tag, &s_to)));
+                    if (dr) md = fmaxf(md, __uint_as_float(get_word(sv + c * 4 + 2, tag, &s_to)));
+                }
+                mt = wave_max(mt);
+                md = wave_max(md);
+                double st = 0.0, sd = 0.0;
+                for (int q2 = 0; q2 < 2; ++q2) {
+                    if (a0[q2] != -INFINITY) st += static_cast<double>(a1[q2]) * __builtin_amdgcn_exp2f((a0[q2] - mt) * k);
+                    if (dr && b0[q2] != -INFINITY) sd += static_cast<double>(b1[q2]) * __builtin_amdgcn_exp2f((b0[q2] - md) * k);
+                }
+                for (int c = lane + 2 * kWave; c < nchunk; c += kWave) {
+                    const float x0 = __uint_as_float(get_word(sv + c * 4, tag, &s_to));
+                    const float x1 = __uint_as_float(get_word(sv + c * 4 + 1, tag, &s_to));
+                    if (x0 != -INFINITY) st += static_cast<double>(x1) * __builtin_amdgcn_exp2f((x0 - mt) * k);
+                    if (dr) {
+                        const float y0 = __uint_as_float(get_word(sv + c * 4 + 2, tag, &s_to));
+                        const float y1 = __uint_as_float(get_word(sv + c * 4 + 3, tag, &s_to));
+                        if (y0 != -INFINITY) sd += static_cast<double>(y1) * __builtin_amdgcn_exp2f((y0 - md) * k);
+                    }
+                }
+                st = wave_sum(st);
+                sd = wave_sum(sd);
+                if (lane == 0) {
+                    Mt[v] = mt; St[v] = st;
+                    Md[v] = md; Sd[v] = sd;
+                }
+            }
+        }
+        __syncthreads();
+
+        // -- E. per node: p, q of its token under its parent's rows, the ratio, its two uniforms
+        for (int v = t; v < n1; v += kThreads) {
+            float pv_ = NAN, qv_ = NAN;
+            if (!kGreedy) {
+                const U64x4 rnd = philox4x64_10(static_cast<uint64_t>(v), static_cast<uint64_t>(b), offset, 0, seed, 0);
+                uacc[v] = word_to_uniform(rnd.w[0]);
+                ures[v] = word_to_uniform(rnd.w[1]);
+                if (v > 0) {
+                    const int pa = par[v];
+                    const float zt = (v == t) ? gzt : Elem<T>::load(target + (seq + pa) * V, tok[v]);
+                    const float zd = (v == t) ? gzd : Elem<T>::load(draft + (seq + pa) * V, tok[v]);
+                    const double lp = (static_cast<double>(zt) - Mt[pa]) * invT;
+                    const double lq = (static_cast<double>(zd) - Md[pa]) * invT;
+                    const double pd = exp(lp) / St[pa];
+                    const double qd = exp(lq) / Sd[pa];
+                    pq[v] = exp(lp - lq) * (Sd[pa] / St[pa]);
+                    qx[v] = static_cast<float>(qd);
+                    pv_ = static_cast<float>(pd);
+                    qv_ = static_cast<float>(qd);
+                }
+            }
+            if (rank == 0) {
+                if (p_tok) p_tok[seq + v] = pv_;
+                if (q_tok) q_tok[seq + v] = qv_;
+            }
+        }
+        __syncthreads();
+
+        // -- F. the walk (wave 0; identical in every workgroup of the team); residual-mass passes
+        //       are split over the team
+        uint4 rt[kPassBatch], rd[kPassBatch];
+        int npass = 0;
+        {
+            int v = 0, n = 0;
+            double cs = 0.0, R = 1.0, Q = 1.0, pend = 0.0;
+            bool pending = false;
+            int nxt = fch[0] < n1 ? fch[0] : -1;
+            while (true) {
+                if (w == 0) {
+                    if (pending) {
+                        const double Rn = s_R;
+                        if (Rn > 0.0) { cs = pend; R = Rn; }
+                        pending = false;
+                    }
+                    int cmd = -1;   // 0: residual-mass pass, 1: draw at v, 2: greedy end at v
+                    while (cmd < 0) {
+                        if (kGreedy) {
+                            const int y = info[v];
+                            int c = fch[v] < n1 ? fch[v] : -1;
+                            while (c >= 0 && tok[c] != y) c = nsib[c];
+                            if (c < 0) { cmd = 2; break; }
+                            if (lane == 0) path[n] = c;
+                            ++n;
+                            v = c;
+                            continue;
+                        }
+                        if (nxt < 0) { cmd = 1; break; }
+                        const int c = nxt;
+                        nxt = nsib[c];
+                        if (dup[c]) continue;
+                        const double ratio = fmax(0.0, pq[c] - cs) * Q / R;
+                        if (uacc[c] < ratio) {
+                            if (lane == 0) path[n] = c;
+                            ++n;
+                            v = c;
+                            cs = 0.0; R = 1.0; Q = 1.0;
+                            nxt = fch[v] < n1 ? fch[v] : -1;
+                            continue;
+                        }
+                        const double cn = cs + R / Q;
+                        Q -= static_cast<double>(qx[c]);
+                        if (nxt >= 0) {
+                            pending = true;
+                            pend = cn;
+                            if (lane == 0) {
+                                s_ps = static_cast<float>(1.0 / St[v]);
+                                s_qs = static_cast<float>(cn / Sd[v]);
+                            }
+                            cmd = 0;
+                        } else {
+                            cs = cn;
+                            cmd = 1;
+                        }
+                    }
+                    if (lane == 0) {
+                        s_cmd = cmd;
+                        s_row = v;
+                        s_n = n;
+                        if (cmd == 1) {
+                            s_ps = static_cast<float>(1.0 / St[v]);
+                            s_qs = (cs > 0.0) ? static_cast<float>(cs / Sd[v]) : 0.f;
+                        }
+                    }
+                }
+                __syncthreads();
+                if (s_cmd != 0) break;
+                const int64_t rr = (seq + s_row) * V;
+                const double mine = range_pass<T, kVecOK>(target + rr, draft + rr, V, my_t0, my_t1, Mt[s_row],
+                                                          Md[s_row], k, s_ps, s_qs, nullptr, red, rt, rd);
+                double Rn = mine;
+                if (P > 1) {
+                    double before_unused;
+                    team_exchange(pw + static_cast<int64_t>(npass) * P, P, rank, static_cast<float>(mine), tag,
+                                  s_vals, &s_to, before_unused, Rn);
+                }
+                ++npass;
+                __syncthreads();
+                if (t == 0) s_R = Rn;
+                __syncthreads();
+            }
+        }
+
+        // -- G. outputs of the walk (rank 0 of the team)
+        const int cmd = s_cmd, e = s_row, na = s_n;
+        if (rank == 0) {
+            for (int i = t; i < n1; i += kThreads) {
+                out_nodes[seq + i] = (i < na) ? path[i] : -1;
+                if (i < na) out_tokens[seq + i] = tok[path[i]];
+                else if (i > na) out_tokens[seq + i] = -1;
+            }
+            if (t == 0) accept_len[b] = na;
+        }
+        if (cmd == 2) {
+            if (rank == 0 && t == 0) out_tokens[seq + na] = info[e];
+            __syncthreads();
+            if (s_to && t == 0) {
+                atomicOr(err, 1u);
+                if (rank == 0) accept_len[b] = -2;
+            }
+            continue;
+        }
+
+        // -- H. the draw at node e: w(x) = (p(x) - c q(x))+, smallest x whose CDF exceeds u * W
+        const int64_t rr = (seq + e) * V;
+        const float mt = Mt[e], ps = s_ps, qs = s_qs;
+        const float md = (qs != 0.f) ? Md[e] : 0.f;
+        const double mine = range_pass<T, kVecOK>(target + rr, draft + rr, V, my_t0, my_t1, mt, md, k, ps, qs,
+                                                  seg, red, rt, rd);
+        double before = 0.0, W = mine;
+        if (P > 1)
+            team_exchange(pw + static_cast<int64_t>(npass) * P, P, rank, static_cast<float>(mine), tag, s_vals,
+                          &s_to, before, W);
+        const double thr = ures[e] * W;
+        // the owner: the first rank whose running sum passes thr (or, if rounding left thr at or
+        // above the total, the last rank with mass); every workgroup finds the same one
+        int owner = -1;
+        if (W > 0.0) {
+            if (P > 1) {
+                double acc = 0.0;
+                int lastpos = -1;
+                for (int r = 0; r < P; ++r) {
+                    if (s_vals[r] > 0.0) lastpos = r;
+                    if (owner < 0 && acc + s_vals[r] > thr) owner = r;
+                    acc += s_vals[r];
+                }
+                if (owner < 0) owner = lastpos;
+            } else {
+                owner = 0;
+            }
+        }
+        if (owner == rank) {
+            const int nseg = (my_t1 - my_t0) * kWaves;
+            if (w == 0) {
+                int sel = -1;
+                double base = 0.0;
+                const int g = (nseg + kWave - 1) / kWave;
+                const int s0 = min(nseg, lane * g), s1 = min(nseg, s0 + g);
+                double gs = 0.0;
+                for (int i = s0; i < s1; ++i) gs += seg[i];
+                double incl = gs;
+#pragma unroll
+                for (int o = 1; o < kWave; o <<= 1) {
+                    const double yv = __shfl_up(incl, o);
+                    if (lane >= o) incl += yv;
+                }
+                const uint64_t hit = __ballot(s1 > s0 && before + incl > thr);
+                int L;
+                bool crossing;
+                if (hit) {
+                    L = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+                    crossing = true;
+                } else {
+                    const uint64_t nz = __ballot(gs > 0.0);
+                    L = nz ? 63 - __clzll(static_cast<long long>(nz)) : -1;
+                    crossing = false;
+                }
+                if (L >= 0 && lane == L) {
+                    double acc = before + incl - gs;
+                    int lastpos = -1;
+                    double lastbase = acc;
+                    for (int i = s0; i < s1; ++i) {
+                        if (seg[i] > 0.f) { lastpos = i; lastbase = acc; }
+                        if (crossing && acc + seg[i] > thr) { sel = i; base = acc; break; }
+                        acc += seg[i];
+                    }
+                    if (sel < 0) { sel = lastpos; base = lastbase; }
+                }
+                if (L >= 0) {
+                    sel = __shfl(sel, L);
+                    base = __shfl(base, L);
                 }
                 if (lane == 0) {
-                    s_cmd = cmd;
-                    s_row = v;
-                    s_n = n;
-                    if (cmd == 1) {
-                        s_ps = static_cast<float>(1.0 / St[v]);
-                        s_qs = (cs > 0.0) ? static_cast<float>(cs / Sd[v]) : 0.f;
+                    s_sel = sel;
+                    s_base = base;
+                    s_found = -1;
+                }
+            }
+            __syncthreads();
+            const int sel = s_sel;
+            if (sel >= 0 && w == sel % kWaves) {
+                const int tl = sel / kWaves;                 // tile within this workgroup's range
+                const int base = (my_t0 + tl) * kTile + (w * kWave + lane) * kVec;
+                float zt[kVec], zd[kVec], wt[kVec];
+#pragma unroll
+                for (int i = 0; i < kVec; ++i) { zt[i] = -INFINITY; zd[i] = -INFINITY; }
+                if (kVecOK && my_t1 - my_t0 <= kPassBatch) {
+                    uint4 a = rt[0], c = rd[0];
+#pragma unroll
+                    for (int j = 1; j < kPassBatch; ++j)
+                        if (j == tl) { a = rt[j]; c = rd[j]; }
+                    if (base < V) {
+                        cvt_vec<T>(a, zt);
+                        if (qs != 0.f) cvt_vec<T>(c, zd);
                     }
-                }
-            }
-            __syncthreads();
-            if (s_cmd != 0) break;
-            const int64_t rr = (seq + s_row) * V;
-            const double Rn = row_pass<T, kVecOK>(target + rr, draft + rr, V, Mt[s_row], Md[s_row], k,
-                                                  s_ps, s_qs, nullptr, red, rt, rd);
-            if (t == 0) s_R = Rn;
-            __syncthreads();
-        }
-    }
-
-    // -- F. outputs of the walk
-    const int cmd = s_cmd, e = s_row, na = s_n;
-    for (int i = t; i < n1; i += kWalkThreads) {
-        out_nodes[seq + i] = (i < na) ? path[i] : -1;
-        if (i < na) out_tokens[seq + i] = tok[path[i]];
-        else if (i > na) out_tokens[seq + i] = -1;
-    }
-    if (t == 0) accept_len[b] = na;
-    if (cmd == 2) {
-        if (t == 0) out_tokens[seq + na] = info[e];
-        return;
-    }
-
-    // -- G. the draw at node e: w(x) = (p(x) - c q(x))+, smallest x whose CDF exceeds u * W
-    const int64_t rr = (seq + e) * V;
-    const float mt = Mt[e], ps = s_ps, qs = s_qs;
-    const float md = (qs != 0.f) ? Md[e] : 0.f;
-    const double W = row_pass<T, kVecOK>(target + rr, draft + rr, V, mt, md, k, ps, qs, seg, red, rt, rd);
-    const int ntile = (V + kTile - 1) / kTile;
-    const int nseg = ntile * kWalkWaves;
-    const double thr = ures[e] * W;
-
-    // -- H. wave 0 finds the segment holding the crossing (lane l owns a contiguous group)
-    if (w == 0) {
-        int sel = -1;
-        double base = 0.0;
-        if (W > 0.0) {
-            const int g = (nseg + kWave - 1) / kWave;
-            const int s0 = min(nseg, lane * g), s1 = min(nseg, s0 + g);
-            double gs = 0.0;
-            for (int i = s0; i < s1; ++i) gs += seg[i];
-            double incl = gs;
+                } else {
 #pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const double yv = __shfl_up(incl, o);
-                if (lane >= o) incl += yv;
-            }
-            const uint64_t hit = __ballot(s1 > s0 && incl > thr);
-            int L;
-            bool crossing;
-            if (hit) {
-                L = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-                crossing = true;
-            } else {   // rounding left u * W at or above every running sum: last group with mass
-                const uint64_t nz = __ballot(gs > 0.0);
-                L = nz ? 63 - __clzll(static_cast<long long>(nz)) : -1;
-                crossing = false;
-            }
-            if (L >= 0 && lane == L) {
-                double acc = incl - gs;
-                int lastpos = -1;
-                double lastbase = acc;
-                for (int i = s0; i < s1; ++i) {
-                    if (seg[i] > 0.f) { lastpos = i; lastbase = acc; }
-                    if (crossing && acc + seg[i] > thr) { sel = i; base = acc; break; }
-                    acc += seg[i];
+                    for (int i = 0; i < kVec; ++i)
+                        if (base + i < V) {
+                            zt[i] = Elem<T>::load(target + rr, base + i);
+                            if (qs != 0.f) zd[i] = Elem<T>::load(draft + rr, base + i);
+                        }
                 }
-                if (sel < 0) { sel = lastpos; base = lastbase; }
-            }
-            if (L >= 0) {
-                sel = __shfl(sel, L);
-                base = __shfl(base, L);
-            }
-        }
-        if (lane == 0) {
-            s_sel = sel;
-            s_base = base;
-            s_found = -1;
-        }
-    }
-    __syncthreads();
-
-    // -- I. the wave owning the segment searches it, from registers when the whole row was held
-    const int sel = s_sel;
-    if (sel >= 0 && w == sel % kWalkWaves) {
-        const int tile = sel / kWalkWaves;
-        const int base = tile * kTile + (w * kWave + lane) * kVec;
-        float zt[kVec], zd[kVec], wt[kVec];
-        if (kVecOK && ntile <= kPassBatch) {
-            uint4 a = rt[0], c = rd[0];
-#pragma unroll
-            for (int j = 1; j < kPassBatch; ++j)
-                if (j == tile) { a = rt[j]; c = rd[j]; }
-            if (base < V) {
-                cvt_vec<T>(a, zt);
-                cvt_vec<T>(c, zd);
-            }
-            if (!(base < V) || qs == 0.f) {
+                float ls = 0.f;
 #pragma unroll
                 for (int i = 0; i < kVec; ++i) {
-                    zd[i] = -INFINITY;
-                    if (!(base < V)) zt[i] = -INFINITY;
+                    wt[i] = draw_weight(zt[i], zd[i], mt, md, k, ps, qs);
+                    ls += wt[i];
                 }
+                double incl2 = ls;
+#pragma unroll
+                for (int o = 1; o < kWave; o <<= 1) {
+                    const double yv = __shfl_up(incl2, o);
+                    if (lane >= o) incl2 += yv;
+                }
+                double acc = s_base + incl2 - ls;
+                int cand = INT_MAX, lastpos = -1;
+#pragma unroll
+                for (int i = 0; i < kVec; ++i) {
+                    acc += wt[i];
+                    if (wt[i] > 0.f) {
+                        lastpos = base + i;
+                        if (cand == INT_MAX && acc > thr) cand = base + i;
+                    }
+                }
+                int y = -1;
+                const uint64_t hit = __ballot(cand != INT_MAX);
+                if (hit) {
+                    y = __shfl(cand, __ffsll(static_cast<unsigned long long>(hit)) - 1);
+                } else {
+                    const uint64_t pos = __ballot(lastpos >= 0);
+                    if (pos) y = __shfl(lastpos, 63 - __clzll(static_cast<long long>(pos)));
+                }
+                if (lane == 0) s_found = y;
             }
-        } else {
-            load_pair<T, kVecOK>(target + rr, draft + rr, V, base, qs != 0.f, zt, zd);
-        }
-        float ls = 0.f;
-#pragma unroll
-        for (int i = 0; i < kVec; ++i) {
-            wt[i] = draw_weight(zt[i], zd[i], mt, md, k, ps, qs);
-            ls += wt[i];
-        }
-        double incl2 = ls;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const double yv = __shfl_up(incl2, o);
-            if (lane >= o) incl2 += yv;
-        }
-        double acc = s_base + incl2 - ls;
-        int cand = INT_MAX, lastpos = -1;
-#pragma unroll
-        for (int i = 0; i < kVec; ++i) {
-            acc += wt[i];
-            if (wt[i] > 0.f) {
-                lastpos = base + i;
-                if (cand == INT_MAX && acc > thr) cand = base + i;
+            __syncthreads();
+            if (t == 0) out_tokens[seq + na] = (s_found >= 0 && s_found < V) ? s_found : 0;
+        } else if (owner < 0 && rank == 0) {
+            // no residual mass at all (a zero-probability event in exact arithmetic): the token with
+            // the largest p(x) - c q(x), lowest index on ties
+            float bv = -INFINITY;
+            int bi = INT_MAX;
+            for (int x = t; x < V; x += kThreads) {
+                const float zt = Elem<T>::load(target + rr, x);
+                const float zd = (qs != 0.f) ? Elem<T>::load(draft + rr, x) : -INFINITY;
+                const float d = __builtin_amdgcn_exp2f((zt - mt) * k) * ps - __builtin_amdgcn_exp2f((zd - md) * k) * qs;
+                argmax_merge(bv, bi, d, x);
             }
-        }
-        int y = -1;
-        const uint64_t hit = __ballot(cand != INT_MAX);
-        if (hit) {
-            y = __shfl(cand, __ffsll(static_cast<unsigned long long>(hit)) - 1);
-        } else {
-            const uint64_t pos = __ballot(lastpos >= 0);
-            if (pos) y = __shfl(lastpos, 63 - __clzll(static_cast<long long>(pos)));
-        }
-        if (lane == 0) s_found = y;
-    }
-    __syncthreads();
-    int y = s_found;
-    if (y < 0) {
-        // no residual mass at all (a zero-probability event in exact arithmetic): the token with
-        // the largest p(x) - c q(x), lowest index on ties
-        float bv = -INFINITY;
-        int bi = INT_MAX;
-        for (int x = t; x < V; x += kWalkThreads) {
-            const float zt = Elem<T>::load(target + rr, x);
-            const float zd = (qs != 0.f) ? Elem<T>::load(draft + rr, x) : -INFINITY;
-            const float d = __builtin_amdgcn_exp2f((zt - mt) * k) * ps - __builtin_amdgcn_exp2f((zd - md) * k) * qs;
-            argmax_merge(bv, bi, d, x);
-        }
-        wave_argmax(bv, bi);
-        __shared__ float pv[kWalkWaves];
-        __shared__ int pi[kWalkWaves];
-        if (lane == 0) { pv[w] = bv; pi[w] = bi; }
-        __syncthreads();
-        if (t == 0) {
-            for (int i = 1; i < kWalkWaves; ++i) argmax_merge(pv[0], pi[0], pv[i], pi[i]);
-            s_found = (pi[0] >= 0 && pi[0] < V) ? pi[0] : 0;
+            wave_argmax(bv, bi);
+            if (lane == 0) { pv[w] = bv; pi[w] = bi; }
+            __syncthreads();
+            if (t == 0) {
+                for (int i = 1; i < kWaves; ++i) argmax_merge(pv[0], pi[0], pv[i], pi[i]);
+                out_tokens[seq + na] = (pi[0] >= 0 && pi[0] < V) ? pi[0] : 0;
+            }
         }
         __syncthreads();
-        y = s_found;
+        if (s_to && t == 0) {
+            atomicOr(err, 1u);
+            if (rank == 0) accept_len[b] = -2;
+        }
     }
-    if (t == 0) out_tokens[seq + na] = y;
+}
+
+// ---------------------------------------------------------------------------------- host side
+
+int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cus[dev]) {
+        hipDeviceProp_t prop;
+        cus[dev] = (hipGetDeviceProperties(&prop, dev) == hipSuccess) ? prop.multiProcessorCount : 256;
+    }
+    return cus[dev];
+}
+
+int team_size(int B) {
+    const int cus = device_cus();
+    return std::max(1, std::min(kMaxTeam, cus / std::max(B, 1)));
+}
+
+template <typename T>
+int chunks_of(int V) { return (V + item_elems<T>() - 1) / item_elems<T>(); }
+
+uint32_t next_tag() {
+    // distinct for 2^31 consecutive launches, never 0, away from small integers
+    static std::atomic<uint32_t> counter{0x2545F491u};
+    const uint32_t c = counter.fetch_add(1u, std::memory_order_relaxed);
+    return (c * 0x9E3779B1u) | 0x80000000u;
+}
+
+template <typename T, bool kGreedy, bool kVecOK>
+hipError_t launch_kernel(const AcceptArgs& a, hipStream_t stream) {
+    int nchunk = chunks_of<T>(a.V);
+    int P = team_size(a.B);
+    const AcceptLayout lay(a.B, a.n1, nchunk, P);
+    char* ws = static_cast<char*>(a.workspace);
+    uint64_t* statw = reinterpret_cast<uint64_t*>(ws + lay.stat);
+    uint64_t* partw = reinterpret_cast<uint64_t*>(ws + lay.part);
+    uint32_t* err = reinterpret_cast<uint32_t*>(ws + lay.err);
+    const void* fn = reinterpret_cast<const void*>(&accept_kernel<T, kGreedy, kVecOK>);
+    static int per_cu = -1;
+    if (per_cu < 0) {
+        int nb = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kThreads, 0) != hipSuccess || nb < 1) nb = 1;
+        per_cu = nb;
+    }
+    const int capacity = per_cu * device_cus();
+    const int nteams = std::max(1, std::min(a.B, capacity / P));
+    const int grid = nteams * P;
+
+    const T* target = static_cast<const T*>(a.target);
+    const T* draft = static_cast<const T*>(a.draft);
+    int B = a.B, n1 = a.n1, V = a.V;
+    double invT = kGreedy ? 0.0 : 1.0 / static_cast<double>(a.temperature);
+    float k = kGreedy ? 0.f : static_cast<float>(1.4426950408889634 * invT);   // log2(e) / T
+    uint64_t seed = a.seed, offset = a.offset;
+    uint32_t tag = next_tag();
+    const int32_t* tokens = a.tokens;
+    const int32_t* parent = a.parent;
+    int32_t* accept_len = a.accept_len;
+    int32_t* out_tokens = a.out_tokens;
+    int32_t* out_nodes = a.out_nodes;
+    float* p_tok = a.p_tok;
+    float* q_tok = a.q_tok;
+    void* args[] = {&target, &draft, &tokens, &parent, &B, &n1, &V, &nchunk, &P, &k, &invT, &seed, &offset,
+                    &tag, &statw, &partw, &err, &accept_len, &out_tokens, &out_nodes, &p_tok, &q_tok};
+    (void)args;
+    hipLaunchKernelGGL((accept_kernel<T, kGreedy, kVecOK>), dim3(grid), dim3(kThreads), 0, stream, target, draft,
+                       tokens, parent, B, n1, V, nchunk, P, k, invT, seed, offset, tag, statw, partw, err,
+                       accept_len, out_tokens, out_nodes, p_tok, q_tok);
+    return hipGetLastError();
 }
 
 template <typename T, bool kVecOK>
 hipError_t launch_typed(const AcceptArgs& a, hipStream_t stream) {
-    constexpr int CH = chunk_elems<T>();
-    const int nchunk = (a.V + CH - 1) / CH;
-    const AcceptLayout lay(a.B, a.n1, nchunk);
-    float4* stats = reinterpret_cast<float4*>(static_cast<char*>(a.workspace) + lay.stats);
-    const T* target = static_cast<const T*>(a.target);
-    const T* draft = static_cast<const T*>(a.draft);
-    const bool greedy = a.temperature == 0.f;
-    const double invT = greedy ? 0.0 : 1.0 / static_cast<double>(a.temperature);
-    const float k = greedy ? 0.f : static_cast<float>(1.4426950408889634 * invT);   // log2(e) / T
-    const dim3 sgrid(nchunk, a.n1, a.B);
-    const bool all_draft = static_cast<double>(a.B) * a.n1 * a.V * sizeof(T) <= kAllDraftBytes;
-    if (greedy) {
-        hipLaunchKernelGGL((accept_stats_kernel<T, true, kVecOK, false>), sgrid, dim3(kStatThreads), 0, stream,
-                           target, draft, a.parent, a.n1, a.V, nchunk, k, stats);
-        hipLaunchKernelGGL((accept_finish_kernel<T, true, kVecOK>), dim3(a.B), dim3(kWalkThreads), 0, stream,
-                           target, draft, a.tokens, a.parent, a.n1, a.V, nchunk, k, invT, a.seed, a.offset,
-                           stats, a.accept_len, a.out_tokens, a.out_nodes, a.p_tok, a.q_tok);
-    } else {
-        if (all_draft)
-            hipLaunchKernelGGL((accept_stats_kernel<T, false, kVecOK, true>), sgrid, dim3(kStatThreads), 0,
-                               stream, target, draft, a.parent, a.n1, a.V, nchunk, k, stats);
-        else
-            hipLaunchKernelGGL((accept_stats_kernel<T, false, kVecOK, false>), sgrid, dim3(kStatThreads), 0,
-                               stream, target, draft, a.parent, a.n1, a.V, nchunk, k, stats);
-        hipLaunchKernelGGL((accept_finish_kernel<T, false, kVecOK>), dim3(a.B), dim3(kWalkThreads), 0, stream,
-                           target, draft, a.tokens, a.parent, a.n1, a.V, nchunk, k, invT, a.seed, a.offset,
-                           stats, a.accept_len, a.out_tokens, a.out_nodes, a.p_tok, a.q_tok);
-    }
-    return hipGetLastError();
+    if (a.temperature == 0.f) return launch_kernel<T, true, kVecOK>(a, stream);
+    return launch_kernel<T, false, kVecOK>(a, stream);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -694,9 +842,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 }  // namespace
 
 size_t accept_workspace_bytes(int B, int n1, int V, bool bf16) {
-    const int CH = bf16 ? chunk_elems<uint16_t>() : chunk_elems<float>();
-    const int nchunk = (V + CH - 1) / CH;
-    return AcceptLayout(B, n1, nchunk).total;
+    const int nchunk = bf16 ? chunks_of<uint16_t>(V) : chunks_of<float>(V);
+    return AcceptLayout(B, n1, nchunk, team_size(B)).total;
 }
 
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream) {
