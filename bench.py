@@ -50,7 +50,7 @@ MFMA_PEAK_TFLOPS = 2500.0
 # HBM traffic of the dominant kernel (attn_decode_kernel<128, 8, 1>) per call on this workload, from
 # two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), each scaled by what the same
 # counter reads for a 256 MiB device-to-device copy (FETCH_SIZE 131084.0 KiB -> x1.99982,
-# WRITE_SIZE 262144.0 KiB -> x1.0).  Summaries and commands: profiles/attn_decode_chain_pmc.md.
+# WRITE_SIZE 262144.0 KiB -> x1.0).  Summaries and commands: profiles/chain_step_pmc.md.
 # Valid only for the kernel sources it was measured on (their SHA-256 below); null otherwise.
 ATTN_TRAFFIC = {
     "sources": ["draft_verify_sampling_specv_amd/csrc/attn_decode.hip",
@@ -255,7 +255,7 @@ def main():
                      "bytes_per_call": ab, "ms_per_call": ms_attn},
         "roofline_accept": {"bound": "hbm", "achieved": acc_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": acc_gbs / HBM_PEAK_GBS, "bytes_per_call": cb, "ms_per_call": ms_accept,
-                            "kernel": "specv_accept_resample (accept_stats + accept_finish)"},
+                            "kernel": "accept_kernel<bf16> (specv_accept_resample, one launch)"},
         "accept_only_positions_per_s": positions / (ms_accept * 1e-3),
         "ms_mask": ms_mask,
         "ms_greedy_accept": ms_greedy,

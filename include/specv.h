@@ -162,7 +162,12 @@ size_t specv_attn_workspace_bytes(int32_t B, int32_t K, int32_t Hq, int32_t Hkv,
  *                 uniform if the walk ends there; a word w maps to
  *                 (2 * (w >> 12) + 1) * 2^-53.  Advance offset once per call.
  *   accept_len    [B] int32: number of accepted draft nodes; -1 if the parent
- *                 array is invalid or a draft token is outside [0, V)
+ *                 array is invalid or a draft token is outside [0, V); -2 if
+ *                 the sequence was not finished because the workgroups that
+ *                 share it could not all run at once (another process holding
+ *                 compute units); each wait gives up after about 0.5 s, so the
+ *                 call always completes; the other outputs of a -2 sequence
+ *                 are then unspecified.
  *   out_nodes     [B][K+1] int32: accepted node ids from the first level down,
  *                 then -1
  *   out_tokens    [B][K+1] int32: the accepted tokens, then the resampled /
@@ -171,6 +176,10 @@ size_t specv_attn_workspace_bytes(int32_t B, int32_t K, int32_t Hq, int32_t Hkv,
  *                 q_parent(v)(tokens[v]) for every v >= 1; NaN at v == 0, at
  *                 T == 0 and for invalid sequences
  *   workspace / workspace_bytes: at least specv_accept_workspace_bytes(...)
+ *
+ * Ownership: every pointer is device memory owned by the caller; the call only
+ * enqueues work on `stream` and returns.  Calls that share a workspace must be
+ * ordered on one stream.
  *
  * Errors: SPECV_ERR_INVALID_ARG (NULL pointer, B < 0, K < 0,
  * K + 1 > SPECV_MAX_NODES, V < 1 or V > SPECV_MAX_VOCAB, T < 0 or not finite,
