@@ -762,19 +762,9 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
 
 // ---------------------------------------------------------------------------------- host side
 
-int device_cus() {
-    static int cus[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cus[dev]) {
-        hipDeviceProp_t prop;
-        cus[dev] = (hipGetDeviceProperties(&prop, dev) == hipSuccess) ? prop.multiProcessorCount : 256;
-    }
-    return cus[dev];
-}
 
 int team_size(int B) {
-    const int cus = device_cus();
+    const int cus = device_cu_count();
     return std::max(1, std::min(kMaxTeam, cus / std::max(B, 1)));
 }
 
@@ -804,7 +794,7 @@ hipError_t launch_kernel(const AcceptArgs& a, hipStream_t stream) {
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kThreads, 0) != hipSuccess || nb < 1) nb = 1;
         per_cu = nb;
     }
-    const int capacity = per_cu * device_cus();
+    const int capacity = per_cu * device_cu_count();
     const int nteams = std::max(1, std::min(a.B, capacity / P));
     const int grid = nteams * P;
 

@@ -17,12 +17,12 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    // round-to-nearest-even fp32 -> bf16, two values per word
-    uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
-    a = (a + 0x7fffu + ((a >> 16) & 1u)) >> 16;
-    b = (b + 0x7fffu + ((b >> 16) & 1u)) & 0xffff0000u;
-    return a | b;
+    // round-to-nearest-even fp32 -> bf16, two values per word (one v_cvt_pk_bf16_f32)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 }  // namespace attn

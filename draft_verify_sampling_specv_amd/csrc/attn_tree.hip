@@ -1,20 +1,32 @@
-// Tree-attention verify, general case (many query rows per KV head: big trees x GQA groups)
+// Tree-attention verify, general case: many query rows per KV head (big trees x GQA groups)
 // ([SD-EAGLE] "Tree Attention Verification"; [PTD] Method 4, "Verification").
-//   * grid (split, KV head x row group, sequence).  The query rows of one KV head are the
-//     G x (K+1) pairs (node, head in group), row r = node * G + g, cut into 32-row blocks; one
-//     wave per row block.  The key range ctx_len + K + 1 is cut into 32-key tiles and the tiles
-//     into `nsplit` contiguous splits (flash-decoding style), one workgroup per split.
-//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K is the A operand (from LDS), Q^T the B operand
-//     (kept in registers), so the 32x32 result puts one query row in each lane column and the
-//     row max / row sum need one cross-half shuffle.
-//   * O^T += V^T P^T with the same instruction; P stays in registers (the accumulator layout of
-//     S^T is reused as the B operand with a matching key permutation), V is staged in LDS
-//     transposed ([d][key]) so each lane reads 4 consecutive keys per 8-byte LDS read.
-//   * K/V tiles are loaded once per workgroup with coalesced 16-byte global loads, double
-//     buffered in LDS (the next tile's loads are in flight while the current one is computed).
-//   * The tree mask is applied only on tiles that reach past the context.
-//   * Each split writes an unnormalised partial (O, running max, sum); a combine kernel merges the
-//     splits (log-sum-exp weights), writes bf16 O and the natural-log LSE.
+//
+// The query rows of one KV head are the G x (K+1) pairs (node, head in group), row r = node * G + g,
+// cut into 32-row blocks.  These shapes are MFMA-bound (about G (K+1) flops per K/V byte):
+//   * a workgroup is 8 waves (two per SIMD) and owns one (sequence, KV head, key split, row
+//     group); a row group is up to 8 row blocks, one per wave; a wave keeps its block's Q^T
+//     operands and O^T accumulators in registers;
+//   * the split's keys go through an LDS ring of 64-key tiles filled by direct global-to-LDS
+//     transfers (no registers, no LDS store instructions), one tile in flight while one is
+//     computed and the next being issued, one barrier per tile;
+//   * K sits in LDS in MFMA operand order, so each S^T = K Q^T operand is one conflict-free
+//     16-byte read; S^T is computed on v_mfma_f32_32x32x16_bf16 as two 32-key blocks (two
+//     independent accumulation chains), and each lane ends up holding one query row;
+//   * O^T += V^T P^T on the same instruction: P stays in registers (the accumulator layout of S^T
+//     reused as the B operand under a matching key permutation); the V^T operands come from
+//     transposing LDS reads (ds_read_b64_tr_b16) of row-major V, laid out so that the four keys of
+//     one read sit in different bank groups and every offset but the lane's own is a constant;
+//   * online softmax in base 2 with the scale folded into the exponent and a lazy reference max:
+//     p = exp2(s c2 - m) is taken against the row's current reference without a per-tile max, and
+//     the reference moves (max, rescale, recompute) only when some lane's p sum would exceed 2^20;
+//   * with one key split the workgroup writes the final bf16 output; with several, each split
+//     writes its output normalised by its own sum (bf16) and its (max, sum), and a combine kernel
+//     merges them;
+//   * the workgroups of one (sequence, KV head, split) that differ only in row group are given
+//     block ids on the same XCD, adjacent in dispatch order, so their K/V reads share that XCD's
+//     L2.
+
+#include <cmath>
 
 #include "attn_common.h"
 #include "kernels.h"
@@ -23,228 +35,357 @@ namespace specv {
 namespace {
 using namespace attn;
 
-constexpr int kMaxWaves = 8;
+constexpr int kTreeWaves = 8;             // one 32-row block per wave, two waves per SIMD
+constexpr int kTreeThreads = kTreeWaves * kWave;
+constexpr int kTreeTile = 64;             // keys per ring stage: two 32-key S^T blocks
+constexpr int kStages = 3;                // LDS ring depth (tiles)
+constexpr float kLazyMax = 1048576.f;     // 2^20: largest p sum a lane may reach before the reference moves
 
+// One ring stage.
+//   K in MFMA operand order: 1 KB block (st, ks) holds, for lane l, the 8 features 16 ks + 8 (l / 32)
+//   .. of key 32 st + l % 32 -- exactly lane l's A operand of S^T block st at k-step ks.
+//   V as kVT transfers of whole key rows: transfer slot u (1 KB + 64 bytes of padding) holds the
+//   rows r with r % kVT == u, in order of r / kVT.  The PV step reads 4 consecutive keys at a
+//   time with transposing reads; those keys sit in 4 slots 64 bytes apart in bank order, so the
+//   reads are conflict-free.
 template <int D>
-struct Smem {
-    static constexpr int kRow = D + 8;             // K tile row pitch (bf16): 16 bytes of padding
-    static constexpr int kVtRow = kTileKeys + 4;   // V^T tile row pitch (bf16): 8 bytes of padding
-    uint16_t k[2][kTileKeys * kRow];
-    uint16_t vt[2][D * kVtRow];
+struct TreeTiles {
+    static constexpr int kKS = D / 16;                     // k-steps of S^T
+    static constexpr int kKT = 2 * kKS;                    // K transfers per tile
+    static constexpr int kVT = kTreeTile * 2 * D / 1024;   // V transfers per tile
+    static constexpr int kVStride = 1024 + 64;             // bytes per V transfer slot
+    uint16_t k[kStages][kTreeTile * D];
+    uint16_t v[kStages][kVT * kVStride / 2];
 };
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes land at lds + 16 i.
+// (Issued as inline assembly so that the compiler neither waits for these loads at its own LDS
+// reads nor counts them; the tile pipeline waits for them explicitly.)
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(g), "s"(lds) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-struct AttnLayout {
+struct TreePlan {
+    int ngroups;    // row groups per (sequence, KV head): up to kTreeWaves row blocks each
+    int nsplit;     // key splits per (sequence, KV head)
+};
+
+struct TreeLayout {
     size_t opart, ml, total;
-    AttnLayout(int B, int Hkv, int nsplit, int R, int D) {
+    TreeLayout(int B, int Hkv, int nsplit, int R, int D) {
         opart = 0;
-        ml = align256(sizeof(float) * size_t(B) * Hkv * nsplit * R * D);
+        if (nsplit <= 1) {
+            ml = total = 0;
+            return;
+        }
+        ml = align256(sizeof(uint16_t) * size_t(B) * Hkv * nsplit * R * D);
         total = align256(ml + sizeof(float2) * size_t(B) * Hkv * nsplit * R);
     }
 };
 
-struct Plan {
-    int nsplit, nw, groups, rbpg, chunks;
+// The state of the row block a wave owns.
+template <int D>
+struct WaveRow {
+    bf16x8_t q[D / 16];             // Q^T operands: row 32 rb + col, features 16 ks + 8 h ..
+    f32x16_t o[D / 32];             // O^T accumulators, block c = features 32 c + i
+    float m, l;                     // reference max (base 2, scaled) and this half-wave's sum
+    const uint32_t* mrow;           // mask row of this lane's node
 };
 
-template <int D, int NW>
-__global__ void __launch_bounds__(NW * kWave)
-attn_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
-                    const uint16_t* __restrict__ vc, const int32_t* __restrict__ ctx_len,
-                    const uint32_t* __restrict__ mask, int n1, int Hq, int Hkv, int Lmax,
-                    float c2, int nsplit, int groups, int rbpg, float* __restrict__ opart,
-                    float2* __restrict__ mlpart) {
-    constexpr int kChunksPerRow = D / 8;                  // 16-byte chunks per K/V row
-    constexpr int kChunks = kTileKeys * kChunksPerRow;    // per tile, for K and for V
-    constexpr int kDB = D / 32;                           // 32-wide d blocks of O^T
-    constexpr int kKS = D / 16;                           // k-steps of S^T = K Q^T
-    constexpr int kThreads = NW * kWave;
-    constexpr int MAXC = (kChunks + kThreads - 1) / kThreads;   // 16-byte chunks per thread
-    __shared__ Smem<D> sm;
+// Issue this wave's share of tile t's transfers into ring stage `stage`: kKT transfers of K (one
+// per (32-key block, k-step)) and kVT of V (1024 / (2 D) whole rows each), dealt to the waves.
+// Keys past the sequence read its last key (finite data, masked out by the softmax).
+template <int D>
+__device__ __forceinline__ void issue_tile(TreeTiles<D>& sm, int stage, const uint16_t* kbase,
+                                           const uint16_t* vbase, int t, int Ltot, int w, int lane) {
+    using T = TreeTiles<D>;
+    constexpr int kCpr = D / 8;                 // 16-byte chunks per V row
+    static_assert((T::kKT + T::kVT) % kTreeWaves == 0, "whole transfers per wave");
+#pragma unroll
+    for (int x = 0; x < (T::kKT + T::kVT) / kTreeWaves; ++x) {
+        const int j = w + x * kTreeWaves;
+        const uint16_t* g;
+        const uint16_t* dst;
+        if (j < T::kKT) {
+            const int st = j / T::kKS, ks = j % T::kKS;
+            const int key = min(t * kTreeTile + 32 * st + (lane & 31), Ltot - 1);
+            g = kbase + static_cast<int64_t>(key) * D + 16 * ks + 8 * (lane >> 5);
+            dst = sm.k[stage] + j * (kWave * 8);
+        } else {
+            const int u = j - T::kKT;           // rows u, u + kVT, ...
+            const int key = min(t * kTreeTile + (lane / kCpr) * T::kVT + u, Ltot - 1);
+            g = vbase + static_cast<int64_t>(key) * D + 8 * (lane % kCpr);
+            dst = sm.v[stage] + u * (T::kVStride / 2);
+        }
+        dma16(g, __builtin_amdgcn_readfirstlane(lds_address(dst)));
+    }
+}
 
-    const int split = blockIdx.x;
-    const int kv = blockIdx.y / groups, grp = blockIdx.y % groups;
-    const int b = blockIdx.z;
+// One 64-key tile for this wave's row block.
+template <int D>
+__device__ __forceinline__ void tile_compute(WaveRow<D>& wr, const uint16_t* kt, const uint16_t* vt,
+                                             int kb, int L, int Ltot, int lane, float c2) {
+    using T = TreeTiles<D>;
+    constexpr int kKS = T::kKS;
+    constexpr int kF = D / 32;
+    const int h = lane >> 5;
+    f32x16_t s[2];
+
+    // S^T = K Q^T for the two 32-key blocks (interleaved, independent chains)
+    auto compute_s = [&]() {
+        s[0] = f32x16_t{};
+        s[1] = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(&kt[((st * kKS + ks) * kWave + lane) * 8]));
+                s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wr.q[ks], s[st], 0, 0, 0);
+            }
+        // s[st][r] is key kb + 32 st + 8 (r / 4) + 4 h + r % 4 of this lane's row
+        if (kb + kTreeTile > L) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kb + 32 * st + 8 * (r / 4) + 4 * h + (r % 4);
+                    bool vis = key < L;
+                    if (!vis && key < Ltot) {
+                        const int jj = key - L;
+                        vis = (wr.mrow[jj >> 5] >> (jj & 31)) & 1u;
+                    }
+                    if (!vis) s[st][r] = -INFINITY;
+                }
+        }
+    };
+    // s := p = exp2(s c2 - m) against the current reference; returns this lane's p sum
+    auto exponentiate = [&]() {
+        const float mref = (wr.m == -INFINITY) ? 0.f : wr.m;
+        float rs = 0.f;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s[st][r] = __builtin_amdgcn_exp2f(fmaf(s[st][r], c2, -mref));
+                rs += s[st][r];
+            }
+        return rs;
+    };
+
+    compute_s();
+    float rs = exponentiate();
+    if (__ballot(!(rs <= kLazyMax) || wr.m == -INFINITY)) {
+        // slow path (first tile of a row, or a score far above the reference): the tile's row
+        // max over both half-waves becomes the reference where it is higher
+        compute_s();
+        float mx = s[0][0];
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[st][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mt = mx * c2;
+        if (mt > wr.m) {
+            const float alpha = __builtin_amdgcn_exp2f(wr.m - mt);    // m = -inf gives 0
+            wr.m = mt;
+            wr.l *= alpha;
+#pragma unroll
+            for (int c = 0; c < kF; ++c) wr.o[c] *= alpha;
+        }
+        rs = exponentiate();
+    }
+    wr.l += rs;
+
+    // P as the B operands of the PV product: k-step (st, ks) covers the keys
+    // 32 st + 16 ks + 8 (e / 4) + 4 h + e % 4 (e = 0..7), the order in which S^T holds them
+    bf16x8_t pb[2][2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            uint4 pw;
+            pw.x = pack_bf16x2(s[st][8 * ks + 0], s[st][8 * ks + 1]);
+            pw.y = pack_bf16x2(s[st][8 * ks + 2], s[st][8 * ks + 3]);
+            pw.z = pack_bf16x2(s[st][8 * ks + 4], s[st][8 * ks + 5]);
+            pw.w = pack_bf16x2(s[st][8 * ks + 6], s[st][8 * ks + 7]);
+            pb[st][ks] = as_bf16x8(pw);
+        }
+
+    // O^T += V^T P^T.  The V^T operand of block c (lane: feature 32 c + col, the 8 keys of the
+    // k-step) comes from two transposing reads of 4 keys each: within each group of 16 lanes,
+    // lane 16 g + 4 a + b receives element b of the 8 bytes addressed by lanes 16 g + a, +4, +8,
+    // +12, so lane x addresses key (.. + x % 16 / 4) at features 32 c + 16 (x / 16 % 2) + 4 (x % 4).
+    // Key r = 32 st + 16 ks + 8 half + 4 h + j sits in slot r % kVT at position r / kVT.
+    typedef __attribute__((address_space(3))) const char lds_char;
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const int kj = (lane & 15) >> 2;
+    const int fo = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    lds_char* vb = (lds_char*)(vt) + (4 * h + kj) * T::kVStride + 2 * fo;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int c = 0; c < kF; ++c) {
+                v4i16 part[2];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    int off;
+                    if constexpr (T::kVT == 16) off = 8 * half * T::kVStride + (2 * st + ks) * (2 * D);   // D = 128
+                    else off = (4 * st + 2 * ks + half) * (2 * D);                                     // D = 64
+                    part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb + off + 64 * c));
+                }
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                wr.o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st][ks], wr.o[c], 0, 0, 0);
+            }
+}
+
+// The split's tiles [t0, t1) through the LDS ring: while tile tt is computed, tile tt + 1 is in
+// flight and tile tt + 2 is being issued.  The barrier at the top of each tile both publishes
+// tile tt (every wave has waited for its own share of it) and frees the stage of tile tt - 1.
+template <int D, bool kActive>
+__device__ __forceinline__ void run_tiles(WaveRow<D>& wr, TreeTiles<D>& sm, const uint16_t* kbase,
+                                          const uint16_t* vbase, int t0, int t1, int L, int Ltot,
+                                          int w, int lane, float c2) {
+    using T = TreeTiles<D>;
+    constexpr int kPerTile = (T::kKT + T::kVT) / kTreeWaves;    // transfers per wave per tile
+    if (t0 >= t1) return;                                      // (workgroup-uniform)
+    // Let the compiler see every earlier load (Q operands, ...) complete here: it cannot count
+    // the ring's transfers, so a load it still believed pending inside the loop would make it
+    // wait for all of them.
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int i = 0; i < kStages - 1; ++i) issue_tile<D>(sm, i, kbase, vbase, min(t0 + i, t1 - 1), Ltot, w, lane);
+    for (int tt = t0; tt < t1; ++tt) {
+        const int i = tt - t0;
+        wait_vmcnt<(kStages - 2) * kPerTile>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue_tile<D>(sm, (i + kStages - 1) % kStages, kbase, vbase, min(tt + kStages - 1, t1 - 1), Ltot, w, lane);
+        if constexpr (kActive)
+            tile_compute<D>(wr, sm.k[i % kStages], sm.v[i % kStages], tt * kTreeTile, L, Ltot, lane, c2);
+    }
+    wait_vmcnt<0>();      // the ring's last (redundant) transfers land before the workgroup ends
+}
+
+template <int D>
+__global__ void __launch_bounds__(kTreeThreads)
+attn_tree_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+                 const uint16_t* __restrict__ vc, const int32_t* __restrict__ ctx_len,
+                 const uint32_t* __restrict__ mask, int n1, int Hq, int Hkv, int Lmax, float c2,
+                 int nsplit, int ngroups, int xcd_map, uint16_t* __restrict__ out, float* __restrict__ lse,
+                 uint16_t* __restrict__ opart, float2* __restrict__ mlpart) {
+    constexpr int kKS = D / 16;
+    constexpr int kF = D / 32;
+    __shared__ TreeTiles<D> sm;
+
+    // block id -> (unit = (sequence, KV head, split), row group)
+    int unit, grp;
+    if (xcd_map) {
+        // dispatch deals block ids to the 8 XCDs round-robin: keep the row groups of a unit on one
+        // XCD and adjacent in that XCD's dispatch order
+        const int x = blockIdx.x & 7, s = blockIdx.x >> 3;
+        unit = (s / ngroups) * 8 + x;
+        grp = s % ngroups;
+    } else {
+        unit = blockIdx.x / ngroups;
+        grp = blockIdx.x % ngroups;
+    }
+    const int split = unit % nsplit;
+    const int kv = (unit / nsplit) % Hkv;
+    const int b = unit / (nsplit * Hkv);
+
     const int G = Hq / Hkv, R = G * n1;
     const int RB = (R + 31) / 32;
-    constexpr int nthreads = kThreads;
+    const int rb0 = grp * RB / ngroups, rb1 = (grp + 1) * RB / ngroups;   // this group's row blocks
     const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int h = lane / 32, col = lane % 32;
-    const int rb = grp * rbpg + w;
-    const bool wave_rows = rb < RB && w < rbpg;
-    const int row = rb * 32 + col;
-    const bool row_ok = wave_rows && row < R;
+    const int h = lane >> 5, col = lane & 31;
+    const bool active = rb0 + w < rb1;                                    // (wave-uniform)
     const int words = (n1 + 31) >> 5;
 
     const int L = ctx_len[b];
     const bool seq_ok = L >= 0 && L + n1 <= Lmax;
     const int Ltot = L + n1;
-    const int ntiles = seq_ok ? (Ltot + kTileKeys - 1) / kTileKeys : 0;
+    const int ntiles = seq_ok ? (Ltot + kTreeTile - 1) / kTreeTile : 0;
     const int tps = (ntiles + nsplit - 1) / nsplit;
-    const int t0 = split * tps, t1 = min(ntiles, t0 + tps);
-    const int64_t pbase = (static_cast<int64_t>(b) * Hkv + kv) * nsplit + split;
+    const int t0 = min(ntiles, split * tps), t1 = min(ntiles, t0 + tps);
 
-    // query row of this lane: node i, head kv*G + g
-    const int node = row_ok ? row / G : 0;
-    const int g = row_ok ? row - node * G : 0;
-    const uint32_t* mrow = mask + (static_cast<int64_t>(b) * n1 + node) * words;
-
-    bf16x8_t qreg[kKS];
+    const int row = (rb0 + w) * 32 + col;
+    const bool ok = active && row < R;
+    const int node = ok ? row / G : 0;
+    const int g = ok ? row - node * G : 0;
+    WaveRow<D> wr;
+    wr.mrow = mask + (static_cast<int64_t>(b) * n1 + node) * words;
     {
-        const uint16_t* qp = q + ((static_cast<int64_t>(b) * n1 + node) * Hq + kv * G + g) * D;
+        const uint16_t* qp = q + ((static_cast<int64_t>(b) * n1 + node) * Hq + kv * G + g) * D + 8 * h;
 #pragma unroll
-        for (int s = 0; s < kKS; ++s) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (row_ok) v = *reinterpret_cast<const uint4*>(qp + 16 * s + 8 * h);
-            qreg[s] = as_bf16x8(v);
-        }
+        for (int ks = 0; ks < kKS; ++ks)
+            wr.q[ks] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(qp + 16 * ks) : make_uint4(0, 0, 0, 0));
     }
+    wr.m = -INFINITY;
+    wr.l = 0.f;
+#pragma unroll
+    for (int c = 0; c < kF; ++c) wr.o[c] = f32x16_t{};
 
     const uint16_t* kbase = kc + (static_cast<int64_t>(b) * Hkv + kv) * Lmax * D;
     const uint16_t* vbase = vc + (static_cast<int64_t>(b) * Hkv + kv) * Lmax * D;
+    // every wave runs the same tile loop (same transfers and barriers); only active waves compute
+    if (active) run_tiles<D, true>(wr, sm, kbase, vbase, t0, t1, L, Ltot, w, lane, c2);
+    else run_tiles<D, false>(wr, sm, kbase, vbase, t0, t1, L, Ltot, w, lane, c2);
 
-    uint4 kpre[MAXC], vpre[MAXC];
-    auto load_tile = [&](int t) {
-#pragma unroll
-        for (int j = 0; j < MAXC; ++j) {
-            const int c = threadIdx.x + j * nthreads;
-            const int key = t * kTileKeys + c / kChunksPerRow;
-            const int d0 = (c % kChunksPerRow) * 8;
-            kpre[j] = make_uint4(0, 0, 0, 0);
-            vpre[j] = make_uint4(0, 0, 0, 0);
-            if (c < kChunks && key < Ltot) {
-                kpre[j] = *reinterpret_cast<const uint4*>(kbase + static_cast<int64_t>(key) * D + d0);
-                vpre[j] = *reinterpret_cast<const uint4*>(vbase + static_cast<int64_t>(key) * D + d0);
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < MAXC; ++j) {
-            const int c = threadIdx.x + j * nthreads;
-            if (c < kChunks) {
-                const int key = c / kChunksPerRow;
-                const int d0 = (c % kChunksPerRow) * 8;
-                *reinterpret_cast<uint4*>(&sm.k[buf][key * Smem<D>::kRow + d0]) = kpre[j];
-                const uint32_t vw[4] = {vpre[j].x, vpre[j].y, vpre[j].z, vpre[j].w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    sm.vt[buf][(d0 + e) * Smem<D>::kVtRow + key] =
-                        static_cast<uint16_t>((e & 1) ? (vw[e >> 1] >> 16) : (vw[e >> 1] & 0xffffu));
-            }
-        }
-    };
-
-    f32x16_t o[kDB];
-#pragma unroll
-    for (int i = 0; i < kDB; ++i) o[i] = f32x16_t{};
-    float m = -INFINITY;   // running max of scaled (base-2) scores of this lane's row
-    float l = 0.f;
-
-    if (t0 < t1) {
-        load_tile(t0);
-        store_tile(0);
+    // epilogue: lane (col, h) holds, in block c register 4 rr + e, feature 32 c + 8 rr + 4 h + e of
+    // its row; l is the sum over this half-wave's keys, the row's is the sum over both halves
+    wr.l += __shfl_xor(wr.l, 32);
+    if (!ok) return;
+    const float l = wr.l;
+    uint16_t* op;
+    float inv;
+    if (nsplit == 1) {
+        const int64_t orow = (static_cast<int64_t>(b) * n1 + node) * Hq + kv * G + g;
+        op = out + orow * D;
+        inv = seq_ok ? 1.f / l : NAN;
+        if (lse && h == 0) lse[orow] = seq_ok ? (wr.m + log2f(l)) * kLn2 : NAN;
+    } else {
+        const int64_t prow = static_cast<int64_t>(unit) * R + row;
+        op = opart + prow * D;
+        inv = l > 0.f ? 1.f / l : 0.f;
+        if (h == 0) mlpart[prow] = make_float2(wr.m, l);
     }
-    __syncthreads();
-    for (int t = t0; t < t1; ++t) {
-        const int buf = (t - t0) & 1;
-        if (t + 1 < t1) load_tile(t + 1);
-        if (wave_rows) {
-            // S^T (keys x rows) = K Q^T
-            f32x16_t s = f32x16_t{};
-            const uint16_t* kt = sm.k[buf];
 #pragma unroll
-            for (int ks = 0; ks < kKS; ++ks) {
-                const uint4 a = *reinterpret_cast<const uint4*>(&kt[col * Smem<D>::kRow + 16 * ks + 8 * h]);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qreg[ks], s, 0, 0, 0);
-            }
-            // s[r] holds key t*32 + 8*(r/4) + 4*h + r%4 of row `row`
-            const int kb = t * kTileKeys;
-            if (kb + kTileKeys > L) {
+    for (int c = 0; c < kF; ++c)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kb + 8 * (r / 4) + 4 * h + (r % 4);
-                    bool vis = key < L;
-                    if (!vis && key < Ltot) {
-                        const int jj = key - L;
-                        vis = (mrow[jj >> 5] >> (jj & 31)) & 1u;
-                    }
-                    if (!vis) s[r] = -INFINITY;
-                }
-            }
-            float mx = s[0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = fmaxf(m, mx * c2);
-            const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-            const float alpha = __builtin_amdgcn_exp2f(m - mref);
-            float p[16];
-            float rs = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -mref));
-                rs += p[r];
-            }
-            rs += __shfl_xor(rs, 32);
-            l = l * alpha + rs;
-            m = mnew;
-            if (__ballot(alpha != 1.f)) {
-#pragma unroll
-                for (int i = 0; i < kDB; ++i) o[i] *= alpha;
-            }
-            // O^T (d x rows) += V^T P^T
-            const uint16_t* vt = sm.vt[buf];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                uint4 pw;
-                pw.x = pack_bf16x2(p[8 * ks + 0], p[8 * ks + 1]);
-                pw.y = pack_bf16x2(p[8 * ks + 2], p[8 * ks + 3]);
-                pw.z = pack_bf16x2(p[8 * ks + 4], p[8 * ks + 5]);
-                pw.w = pack_bf16x2(p[8 * ks + 6], p[8 * ks + 7]);
-                const bf16x8_t pb = as_bf16x8(pw);
-#pragma unroll
-                for (int db = 0; db < kDB; ++db) {
-                    const uint16_t* vr = &vt[(db * 32 + col) * Smem<D>::kVtRow + 16 * ks + 4 * h];
-                    const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-                    const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, o[db], 0, 0, 0);
-                }
-            }
+        for (int rr = 0; rr < 4; ++rr) {
+            uint2 st;
+            st.x = pack_bf16x2(wr.o[c][4 * rr + 0] * inv, wr.o[c][4 * rr + 1] * inv);
+            st.y = pack_bf16x2(wr.o[c][4 * rr + 2] * inv, wr.o[c][4 * rr + 3] * inv);
+            *reinterpret_cast<uint2*>(op + 32 * c + 8 * rr + 4 * h) = st;
         }
-        if (t + 1 < t1) store_tile(buf ^ 1);
-        __syncthreads();
-    }
-
-    if (row_ok) {
-        const int64_t prow = pbase * R + row;
-        float* op = opart + prow * D;
-#pragma unroll
-        for (int db = 0; db < kDB; ++db)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int d0 = db * 32 + 8 * rr + 4 * h;
-                *reinterpret_cast<float4*>(op + d0) =
-                    make_float4(o[db][4 * rr + 0], o[db][4 * rr + 1], o[db][4 * rr + 2], o[db][4 * rr + 3]);
-            }
-        if (h == 0) mlpart[prow] = make_float2(m, l);
-    }
 }
 
-// Merge the splits of one output row: weights 2^(m_s - M) l_s; out = sum w O_s / sum w l_s.
-template <typename OutT>
+// Merge the key splits of one output row: weights l_s 2^(m_s - M) on the split outputs O_s (each
+// already divided by its own l_s): out = sum w_s O_s / sum w_s; lse = M + log2(sum_s l_s 2^(m_s - M)).
 __global__ void __launch_bounds__(256)
-attn_combine_kernel(const float* __restrict__ opart, const float2* __restrict__ mlpart,
-                    const int32_t* __restrict__ ctx_len, int B, int n1, int Hq, int Hkv, int D,
-                    int Lmax, int nsplit, OutT* __restrict__ out, float* __restrict__ lse) {
+attn_tree_combine_kernel(const uint16_t* __restrict__ opart, const float2* __restrict__ mlpart,
+                         const int32_t* __restrict__ ctx_len, int B, int n1, int Hq, int Hkv, int D,
+                         int Lmax, int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse) {
     const int G = Hq / Hkv, R = G * n1;
-    const int dv = D / 4;
+    const int dv = D / 8;                           // 8 features (16 bytes) per thread
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t total = static_cast<int64_t>(B) * n1 * Hq * dv;
     if (gid >= total) return;
-    const int d0 = static_cast<int>(gid % dv) * 4;
+    const int d0 = static_cast<int>(gid % dv) * 8;
     const int64_t orow = gid / dv;                  // (b, node, head)
     const int hh = static_cast<int>(orow % Hq);
     const int node = static_cast<int>((orow / Hq) % n1);
@@ -252,99 +393,98 @@ attn_combine_kernel(const float* __restrict__ opart, const float2* __restrict__ 
     const int kv = hh / G, g = hh % G;
     const int row = node * G + g;
     const int L = ctx_len[b];
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    float den = 0.f, M = -INFINITY;
     const bool ok = L >= 0 && L + n1 <= Lmax;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float den = 0.f, M = -INFINITY;
+    const int64_t ubase = (static_cast<int64_t>(b) * Hkv + kv) * nsplit;
     if (ok) {
         for (int s = 0; s < nsplit; ++s) {
-            const float2 ml = mlpart[((static_cast<int64_t>(b) * Hkv + kv) * nsplit + s) * R + row];
+            const float2 ml = mlpart[(ubase + s) * R + row];
             if (ml.y > 0.f) M = fmaxf(M, ml.x);
         }
         for (int s = 0; s < nsplit; ++s) {
-            const int64_t prow = ((static_cast<int64_t>(b) * Hkv + kv) * nsplit + s) * R + row;
+            const int64_t prow = (ubase + s) * R + row;
             const float2 ml = mlpart[prow];
             if (!(ml.y > 0.f)) continue;
-            const float wgt = __builtin_amdgcn_exp2f(ml.x - M);
-            const float4 v = *reinterpret_cast<const float4*>(opart + prow * D + d0);
-            acc.x += wgt * v.x; acc.y += wgt * v.y; acc.z += wgt * v.z; acc.w += wgt * v.w;
-            den += wgt * ml.y;
+            const float wgt = ml.y * __builtin_amdgcn_exp2f(ml.x - M);
+            const uint4 v = *reinterpret_cast<const uint4*>(opart + prow * D + d0);
+            const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += wgt * __uint_as_float(x[e] << 16);
+                acc[2 * e + 1] += wgt * __uint_as_float(x[e] & 0xffff0000u);
+            }
+            den += wgt;
         }
     }
     const float inv = ok ? 1.f / den : NAN;
-    const float r[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
-    OutT* op = out + orow * D + d0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        if constexpr (sizeof(OutT) == 2) {
-            const uint32_t u = __float_as_uint(r[e]);
-            op[e] = (r[e] != r[e]) ? static_cast<uint16_t>(0x7fc0u)
-                                   : static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-        } else {
-            op[e] = r[e];
-        }
-    }
+    uint4 st;
+    st.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    st.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    st.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+    st.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+    *reinterpret_cast<uint4*>(out + orow * D + d0) = st;
     if (lse && d0 == 0) lse[orow] = ok ? (M + log2f(den)) * kLn2 : NAN;
 }
 
-Plan make_plan(int B, int n1, int Hq, int Hkv, int D, int Lmax) {
-    const int G = Hq / Hkv, R = G * n1;
-    const int RB = (R + 31) / 32;
-    Plan p;
-    p.groups = (RB + kMaxWaves - 1) / kMaxWaves;
-    p.rbpg = (RB + p.groups - 1) / p.groups;
-    p.nw = 1;
-    while (p.nw < p.rbpg) p.nw *= 2;   // 1, 2, 4 or 8 waves; spare waves only help loading
-    p.chunks = 0;
-    // Splits over the key range: enough workgroups to cover the machine several times over, at
-    // least 4 tiles per split.
-    const int tiles = (Lmax + kTileKeys - 1) / kTileKeys;
-    const int units = B * Hkv * p.groups;
-    int ns = 1;
-    while ((units * ns < 512 || units * ns * p.nw < 2048) && tiles / (ns * 2) >= 4) ns *= 2;
-    p.nsplit = ns;
+// Row groups of at most kTreeWaves blocks (one per wave), balanced.  Key splits: one workgroup
+// fits per compute unit (LDS ring), so the time goes as rounds of resident workgroups x tiles per
+// split; take the number of splits (a power of two, at least 2 tiles each) that minimises that,
+// counting the combine pass as two tiles.
+TreePlan make_plan(int B, int n1, int Hq, int Hkv, int Lmax) {
+    const int RB = ((Hq / Hkv) * n1 + 31) / 32;
+    const int cus = device_cu_count();
+    const int tiles = (Lmax + kTreeTile - 1) / kTreeTile;
+    TreePlan p;
+    p.ngroups = (RB + kTreeWaves - 1) / kTreeWaves;
+    p.nsplit = 1;
+    const long long wgs1 = static_cast<long long>(B) * Hkv * p.ngroups;
+    long long best = -1;
+    for (int ns = 1; ns <= 64 && (ns == 1 || tiles / ns >= 2); ns *= 2) {
+        const long long rounds = (wgs1 * ns + cus - 1) / cus;
+        const long long cost = rounds * ((tiles + ns - 1) / ns) + (ns > 1 ? 2 : 0);
+        if (best < 0 || cost < best) {
+            best = cost;
+            p.nsplit = ns;
+        }
+    }
     return p;
 }
 
-template <int D, int NW>
-void launch_partial(const AttnArgs& a, const Plan& p, float* opart, float2* ml, hipStream_t stream) {
-    const float c2 = a.scale * kLog2e;
-    hipLaunchKernelGGL((attn_partial_kernel<D, NW>), dim3(p.nsplit, a.Hkv * p.groups, a.B),
-                       dim3(p.nw * kWave), 0, stream, static_cast<const uint16_t*>(a.q),
-                       static_cast<const uint16_t*>(a.k_cache), static_cast<const uint16_t*>(a.v_cache),
-                       a.ctx_len, a.mask, a.n1, a.Hq, a.Hkv, a.Lmax, c2, p.nsplit, p.groups, p.rbpg,
-                       opart, ml);
-}
-
 template <int D>
-void dispatch_partial(const AttnArgs& a, const Plan& p, float* opart, float2* ml, hipStream_t stream) {
-    switch (p.nw) {
-        case 1: launch_partial<D, 1>(a, p, opart, ml, stream); break;
-        case 2: launch_partial<D, 2>(a, p, opart, ml, stream); break;
-        case 4: launch_partial<D, 4>(a, p, opart, ml, stream); break;
-        default: launch_partial<D, 8>(a, p, opart, ml, stream); break;
-    }
+void launch_tree(const AttnArgs& a, const TreePlan& p, uint16_t* opart, float2* ml, hipStream_t stream) {
+    const int units = a.B * a.Hkv * p.nsplit;
+    const int blocks = units * p.ngroups;
+    const int xcd_map = (p.ngroups > 1 && units % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL((attn_tree_kernel<D>), dim3(blocks), dim3(kTreeThreads), 0, stream,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_cache),
+                       static_cast<const uint16_t*>(a.v_cache), a.ctx_len, a.mask, a.n1, a.Hq, a.Hkv,
+                       a.Lmax, a.scale * kLog2e, p.nsplit, p.ngroups, xcd_map,
+                       static_cast<uint16_t*>(a.out), a.lse, opart, ml);
 }
 
 }  // namespace
 
 size_t attn_tree_workspace_bytes(int B, int n1, int Hq, int Hkv, int D, int Lmax) {
-    const Plan p = make_plan(B, n1, Hq, Hkv, D, Lmax);
-    return AttnLayout(B, Hkv, p.nsplit, (Hq / Hkv) * n1, D).total;
+    const TreePlan p = make_plan(B, n1, Hq, Hkv, Lmax);
+    return TreeLayout(B, Hkv, p.nsplit, (Hq / Hkv) * n1, D).total;
 }
 
 hipError_t launch_attn_tree(const AttnArgs& a, hipStream_t stream) {
-    const Plan p = make_plan(a.B, a.n1, a.Hq, a.Hkv, a.D, a.Lmax);
-    const AttnLayout lay(a.B, a.Hkv, p.nsplit, (a.Hq / a.Hkv) * a.n1, a.D);
+    const TreePlan p = make_plan(a.B, a.n1, a.Hq, a.Hkv, a.Lmax);
+    const TreeLayout lay(a.B, a.Hkv, p.nsplit, (a.Hq / a.Hkv) * a.n1, a.D);
     char* ws = static_cast<char*>(a.workspace);
-    float* opart = reinterpret_cast<float*>(ws + lay.opart);
-    float2* ml = reinterpret_cast<float2*>(ws + lay.ml);
-    if (a.D == 64) dispatch_partial<64>(a, p, opart, ml, stream);
-    else dispatch_partial<128>(a, p, opart, ml, stream);
-    const int64_t total = static_cast<int64_t>(a.B) * a.n1 * a.Hq * (a.D / 4);
-    const int blocks = static_cast<int>((total + 255) / 256);
-    hipLaunchKernelGGL((attn_combine_kernel<uint16_t>), dim3(blocks), dim3(256), 0, stream, opart, ml,
-                       a.ctx_len, a.B, a.n1, a.Hq, a.Hkv, a.D, a.Lmax, p.nsplit,
-                       static_cast<uint16_t*>(a.out), a.lse);
+    uint16_t* opart = p.nsplit > 1 ? reinterpret_cast<uint16_t*>(ws + lay.opart) : nullptr;
+    float2* ml = p.nsplit > 1 ? reinterpret_cast<float2*>(ws + lay.ml) : nullptr;
+    if (a.D == 64) launch_tree<64>(a, p, opart, ml, stream);
+    else launch_tree<128>(a, p, opart, ml, stream);
+    if (p.nsplit > 1) {
+        const int64_t total = static_cast<int64_t>(a.B) * a.n1 * a.Hq * (a.D / 8);
+        const int blocks = static_cast<int>((total + 255) / 256);
+        hipLaunchKernelGGL(attn_tree_combine_kernel, dim3(blocks), dim3(256), 0, stream, opart, ml,
+                           a.ctx_len, a.B, a.n1, a.Hq, a.Hkv, a.D, a.Lmax, p.nsplit,
+                           static_cast<uint16_t*>(a.out), a.lse);
+    }
     return hipGetLastError();
 }
 

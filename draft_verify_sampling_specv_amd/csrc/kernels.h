@@ -10,6 +10,18 @@ namespace specv {
 
 constexpr int kMaxNodes = 1024;
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+inline int device_cu_count() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cus[dev]) {
+        hipDeviceProp_t prop;
+        cus[dev] = (hipGetDeviceProperties(&prop, dev) == hipSuccess) ? prop.multiProcessorCount : 256;
+    }
+    return cus[dev];
+}
+
 hipError_t launch_build_tree_mask(const int32_t* parent, int B, int n1, uint32_t* mask,
                                   int32_t* depth, int32_t* tree_status, hipStream_t stream);
 

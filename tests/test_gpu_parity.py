@@ -245,6 +245,26 @@ def test_attn_random_shapes(dtype):
         _attn_compare(a, name=f"attn-random{case}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_attn_tree_long_context_with_score_jumps(d):
+    """Many row groups (R = 8 x 100 rows per KV head), contexts long enough for key splits and
+    ragged against the tiles, and a few late keys scaled up so that a row's running max jumps
+    by far more than the lazy-rescale headroom in the middle of the sequence."""
+    rng = np.random.default_rng(11 + d)
+    B, n1, hkv, g = 2, 100, 4, 8
+    par = np.stack([workloads.random_tree(rng, n1 - 1, 4, 12) for _ in range(B)])
+    ctx = [3001, 1717]
+    a = workloads.make_attention(f"jumps{d}", par, ctx, hkv * g, hkv, d, "bf16", 77 + d)
+    k = a.k_cache.astype(np.float32)
+    for b in range(B):
+        for pos in (ctx[b] // 2, ctx[b] - 5, ctx[b] + 3):      # context keys and a tree key
+            k[b, :, pos, :] *= 12.0
+    a.k_cache = workloads.as_dtype(k, "bf16")
+    rows = [(b, i) for b in range(B) for i in (0, 1, 2, 50, 98, 99)]
+    log(f"attn: long context with score jumps D={d} ctx={ctx} N1={n1} Hq={hkv * g} Hkv={hkv}")
+    _attn_compare(a, rows=rows, name=f"jumps-d{d}")
+
+
 def test_attn_invalid_context_length_gives_nan():
     a = workloads.make_attention("bad", workloads.chain_parent(3, 4), [10, 20, 30], 4, 2, 64, "bf16", 9)
     a.ctx_len = np.array([10, -1, 10_000], dtype=np.int32)

@@ -81,9 +81,12 @@ def test_accept_host_validation(specv):
 def test_workspace_queries(specv):
     assert specv.accept_workspace_bytes(32, 5, 32000, None) > 0
     assert specv.lib.specv_accept_workspace_bytes(0, 5, 100, 0) == 0
-    # many query rows per KV head (tree x GQA group) use split partials and need a workspace;
-    # decode-shaped calls (at most 64 rows per KV head) need none
-    assert specv.attn_workspace_bytes(16, 60, 64, 8, 128, 4157) > 0
+    # many query rows per KV head (tree x GQA group) over a long context are split along the
+    # keys and need a workspace for the partials; when sequences x KV heads x row groups already
+    # cover the device (or the context is short) there is no split; decode-shaped calls (at most
+    # 64 rows per KV head) need none
+    assert specv.attn_workspace_bytes(4, 64, 64, 8, 128, 32833) > 0
+    assert specv.attn_workspace_bytes(16, 60, 64, 8, 128, 4157) == 0
     assert specv.attn_workspace_bytes(32, 5, 32, 8, 128, 2054) == 0
     assert specv.attn_workspace_bytes(32, 5, 32, 8, 96, 2054) == 0
     assert specv.attn_workspace_bytes(32, 5, 30, 8, 128, 2054) == 0
@@ -95,7 +98,7 @@ def test_attention_and_mask_host_validation(specv):
 
     # every call below must be rejected on the host: the pointers are not device memory
     def attn(**kw):
-        a = dict(B=2, K=60, Hq=64, Hkv=8, D=128, Lmax=100, scale=0.1, dtype=1, ws=v, wsb=8)
+        a = dict(B=4, K=64, Hq=64, Hkv=8, D=128, Lmax=32833, scale=0.1, dtype=1, ws=v, wsb=8)
         a.update(kw)
         return lib.specv_tree_attn_verify(v, v, v, v, v, a["B"], a["K"], a["Hq"], a["Hkv"], a["D"], a["Lmax"],
                                           a["scale"], a["dtype"], v, None, a["ws"], a["wsb"], None)
