@@ -26,14 +26,26 @@ __global__ void __launch_bounds__(KS * kWave)
 attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
                    const uint16_t* __restrict__ vc, const int32_t* __restrict__ ctx_len,
                    const uint32_t* __restrict__ mask, int n1, int Hq, int Hkv, int Lmax, float c2,
-                   uint16_t* __restrict__ out, float* __restrict__ lse) {
+                   int ngroups, int xcd_map, uint16_t* __restrict__ out, float* __restrict__ lse) {
     constexpr int kKS = D / 16;        // k-steps of S^T = K Q^T
     constexpr int kDH = D / 64;        // 64-feature halves: MFMA blocks 2 dh (even) and 2 dh + 1 (odd)
     constexpr int kDB = D / 32;
     extern __shared__ float xs[];      // merge buffer: (KS / 2) x RBW x kDB x 16 x 64 floats + m, l
     __shared__ uint4 sq[RBW][kKS][kWave];   // Q^T operands of the workgroup's row blocks
 
-    const int kv = blockIdx.y, b = blockIdx.z;
+    // block id -> (unit = (sequence, KV head), row group of RBW blocks); with xcd_map the row
+    // groups of a unit get ids on the same XCD (ids are dealt to the 8 XCDs round-robin), adjacent
+    // in its dispatch order, so they share that XCD's L2 for the unit's K/V
+    int unit, grp;
+    if (xcd_map) {
+        const int x = blockIdx.x & 7, s = blockIdx.x >> 3;
+        unit = (s / ngroups) * 8 + x;
+        grp = s % ngroups;
+    } else {
+        unit = blockIdx.x / ngroups;
+        grp = blockIdx.x % ngroups;
+    }
+    const int kv = unit % Hkv, b = unit / Hkv;
     const int G = Hq / Hkv, R = G * n1;
     const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int h = lane / 32, col = lane % 32;
@@ -48,7 +60,7 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const uint32_t* mrow[RBW];
 #pragma unroll
     for (int j = 0; j < RBW; ++j) {
-        rows[j] = (blockIdx.x * RBW + j) * 32 + col;
+        rows[j] = (grp * RBW + j) * 32 + col;
         rok[j] = rows[j] < R;
         const int node = rok[j] ? rows[j] / G : 0;
         mrow[j] = mask + (static_cast<int64_t>(b) * n1 + node) * words;
@@ -56,7 +68,7 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     // stage Q^T operands: entry (j, s, lane) = Q[row j*32 + col][16 s + 8 h .. +8]
     for (int e = threadIdx.x; e < RBW * kKS * kWave; e += KS * kWave) {
         const int j = e / (kKS * kWave), s2 = (e / kWave) % kKS, ln = e % kWave;
-        const int row = (blockIdx.x * RBW + j) * 32 + ln % 32;
+        const int row = (grp * RBW + j) * 32 + ln % 32;
         uint4 v = make_uint4(0, 0, 0, 0);
         if (row < R) {
             const int node = row / G, g = row - node * G;
@@ -246,30 +258,28 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 }
 
 template <int D, int KS, int RBW>
-void launch_decode(const AttnArgs& a, dim3 grid, hipStream_t stream) {
+void launch_decode(const AttnArgs& a, int ngroups, hipStream_t stream) {
     const size_t lds = sizeof(float) * (size_t(KS / 2) * RBW * (D / 32) * 16 * kWave + size_t(KS / 2) * RBW * 2 * kWave);
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&attn_decode_kernel<D, KS, RBW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     (void)attr;
-    hipLaunchKernelGGL((attn_decode_kernel<D, KS, RBW>), grid, dim3(KS * kWave), lds, stream,
+    const int units = a.B * a.Hkv;
+    const int xcd_map = (ngroups > 1 && units % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL((attn_decode_kernel<D, KS, RBW>), dim3(units * ngroups), dim3(KS * kWave), lds, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_cache),
                        static_cast<const uint16_t*>(a.v_cache), a.ctx_len, a.mask, a.n1, a.Hq, a.Hkv,
-                       a.Lmax, a.scale * kLog2e, static_cast<uint16_t*>(a.out), a.lse);
+                       a.Lmax, a.scale * kLog2e, ngroups, xcd_map, static_cast<uint16_t*>(a.out), a.lse);
 }
 
 }  // namespace
 
 hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t stream) {
+    // one row block: one workgroup per (sequence, KV head); two: one workgroup per row block (the
+    // pair shares the K/V stream through L2), which keeps each wave to one block's accumulators
     const int RB = ((a.Hq / a.Hkv) * a.n1 + 31) / 32;
-    const dim3 grid(1, a.Hkv, a.B);
-    if (a.D == 64) {
-        if (RB == 1) launch_decode<64, 8, 1>(a, grid, stream);
-        else launch_decode<64, 4, 2>(a, grid, stream);
-    } else {
-        if (RB == 1) launch_decode<128, 8, 1>(a, grid, stream);
-        else launch_decode<128, 4, 2>(a, grid, stream);
-    }
+    if (a.D == 64) launch_decode<64, 8, 1>(a, RB, stream);
+    else launch_decode<128, 8, 1>(a, RB, stream);
     return hipGetLastError();
 }
 

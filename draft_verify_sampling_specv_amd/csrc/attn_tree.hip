@@ -37,7 +37,8 @@ using namespace attn;
 
 constexpr int kTreeWaves = 8;             // one 32-row block per wave, two waves per SIMD
 constexpr int kTreeThreads = kTreeWaves * kWave;
-constexpr int kTreeTile = 64;             // keys per ring stage: two 32-key S^T blocks
+constexpr int kTreeTile = 64;             // keys per ring stage
+constexpr int kNst = kTreeTile / 32;      // 32-key S^T blocks per tile
 constexpr int kStages = 3;                // LDS ring depth (tiles)
 constexpr float kLazyMax = 1048576.f;     // 2^20: largest p sum a lane may reach before the reference moves
 
@@ -51,7 +52,7 @@ constexpr float kLazyMax = 1048576.f;     // 2^20: largest p sum a lane may reac
 template <int D>
 struct TreeTiles {
     static constexpr int kKS = D / 16;                     // k-steps of S^T
-    static constexpr int kKT = 2 * kKS;                    // K transfers per tile
+    static constexpr int kKT = kNst * kKS;                 // K transfers per tile
     static constexpr int kVT = kTreeTile * 2 * D / 1024;   // V transfers per tile
     static constexpr int kVStride = 1024 + 64;             // bytes per V transfer slot
     uint16_t k[kStages][kTreeTile * D];
@@ -67,6 +68,11 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 // reads nor counts them; the tile pipeline waits for them explicitly.)
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(g), "s"(lds) : "memory", "m0");
+}
+
+// The same with a wave-uniform 64-bit base and a per-lane 32-bit byte offset.
+__device__ __forceinline__ void dma16_sbase(const void* base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
 
 template <int N>
@@ -103,34 +109,59 @@ struct WaveRow {
     const uint32_t* mrow;           // mask row of this lane's node
 };
 
-// Issue this wave's share of tile t's transfers into ring stage `stage`: kKT transfers of K (one
-// per (32-key block, k-step)) and kVT of V (1024 / (2 D) whole rows each), dealt to the waves.
-// Keys past the sequence read its last key (finite data, masked out by the softmax).
+// This wave's transfers of a tile: kKT transfers of K (one per (32-key block, k-step)) and kVT of
+// V (1024 / (2 D) whole rows each), dealt to the waves.  Transfer x of wave w is j = w + 8 x.
 template <int D>
-__device__ __forceinline__ void issue_tile(TreeTiles<D>& sm, int stage, const uint16_t* kbase,
-                                           const uint16_t* vbase, int t, int Ltot, int w, int lane) {
+struct TileTransfers {
     using T = TreeTiles<D>;
-    constexpr int kCpr = D / 8;                 // 16-byte chunks per V row
+    static constexpr int kCpr = D / 8;                             // 16-byte chunks per V row
+    static constexpr int kPerWave = (T::kKT + T::kVT) / kTreeWaves;
     static_assert((T::kKT + T::kVT) % kTreeWaves == 0, "whole transfers per wave");
-#pragma unroll
-    for (int x = 0; x < (T::kKT + T::kVT) / kTreeWaves; ++x) {
-        const int j = w + x * kTreeWaves;
-        const uint16_t* g;
-        const uint16_t* dst;
-        if (j < T::kKT) {
-            const int st = j / T::kKS, ks = j % T::kKS;
-            const int key = min(t * kTreeTile + 32 * st + (lane & 31), Ltot - 1);
-            g = kbase + static_cast<int64_t>(key) * D + 16 * ks + 8 * (lane >> 5);
-            dst = sm.k[stage] + j * (kWave * 8);
+    uint32_t off[kPerWave];     // this lane's byte offset from the tile's first key row
+
+    __device__ __forceinline__ static bool is_v(int j) { return j >= T::kKT; }
+    // key row (within the tile) and feature of this lane's 16 bytes in transfer j
+    __device__ __forceinline__ static void source(int j, int lane, int& row, int& feat) {
+        if (!is_v(j)) {
+            row = 32 * (j / T::kKS) + (lane & 31);
+            feat = 16 * (j % T::kKS) + 8 * (lane >> 5);
         } else {
-            const int u = j - T::kKT;           // rows u, u + kVT, ...
-            const int key = min(t * kTreeTile + (lane / kCpr) * T::kVT + u, Ltot - 1);
-            g = vbase + static_cast<int64_t>(key) * D + 8 * (lane % kCpr);
-            dst = sm.v[stage] + u * (T::kVStride / 2);
+            row = (lane / kCpr) * T::kVT + (j - T::kKT);      // rows u, u + kVT, ...
+            feat = 8 * (lane % kCpr);
         }
-        dma16(g, __builtin_amdgcn_readfirstlane(lds_address(dst)));
     }
-}
+    __device__ __forceinline__ static uint16_t* dest(TreeTiles<D>& sm, int stage, int j) {
+        return is_v(j) ? sm.v[stage] + (j - T::kKT) * (T::kVStride / 2) : sm.k[stage] + j * (kWave * 8);
+    }
+    __device__ __forceinline__ void init(int w, int lane) {
+#pragma unroll
+        for (int x = 0; x < kPerWave; ++x) {
+            int row, feat;
+            source(w + x * kTreeWaves, lane, row, feat);
+            off[x] = static_cast<uint32_t>((row * D + feat) * 2);
+        }
+    }
+    // Issue tile t into ring stage `stage`.  Tiles entirely inside the sequence use the scalar
+    // base + lane offset form; the last tile reads, for keys past the sequence, its last key
+    // instead (finite data, masked out by the softmax).
+    __device__ __forceinline__ void issue(TreeTiles<D>& sm, int stage, const uint16_t* kbase,
+                                          const uint16_t* vbase, int t, int Ltot, int w, int lane) const {
+#pragma unroll
+        for (int x = 0; x < kPerWave; ++x) {
+            const int j = w + x * kTreeWaves;
+            const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_address(dest(sm, stage, j)));
+            const uint16_t* base = is_v(j) ? vbase : kbase;
+            if ((t + 1) * kTreeTile <= Ltot) {
+                dma16_sbase(base + static_cast<int64_t>(t) * kTreeTile * D, off[x], lds);
+            } else {
+                int row, feat;
+                source(j, lane, row, feat);
+                const int key = min(t * kTreeTile + row, Ltot - 1);
+                dma16(base + static_cast<int64_t>(key) * D + feat, lds);
+            }
+        }
+    }
+};
 
 // One 64-key tile for this wave's row block.
 template <int D>
@@ -140,23 +171,23 @@ __device__ __forceinline__ void tile_compute(WaveRow<D>& wr, const uint16_t* kt,
     constexpr int kKS = T::kKS;
     constexpr int kF = D / 32;
     const int h = lane >> 5;
-    f32x16_t s[2];
+    f32x16_t s[kNst];
 
     // S^T = K Q^T for the two 32-key blocks (interleaved, independent chains)
     auto compute_s = [&]() {
-        s[0] = f32x16_t{};
-        s[1] = f32x16_t{};
+#pragma unroll
+        for (int st = 0; st < kNst; ++st) s[st] = f32x16_t{};
 #pragma unroll
         for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
+            for (int st = 0; st < kNst; ++st) {
                 const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(&kt[((st * kKS + ks) * kWave + lane) * 8]));
                 s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wr.q[ks], s[st], 0, 0, 0);
             }
         // s[st][r] is key kb + 32 st + 8 (r / 4) + 4 h + r % 4 of this lane's row
         if (kb + kTreeTile > L) {
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
+            for (int st = 0; st < kNst; ++st)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = kb + 32 * st + 8 * (r / 4) + 4 * h + (r % 4);
@@ -174,7 +205,7 @@ __device__ __forceinline__ void tile_compute(WaveRow<D>& wr, const uint16_t* kt,
         const float mref = (wr.m == -INFINITY) ? 0.f : wr.m;
         float rs = 0.f;
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+        for (int st = 0; st < kNst; ++st)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 s[st][r] = __builtin_amdgcn_exp2f(fmaf(s[st][r], c2, -mref));
@@ -191,7 +222,7 @@ __device__ __forceinline__ void tile_compute(WaveRow<D>& wr, const uint16_t* kt,
         compute_s();
         float mx = s[0][0];
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+        for (int st = 0; st < kNst; ++st)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[st][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -209,9 +240,9 @@ __device__ __forceinline__ void tile_compute(WaveRow<D>& wr, const uint16_t* kt,
 
     // P as the B operands of the PV product: k-step (st, ks) covers the keys
     // 32 st + 16 ks + 8 (e / 4) + 4 h + e % 4 (e = 0..7), the order in which S^T holds them
-    bf16x8_t pb[2][2];
+    bf16x8_t pb[kNst][2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int st = 0; st < kNst; ++st)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             uint4 pw;
@@ -232,9 +263,11 @@ __device__ __forceinline__ void tile_compute(WaveRow<D>& wr, const uint16_t* kt,
     typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
     const int kj = (lane & 15) >> 2;
     const int fo = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    lds_char* vb = (lds_char*)(vt) + (4 * h + kj) * T::kVStride + 2 * fo;
+    // lane part of key 4 h + j: slot 4 h + j with at least 8 slots, else slot j and position + h
+    lds_char* vb = (lds_char*)(vt) + 2 * fo +
+                   ((T::kVT >= 8) ? (4 * h + kj) * T::kVStride : kj * T::kVStride + h * (2 * D));
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int st = 0; st < kNst; ++st)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -242,9 +275,10 @@ __device__ __forceinline__ void tile_compute(WaveRow<D>& wr, const uint16_t* kt,
                 v4i16 part[2];
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
-                    int off;
-                    if constexpr (T::kVT == 16) off = 8 * half * T::kVStride + (2 * st + ks) * (2 * D);   // D = 128
-                    else off = (4 * st + 2 * ks + half) * (2 * D);                                     // D = 64
+                    constexpr int kVT = T::kVT;
+                    const int rc = 32 * st + 16 * ks + 8 * half;    // key less its lane part 4 h + j
+                    const int off = (kVT >= 8) ? (rc % kVT) * T::kVStride + (rc / kVT) * (2 * D)
+                                               : (rc / 4) * (2 * D);
                     part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb + off + 64 * c));
                 }
                 const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
@@ -259,21 +293,22 @@ template <int D, bool kActive>
 __device__ __forceinline__ void run_tiles(WaveRow<D>& wr, TreeTiles<D>& sm, const uint16_t* kbase,
                                           const uint16_t* vbase, int t0, int t1, int L, int Ltot,
                                           int w, int lane, float c2) {
-    using T = TreeTiles<D>;
-    constexpr int kPerTile = (T::kKT + T::kVT) / kTreeWaves;    // transfers per wave per tile
+    constexpr int kPerTile = TileTransfers<D>::kPerWave;        // transfers per wave per tile
     if (t0 >= t1) return;                                      // (workgroup-uniform)
+    TileTransfers<D> tx;
+    tx.init(w, lane);
     // Let the compiler see every earlier load (Q operands, ...) complete here: it cannot count
     // the ring's transfers, so a load it still believed pending inside the loop would make it
     // wait for all of them.
     __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
-    for (int i = 0; i < kStages - 1; ++i) issue_tile<D>(sm, i, kbase, vbase, min(t0 + i, t1 - 1), Ltot, w, lane);
+    for (int i = 0; i < kStages - 1; ++i) tx.issue(sm, i, kbase, vbase, min(t0 + i, t1 - 1), Ltot, w, lane);
     for (int tt = t0; tt < t1; ++tt) {
         const int i = tt - t0;
         wait_vmcnt<(kStages - 2) * kPerTile>();
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        issue_tile<D>(sm, (i + kStages - 1) % kStages, kbase, vbase, min(tt + kStages - 1, t1 - 1), Ltot, w, lane);
+        tx.issue(sm, (i + kStages - 1) % kStages, kbase, vbase, min(tt + kStages - 1, t1 - 1), Ltot, w, lane);
         if constexpr (kActive)
             tile_compute<D>(wr, sm.k[i % kStages], sm.v[i % kStages], tt * kTreeTile, L, Ltot, lane, c2);
     }
@@ -310,7 +345,7 @@ attn_tree_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc
     const int G = Hq / Hkv, R = G * n1;
     const int RB = (R + 31) / 32;
     const int rb0 = grp * RB / ngroups, rb1 = (grp + 1) * RB / ngroups;   // this group's row blocks
-    const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int h = lane >> 5, col = lane & 31;
     const bool active = rb0 + w < rb1;                                    // (wave-uniform)
     const int words = (n1 + 31) >> 5;
@@ -427,13 +462,35 @@ attn_tree_combine_kernel(const uint16_t* __restrict__ opart, const float2* __res
     if (lse && d0 == 0) lse[orow] = ok ? (M + log2f(den)) * kLn2 : NAN;
 }
 
-// Row groups of at most kTreeWaves blocks (one per wave), balanced.  Key splits: one workgroup
-// fits per compute unit (LDS ring), so the time goes as rounds of resident workgroups x tiles per
-// split; take the number of splits (a power of two, at least 2 tiles each) that minimises that,
-// counting the combine pass as two tiles.
-TreePlan make_plan(int B, int n1, int Hq, int Hkv, int Lmax) {
+template <int D>
+__global__ void __launch_bounds__(kTreeThreads)
+attn_tree_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+                 const uint16_t* __restrict__ vc, const int32_t* __restrict__ ctx_len,
+                 const uint32_t* __restrict__ mask, int n1, int Hq, int Hkv, int Lmax, float c2,
+                 int nsplit, int ngroups, int xcd_map, uint16_t* __restrict__ out, float* __restrict__ lse,
+                 uint16_t* __restrict__ opart, float2* __restrict__ mlpart);
+
+// Workgroups of the tree kernel one compute unit holds at once (LDS ring and registers).
+int tree_blocks_per_cu(int D) {
+    static int cache[64][2] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+    int& c = cache[dev][D == 64 ? 0 : 1];
+    if (!c) {
+        int n = 0;
+        const void* f = (D == 64) ? reinterpret_cast<const void*>(&attn_tree_kernel<64>)
+                                  : reinterpret_cast<const void*>(&attn_tree_kernel<128>);
+        c = (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, kTreeThreads, 0) == hipSuccess && n > 0) ? n : 1;
+    }
+    return c;
+}
+
+// Row groups of at most kTreeWaves blocks (one per wave), balanced.  Key splits: the time goes as
+// rounds of resident workgroups x tiles per split; take the number of splits (a power of two, at
+// least 2 tiles each) that minimises that, counting the combine pass as two tiles.
+TreePlan make_plan(int B, int n1, int Hq, int Hkv, int D, int Lmax) {
     const int RB = ((Hq / Hkv) * n1 + 31) / 32;
-    const int cus = device_cu_count();
+    const int slots = device_cu_count() * tree_blocks_per_cu(D);
     const int tiles = (Lmax + kTreeTile - 1) / kTreeTile;
     TreePlan p;
     p.ngroups = (RB + kTreeWaves - 1) / kTreeWaves;
@@ -441,7 +498,7 @@ TreePlan make_plan(int B, int n1, int Hq, int Hkv, int Lmax) {
     const long long wgs1 = static_cast<long long>(B) * Hkv * p.ngroups;
     long long best = -1;
     for (int ns = 1; ns <= 64 && (ns == 1 || tiles / ns >= 2); ns *= 2) {
-        const long long rounds = (wgs1 * ns + cus - 1) / cus;
+        const long long rounds = (wgs1 * ns + slots - 1) / slots;
         const long long cost = rounds * ((tiles + ns - 1) / ns) + (ns > 1 ? 2 : 0);
         if (best < 0 || cost < best) {
             best = cost;
@@ -466,12 +523,12 @@ void launch_tree(const AttnArgs& a, const TreePlan& p, uint16_t* opart, float2* 
 }  // namespace
 
 size_t attn_tree_workspace_bytes(int B, int n1, int Hq, int Hkv, int D, int Lmax) {
-    const TreePlan p = make_plan(B, n1, Hq, Hkv, Lmax);
+    const TreePlan p = make_plan(B, n1, Hq, Hkv, D, Lmax);
     return TreeLayout(B, Hkv, p.nsplit, (Hq / Hkv) * n1, D).total;
 }
 
 hipError_t launch_attn_tree(const AttnArgs& a, hipStream_t stream) {
-    const TreePlan p = make_plan(a.B, a.n1, a.Hq, a.Hkv, a.Lmax);
+    const TreePlan p = make_plan(a.B, a.n1, a.Hq, a.Hkv, a.D, a.Lmax);
     const TreeLayout lay(a.B, a.Hkv, p.nsplit, (a.Hq / a.Hkv) * a.n1, a.D);
     char* ws = static_cast<char*>(a.workspace);
     uint16_t* opart = p.nsplit > 1 ? reinterpret_cast<uint16_t*>(ws + lay.opart) : nullptr;
