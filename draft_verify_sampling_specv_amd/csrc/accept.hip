@@ -114,6 +114,39 @@ __device__ uint32_t get_word(uint64_t* p, uint32_t tag, int* timed_out) {
     return static_cast<uint32_t>(w);
 }
 
+// Read n tagged words at p (n <= N): all loads are issued before any tag is checked, and the
+// words not yet published are polled together (bounded as in get_word).
+template <int N>
+__device__ __forceinline__ void get_words(uint64_t* p, int n, uint32_t tag, int* timed_out, uint32_t (&v)[N]) {
+    uint64_t raw[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        raw[i] = (i < n) ? __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+    auto missing = [&]() {
+        bool any = false;
+#pragma unroll
+        for (int i = 0; i < N; ++i) any |= (i < n) && static_cast<uint32_t>(raw[i] >> 32) != tag;
+        return any;
+    };
+    if (missing() && !*timed_out) {
+        // poll the missing words together, one round trip per round
+        const uint64_t t0 = wall_clock64();
+        do {
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+                if (i < n && static_cast<uint32_t>(raw[i] >> 32) != tag)
+                    raw[i] = __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (wall_clock64() - t0 > kTimeoutTicks) {
+                *timed_out = 1;
+                break;
+            }
+        } while (missing());
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = static_cast<uint32_t>(raw[i]);
+}
+
 // Streaming pass over tiles [t0, t1) of one row pair with the draw weights.  Tile i covers
 // kThreads * kVec consecutive elements; within a tile wave ww owns the contiguous segment of
 // 64 * kVec elements at (ww * 64) * kVec.  Segment sums go to seg[(i - t0) * kWaves + ww] if seg is
@@ -350,12 +383,11 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
             auto values = [&](int u, float* z) {
                 const int base = lo + (u * kWave + lane) * kVec;
                 if (kVecOK) {
-                    if (base < hi) {
-                        cvt_vec<T>(r[u], z);
-                    } else {
+                    // (a vector lies wholly inside or outside the row; selects, no branches)
+                    cvt_vec<T>(r[u], z);
+                    const bool in = base < hi;
 #pragma unroll
-                        for (int e = 0; e < kVec; ++e) z[e] = -INFINITY;
-                    }
+                    for (int e = 0; e < kVec; ++e) z[e] = in ? z[e] : -INFINITY;
                 } else {
 #pragma unroll
                     for (int e = 0; e < kVec; ++e) z[e] = (base + e < hi) ? Elem<T>::load(src, base + e) : -INFINITY;
@@ -364,16 +396,32 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
             if (kGreedy) {
                 float bv = -INFINITY;
                 int bi = INT_MAX;
+                // this lane's elements come in increasing index order, so a strict > keeps the
+                // lowest index among equal values; branch-free selects
+                // kVec independent running maxima (one per vector position), merged at the end
+                float bvs[kVec];
+                int bis[kVec];
 #pragma unroll
-                for (int u = 0; u < kWaveLoads; ++u) {
+                for (int e = 0; e < kVec; ++e) { bvs[e] = -INFINITY; bis[e] = INT_MAX; }
+                auto scan = [&](int u) {
                     float z[kVec];
                     values(u, z);
 #pragma unroll
                     for (int e = 0; e < kVec; ++e) {
                         const int x = lo + (u * kWave + lane) * kVec + e;
-                        if (x < hi) argmax_merge(bv, bi, z[e], x);
+                        const bool take = (z[e] > bvs[e]) & (x < hi);
+                        bvs[e] = take ? z[e] : bvs[e];
+                        bis[e] = take ? x : bis[e];
                     }
+                };
+                if constexpr (kVecOK) {
+#pragma unroll
+                    for (int u = 0; u < kWaveLoads; ++u) scan(u);
+                } else {
+                    for (int u = 0; u < kWaveLoads; ++u) scan(u);
                 }
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) argmax_merge(bv, bi, bvs[e], bis[e]);
                 wave_argmax(bv, bi);
                 if (lane == 0) {
                     put_word(slot, __float_as_uint(bv), tag);
@@ -381,21 +429,26 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                 }
             } else {
                 // online over the 16-byte vectors: the running sum is rescaled once per vector
+                // (branch-free: a reference of 0 while everything is -inf makes every term 0)
                 float m = -INFINITY, s = 0.f;
-#pragma unroll
-                for (int u = 0; u < kWaveLoads; ++u) {
+                auto fold = [&](int u) {
                     float z[kVec];
                     values(u, z);
                     float mu = m;
 #pragma unroll
                     for (int e = 0; e < kVec; ++e) mu = fmaxf(mu, z[e]);
-                    if (mu != -INFINITY) {
-                        float add = 0.f;
+                    const float mref = (mu == -INFINITY) ? 0.f : mu;
+                    float add = 0.f;
 #pragma unroll
-                        for (int e = 0; e < kVec; ++e) add += __builtin_amdgcn_exp2f((z[e] - mu) * k);
-                        s = (m == -INFINITY ? 0.f : s * __builtin_amdgcn_exp2f((m - mu) * k)) + add;
-                        m = mu;
-                    }
+                    for (int e = 0; e < kVec; ++e) add += __builtin_amdgcn_exp2f((z[e] - mref) * k);
+                    s = s * __builtin_amdgcn_exp2f((m - mref) * k) + add;
+                    m = mu;
+                };
+                if constexpr (kVecOK) {
+#pragma unroll
+                    for (int u = 0; u < kWaveLoads; ++u) fold(u);
+                } else {
+                    for (int u = 0; u < kWaveLoads; ++u) fold(u);
                 }
                 wave_max_sum(m, s, k);
                 if (lane == 0) {
@@ -412,9 +465,9 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                 float bv = -INFINITY;
                 int bi = INT_MAX;
                 for (int c = lane; c < nchunk; c += kWave) {
-                    const float cv = __uint_as_float(get_word(sv + c * 4, tag, &s_to));
-                    const int ci = static_cast<int>(get_word(sv + c * 4 + 1, tag, &s_to));
-                    argmax_merge(bv, bi, cv, ci);
+                    uint32_t wv[2];
+                    get_words<2>(sv + c * 4, 2, tag, &s_to, wv);
+                    argmax_merge(bv, bi, __uint_as_float(wv[0]), static_cast<int>(wv[1]));
                 }
                 wave_argmax(bv, bi);
                 if (lane == 0) info[v] = (bi >= 0 && bi < V) ? bi : 0;
@@ -422,15 +475,22 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                 const bool dr = info[v] != 0;
                 float mt = -INFINITY, md = -INFINITY;
                 float a0[2], a1[2], b0[2], b1[2];   // up to 128 chunks per row held in registers
+                uint32_t wv[2][4];
+                for (int q2 = 0; q2 < 2; ++q2) {
+                    const int c = lane + q2 * kWave;
+                    const int n = (c < nchunk) ? (dr ? 4 : 2) : 0;
+                    get_words<4>(sv + (c < nchunk ? c : 0) * 4, n, tag, &s_to, wv[q2]);
+                }
+#pragma unroll
                 for (int q2 = 0; q2 < 2; ++q2) {
                     const int c = lane + q2 * kWave;
                     a0[q2] = -INFINITY; a1[q2] = 0.f; b0[q2] = -INFINITY; b1[q2] = 0.f;
                     if (c < nchunk) {
-                        a0[q2] = __uint_as_float(get_word(sv + c * 4, tag, &s_to));
-                        a1[q2] = __uint_as_float(get_word(sv + c * 4 + 1, tag, &s_to));
+                        a0[q2] = __uint_as_float(wv[q2][0]);
+                        a1[q2] = __uint_as_float(wv[q2][1]);
                         if (dr) {
-                            b0[q2] = __uint_as_float(get_word(sv + c * 4 + 2, tag, &s_to));
-                            b1[q2] = __uint_as_float(get_word(sv + c * 4 + 3, tag, &s_to));
+                            b0[q2] = __uint_as_float(wv[q2][2]);
+                            b1[q2] = __uint_as_float(wv[q2][3]);
                         }
                     }
                     mt = fmaxf(mt, a0[q2]);
@@ -812,9 +872,6 @@ hipError_t launch_kernel(const AcceptArgs& a, hipStream_t stream) {
     int32_t* out_nodes = a.out_nodes;
     float* p_tok = a.p_tok;
     float* q_tok = a.q_tok;
-    void* args[] = {&target, &draft, &tokens, &parent, &B, &n1, &V, &nchunk, &P, &k, &invT, &seed, &offset,
-                    &tag, &statw, &partw, &err, &accept_len, &out_tokens, &out_nodes, &p_tok, &q_tok};
-    (void)args;
     hipLaunchKernelGGL((accept_kernel<T, kGreedy, kVecOK>), dim3(grid), dim3(kThreads), 0, stream, target, draft,
                        tokens, parent, B, n1, V, nchunk, P, k, invT, seed, offset, tag, statw, partw, err,
                        accept_len, out_tokens, out_nodes, p_tok, q_tok);
