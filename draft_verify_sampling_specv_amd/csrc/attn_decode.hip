@@ -55,15 +55,18 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const int Ltot = L + n1;
     const int ntiles = seq_ok ? (Ltot + kTileKeys - 1) / kTileKeys : 0;
 
+    // this lane's mask row in registers: the decode shape has at most 64 rows per KV head, so at
+    // most 64 nodes and two mask words
     int rows[RBW];
     bool rok[RBW];
-    const uint32_t* mrow[RBW];
+    uint64_t mbits[RBW];
 #pragma unroll
     for (int j = 0; j < RBW; ++j) {
         rows[j] = (grp * RBW + j) * 32 + col;
         rok[j] = rows[j] < R;
         const int node = rok[j] ? rows[j] / G : 0;
-        mrow[j] = mask + (static_cast<int64_t>(b) * n1 + node) * words;
+        const uint32_t* mrow = mask + (static_cast<int64_t>(b) * n1 + node) * words;
+        mbits[j] = mrow[0] | (words > 1 ? static_cast<uint64_t>(mrow[1]) << 32 : 0ull);
     }
     // stage Q^T operands: entry (j, s, lane) = Q[row j*32 + col][16 s + 8 h .. +8]
     for (int e = threadIdx.x; e < RBW * kKS * kWave; e += KS * kWave) {
@@ -82,13 +85,15 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const uint16_t* kbase = kc + (static_cast<int64_t>(b) * Hkv + kv) * Lmax * D;
     const uint16_t* vbase = vc + (static_cast<int64_t>(b) * Hkv + kv) * Lmax * D;
 
+    // Loads are unconditional: a key past the sequence reads its last key instead (finite data,
+    // masked out by the softmax).  With no register zeroed under a branch, the compiler's load
+    // counting stays exact and the next tile's K stays in flight while this tile is computed.
     uint4 kn[kKS];
     auto load_k = [&](int t) {
-        const int kkey = t * kTileKeys + col;
+        const int kkey = min(t * kTileKeys + col, Ltot - 1);
 #pragma unroll
         for (int s2 = 0; s2 < kKS; ++s2)
-            kn[s2] = (kkey < Ltot) ? *reinterpret_cast<const uint4*>(kbase + static_cast<int64_t>(kkey) * D + 16 * s2 + 8 * h)
-                                   : make_uint4(0, 0, 0, 0);
+            kn[s2] = *reinterpret_cast<const uint4*>(kbase + static_cast<int64_t>(kkey) * D + 16 * s2 + 8 * h);
     };
 
     f32x16_t o[RBW][kDB];
@@ -113,14 +118,12 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int key = kb + 16 * ks + 8 * (e / 4) + 4 * h + (e % 4);
+                const int key = min(kb + 16 * ks + 8 * (e / 4) + 4 * h + (e % 4), Ltot - 1);
 #pragma unroll
                 for (int dh = 0; dh < kDH; ++dh)
-                    vr[ks][dh][e] = (key < Ltot)
-                        ? *reinterpret_cast<const uint32_t*>(vbase + static_cast<int64_t>(key) * D + 64 * dh + 2 * col)
-                        : 0u;
+                    vr[ks][dh][e] = *reinterpret_cast<const uint32_t*>(vbase + static_cast<int64_t>(key) * D + 64 * dh + 2 * col);
             }
-        if (t + KS < ntiles) load_k(t + KS);
+        load_k(min(t + KS, ntiles - 1));
 
         bf16x8_t pb[RBW][2];
 #pragma unroll
@@ -133,12 +136,9 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = kb + 8 * (r / 4) + 4 * h + (r % 4);
-                    bool vis = key < L;
-                    if (!vis && key < Ltot) {
-                        const int jj = key - L;
-                        vis = (mrow[j][jj >> 5] >> (jj & 31)) & 1u;
-                    }
-                    if (!vis) s[r] = -INFINITY;
+                    const int jj = key - L;    // tree index when 0 <= jj < n1
+                    const bool vis = key < L || (key < Ltot && ((mbits[j] >> (jj & 63)) & 1ull));
+                    s[r] = vis ? s[r] : -INFINITY;
                 }
             }
             float mx = s[0];
