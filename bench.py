@@ -55,9 +55,10 @@ MFMA_PEAK_TFLOPS = 2500.0
 ATTN_TRAFFIC = {
     "sources": ["draft_verify_sampling_specv_amd/csrc/attn_decode.hip",
                 "draft_verify_sampling_specv_amd/csrc/attn_common.h",
-                "draft_verify_sampling_specv_amd/csrc/common.h"],
-    "sha256": "3b59d703509c165447b46260e69a4279a854121482dc61a0b13069377b65a6a3",
-    "fetch_kib": 132343.7, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131084.0, "write_scale": 1.0,
+                "draft_verify_sampling_specv_amd/csrc/common.h",
+                "draft_verify_sampling_specv_amd/csrc/kernels.h"],
+    "sha256": "755c3b7e2771eb228f5a9e2a237692025abe602eb958fc1da2bc02576cf0a7c3",
+    "fetch_kib": 132488.7, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131084.0, "write_scale": 1.0,
 }
 
 

@@ -323,6 +323,14 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
             gzt = Elem<T>::load(target + (seq + pa) * V, x);
             gzd = Elem<T>::load(draft + (seq + pa) * V, x);
         }
+        // both uniforms of every node (Philox; computed while the gathers are in flight)
+        if (!kGreedy) {
+            for (int v = t; v < n1; v += kThreads) {
+                const U64x4 rnd = philox4x64_10(static_cast<uint64_t>(v), static_cast<uint64_t>(b), offset, 0, seed, 0);
+                uacc[v] = word_to_uniform(rnd.w[0]);
+                ures[v] = word_to_uniform(rnd.w[1]);
+            }
+        }
         for (int c = 1 + t; c < n1; c += kThreads) {
             const int pa = par[c], x = tok[c];
             info[pa] = 1;
@@ -531,21 +539,18 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
         for (int v = t; v < n1; v += kThreads) {
             float pv_ = NAN, qv_ = NAN;
             if (!kGreedy) {
-                const U64x4 rnd = philox4x64_10(static_cast<uint64_t>(v), static_cast<uint64_t>(b), offset, 0, seed, 0);
-                uacc[v] = word_to_uniform(rnd.w[0]);
-                ures[v] = word_to_uniform(rnd.w[1]);
                 if (v > 0) {
                     const int pa = par[v];
                     const float zt = (v == t) ? gzt : Elem<T>::load(target + (seq + pa) * V, tok[v]);
                     const float zd = (v == t) ? gzd : Elem<T>::load(draft + (seq + pa) * V, tok[v]);
                     const double lp = (static_cast<double>(zt) - Mt[pa]) * invT;
                     const double lq = (static_cast<double>(zd) - Md[pa]) * invT;
-                    const double pd = exp(lp) / St[pa];
-                    const double qd = exp(lq) / Sd[pa];
+                    // the ratio that decides acceptance in fp64; p and q themselves (outputs, and q
+                    // for the residual bookkeeping) in fp32
                     pq[v] = exp(lp - lq) * (Sd[pa] / St[pa]);
-                    qx[v] = static_cast<float>(qd);
-                    pv_ = static_cast<float>(pd);
-                    qv_ = static_cast<float>(qd);
+                    pv_ = expf(static_cast<float>(lp)) / static_cast<float>(St[pa]);
+                    qv_ = expf(static_cast<float>(lq)) / static_cast<float>(Sd[pa]);
+                    qx[v] = qv_;
                 }
             }
             if (rank == 0) {

@@ -11,9 +11,14 @@ using namespace attn;
 
 // ------------------------------------------------------------------------------------------
 // Decode-shaped case (at most two 32-row blocks per KV head, e.g. chains with small G): the
-// workgroup owns one (sequence, KV head); its KS waves split the key tiles round-robin, each wave
-// computing all RBW row blocks for its tiles, and the waves' partial softmax states are merged
-// through LDS at the end, so the final output is written directly (no partials in HBM).
+// workgroup owns RBW row blocks of one (sequence, KV head) -- the launch uses RBW = 1, so a KV
+// head with two row blocks gets two workgroups, placed on one XCD so that the second one's K/V
+// reads hit that XCD's L2; its KS waves split the key tiles round-robin, each wave computing the
+// workgroup's row blocks for its tiles, and the waves' partial softmax states are merged through
+// LDS at the end, so the final output is written directly (no partials in HBM).
+//   * every K/V load is unconditional, its key index clamped to the last valid key (masked in
+//     the softmax), so the compiler never waits for the prefetch before it is needed;
+//   * each lane keeps its query row's tree-mask words (at most two) in registers.
 //   * K goes straight from HBM into MFMA A-operand registers (16-byte loads; lane (c, h) reads key
 //     c of the tile, features 16 ks + 8 h .. +8).
 //   * V^T operands are built without a transpose: the O^T rows (feature index) are permuted so that
