@@ -269,12 +269,13 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
     __shared__ int wcount[kWaves];
     __shared__ float pv[kWaves];
     __shared__ int pi[kWaves];
-    __shared__ int s_bad, s_ni, s_cmd, s_row, s_n, s_sel, s_found, s_to;
+    __shared__ int s_bad, s_ni, s_cmd, s_row, s_n, s_sel, s_found, s_to, s_next;
     __shared__ float s_ps, s_qs;
     __shared__ double s_R, s_base;
 
     const int t = threadIdx.x;
     const int w = t / kWave, lane = t % kWave;
+    const int wu = __builtin_amdgcn_readfirstlane(w);      // the same, known wave-uniform
     const int team = blockIdx.x / P, rank = blockIdx.x % P, nteams = gridDim.x / P;
     const int ntile = (V + kTile - 1) / kTile;
     const int tpb = (ntile + P - 1) / P;
@@ -288,7 +289,10 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
 
         // -- A. stage and validate the parent array and the draft tokens
         __syncthreads();
-        if (t == 0) s_bad = 0;
+        if (t == 0) {
+            s_bad = 0;
+            s_next = kWaves;      // the first kWaves takes of the statistics phase are by position
+        }
         for (int i = t; i < n1; i += kThreads) {
             info[i] = 0;
             fch[i] = n1;
@@ -331,18 +335,37 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                 ures[v] = word_to_uniform(rnd.w[1]);
             }
         }
-        for (int c = 1 + t; c < n1; c += kThreads) {
-            const int pa = par[c], x = tok[c];
-            info[pa] = 1;
-            atomicMin(&fch[pa], c);
-            int nx = -1;
-            for (int i = c + 1; i < n1; ++i)
-                if (par[i] == pa) { nx = i; break; }
-            nsib[c] = nx;
-            int d = 0;
-            for (int i = c - 1; i > pa; --i)
-                if (par[i] == pa && tok[i] == x) { d = 1; break; }
-            dup[c] = d;
+        // next sibling (smallest i > c with the same parent) and repeated token (an earlier
+        // sibling with the same token): each wave walks all nodes 64 at a time, one LDS read per
+        // lane, the values handed to every lane by readlane, so no step waits on LDS
+        for (int c0 = 1 + wu * kWave; c0 < n1; c0 += kThreads) {     // wave-uniform
+            const int c = c0 + lane;
+            const bool valid = c < n1;
+            const int pa = valid ? par[c] : -3;
+            const int x = valid ? tok[c] : -1;
+            if (valid) {
+                info[pa] = 1;
+                atomicMin(&fch[pa], c);
+            }
+            int nx = INT_MAX, d = 0;
+            for (int base = 0; base < n1; base += kWave) {
+                const int i0 = base + lane;
+                const int pl = i0 < n1 ? par[i0] : -2;
+                const int tl = i0 < n1 ? tok[i0] : -1;
+                const int cnt = min(kWave, n1 - base);
+                for (int j = 0; j < cnt; ++j) {
+                    const int pi = __builtin_amdgcn_readlane(pl, j);
+                    const int ti = __builtin_amdgcn_readlane(tl, j);
+                    const int i = base + j;
+                    const bool same = pi == pa;
+                    nx = (same && i > c) ? min(nx, i) : nx;
+                    d |= (same && i < c && ti == x) ? 1 : 0;
+                }
+            }
+            if (valid) {
+                nsib[c] = nx == INT_MAX ? -1 : nx;
+                dup[c] = d;
+            }
         }
         __syncthreads();
         {   // compact list of internal rows, in index order
@@ -367,9 +390,18 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
         }
         const int ni = kGreedy ? 0 : s_ni;
 
-        // -- C. chunk statistics: one wave per item, items split over the team
+        // -- C. chunk statistics: one wave per item.  Workgroup `rank` of the team owns items
+        //    rank * kWaves + j + m * P * kWaves (j < kWaves); its waves take them in that order
+        //    from a workgroup counter in LDS as they finish, since the two waves sharing a SIMD do
+        //    not progress at the same rate (the older one is favoured at issue), which a fixed
+        //    split would turn into idle waves at the end of the phase
         const int nitems = (n1 + ni) * nchunk;
-        for (int it = rank * kWaves + w; it < nitems; it += P * kWaves) {
+        for (int kk = w;;) {
+            const int it = rank * kWaves + (kk % kWaves) + (kk / kWaves) * (P * kWaves);
+            if (it >= nitems) break;
+            int nk = 0;
+            if (lane == 0) nk = atomicAdd(&s_next, 1);
+            nk = __builtin_amdgcn_readfirstlane(nk);
             const bool isd = it >= n1 * nchunk;
             const int j = isd ? it - n1 * nchunk : it;
             const int row = isd ? ilist[j / nchunk] : j / nchunk;
@@ -464,76 +496,114 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                     put_word(slot + 1, __float_as_uint(s), tag);
                 }
             }
+            kk = nk;
         }
 
-        // -- D. combine the chunk statistics of every row (one wave per row, lanes over chunks)
-        for (int v = w; v < n1; v += kWaves) {
-            uint64_t* sv = sw + static_cast<int64_t>(v) * nchunk * 4;
-            if (kGreedy) {
-                float bv = -INFINITY;
-                int bi = INT_MAX;
-                for (int c = lane; c < nchunk; c += kWave) {
-                    uint32_t wv[2];
-                    get_words<2>(sv + c * 4, 2, tag, &s_to, wv);
-                    argmax_merge(bv, bi, __uint_as_float(wv[0]), static_cast<int>(wv[1]));
+        // -- D. combine the chunk statistics of every row.  Rows go in batches whose words fit the
+        //    segment buffer (free until the draw): each thread reads its share of the batch's
+        //    tagged words into LDS -- every load issued first, the words not yet published then
+        //    polled together -- so the whole batch costs about one round trip; then g lanes per row
+        //    (g = chunk count rounded up to a power of two, at most 64) reduce them, fp64 above
+        //    chunk level.  (A row has at most 256 bf16 / 512 fp32 chunks, 4 words each, so one row
+        //    always fits.)
+        {
+            constexpr int kStage = kMaxSeg / kThreads;
+            const int rw = nchunk * 4;
+            const int rb = min(n1, kMaxSeg / rw);
+            int g = 1;
+            while (g < nchunk && g < kWave) g <<= 1;
+            const int rpw = kWave / g, sub = lane / g, cl = lane % g;
+            for (int r0 = 0; r0 < n1; r0 += rb) {
+                const int nr = min(rb, n1 - r0);
+                const int nw = nr * rw;
+                uint64_t* src = sw + static_cast<int64_t>(r0) * rw;
+                uint64_t raw[kStage];
+                bool need[kStage];
+#pragma unroll
+                for (int j = 0; j < kStage; ++j) {
+                    const int i = t + j * kThreads;
+                    const int wi = i & 3;
+                    need[j] = i < nw && (wi < 2 || (!kGreedy && info[r0 + i / rw] != 0));
+                    raw[j] = need[j] ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
                 }
-                wave_argmax(bv, bi);
-                if (lane == 0) info[v] = (bi >= 0 && bi < V) ? bi : 0;
-            } else {
-                const bool dr = info[v] != 0;
-                float mt = -INFINITY, md = -INFINITY;
-                float a0[2], a1[2], b0[2], b1[2];   // up to 128 chunks per row held in registers
-                uint32_t wv[2][4];
-                for (int q2 = 0; q2 < 2; ++q2) {
-                    const int c = lane + q2 * kWave;
-                    const int n = (c < nchunk) ? (dr ? 4 : 2) : 0;
-                    get_words<4>(sv + (c < nchunk ? c : 0) * 4, n, tag, &s_to, wv[q2]);
+                auto missing = [&]() {
+                    bool any = false;
+#pragma unroll
+                    for (int j = 0; j < kStage; ++j) any |= need[j] && static_cast<uint32_t>(raw[j] >> 32) != tag;
+                    return any;
+                };
+                if (missing() && !s_to) {
+                    const uint64_t t0 = wall_clock64();
+                    do {
+                        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+                        for (int j = 0; j < kStage; ++j)
+                            if (need[j] && static_cast<uint32_t>(raw[j] >> 32) != tag)
+                                raw[j] = __hip_atomic_load(src + t + j * kThreads, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+                        if (wall_clock64() - t0 > kTimeoutTicks) {
+                            s_to = 1;
+                            break;
+                        }
+                    } while (missing());
                 }
 #pragma unroll
-                for (int q2 = 0; q2 < 2; ++q2) {
-                    const int c = lane + q2 * kWave;
-                    a0[q2] = -INFINITY; a1[q2] = 0.f; b0[q2] = -INFINITY; b1[q2] = 0.f;
-                    if (c < nchunk) {
-                        a0[q2] = __uint_as_float(wv[q2][0]);
-                        a1[q2] = __uint_as_float(wv[q2][1]);
-                        if (dr) {
-                            b0[q2] = __uint_as_float(wv[q2][2]);
-                            b1[q2] = __uint_as_float(wv[q2][3]);
+                for (int j = 0; j < kStage; ++j)
+                    if (need[j]) seg[t + j * kThreads] = __uint_as_float(static_cast<uint32_t>(raw[j]));
+                __syncthreads();
+                // wave-uniform loop over groups of rpw rows; lane group `sub` owns one row
+                for (int k0 = w * rpw; k0 < nr; k0 += kWaves * rpw) {
+                    const int rl = k0 + sub;
+                    const bool ok = rl < nr;
+                    const int v = r0 + rl;
+                    const float* sv = seg + (ok ? rl : 0) * rw;
+                    if (kGreedy) {
+                        float bv = -INFINITY;
+                        int bi = INT_MAX;
+                        if (ok)
+                            for (int c = cl; c < nchunk; c += g)
+                                argmax_merge(bv, bi, sv[c * 4], __float_as_int(sv[c * 4 + 1]));
+                        for (int o = g >> 1; o > 0; o >>= 1) {
+                            const float v2 = __shfl_xor(bv, o);
+                            const int i2 = __shfl_xor(bi, o);
+                            argmax_merge(bv, bi, v2, i2);
+                        }
+                        if (ok && cl == 0) info[v] = (bi >= 0 && bi < V) ? bi : 0;
+                    } else {
+                        const bool dr = ok && info[v] != 0;
+                        float mt = -INFINITY, md = -INFINITY;
+                        if (ok)
+                            for (int c = cl; c < nchunk; c += g) {
+                                mt = fmaxf(mt, sv[c * 4]);
+                                if (dr) md = fmaxf(md, sv[c * 4 + 2]);
+                            }
+                        for (int o = g >> 1; o > 0; o >>= 1) {
+                            mt = fmaxf(mt, __shfl_xor(mt, o));
+                            md = fmaxf(md, __shfl_xor(md, o));
+                        }
+                        double st = 0.0, sd = 0.0;
+                        if (ok)
+                            for (int c = cl; c < nchunk; c += g) {
+                                const float x0 = sv[c * 4], x1 = sv[c * 4 + 1];
+                                if (x0 != -INFINITY) st += static_cast<double>(x1) * __builtin_amdgcn_exp2f((x0 - mt) * k);
+                                if (dr) {
+                                    const float y0 = sv[c * 4 + 2], y1 = sv[c * 4 + 3];
+                                    if (y0 != -INFINITY) sd += static_cast<double>(y1) * __builtin_amdgcn_exp2f((y0 - md) * k);
+                                }
+                            }
+                        for (int o = g >> 1; o > 0; o >>= 1) {
+                            st += __shfl_xor(st, o);
+                            sd += __shfl_xor(sd, o);
+                        }
+                        if (ok && cl == 0) {
+                            Mt[v] = mt; St[v] = st;
+                            Md[v] = md; Sd[v] = sd;
                         }
                     }
-                    mt = fmaxf(mt, a0[q2]);
-                    md = fmaxf(md, b0[q2]);
                 }
-                for (int c = lane + 2 * kWave; c < nchunk; c += kWave) {
-                    mt = fmaxf(mt, __uint_as_float(get_word(sv + c * 4, tag, &s_to)));
-                    if (dr) md = fmaxf(md, __uint_as_float(get_word(sv + c * 4 + 2, tag, &s_to)));
-                }
-                mt = wave_max(mt);
-                md = wave_max(md);
-                double st = 0.0, sd = 0.0;
-                for (int q2 = 0; q2 < 2; ++q2) {
-                    if (a0[q2] != -INFINITY) st += static_cast<double>(a1[q2]) * __builtin_amdgcn_exp2f((a0[q2] - mt) * k);
-                    if (dr && b0[q2] != -INFINITY) sd += static_cast<double>(b1[q2]) * __builtin_amdgcn_exp2f((b0[q2] - md) * k);
-                }
-                for (int c = lane + 2 * kWave; c < nchunk; c += kWave) {
-                    const float x0 = __uint_as_float(get_word(sv + c * 4, tag, &s_to));
-                    const float x1 = __uint_as_float(get_word(sv + c * 4 + 1, tag, &s_to));
-                    if (x0 != -INFINITY) st += static_cast<double>(x1) * __builtin_amdgcn_exp2f((x0 - mt) * k);
-                    if (dr) {
-                        const float y0 = __uint_as_float(get_word(sv + c * 4 + 2, tag, &s_to));
-                        const float y1 = __uint_as_float(get_word(sv + c * 4 + 3, tag, &s_to));
-                        if (y0 != -INFINITY) sd += static_cast<double>(y1) * __builtin_amdgcn_exp2f((y0 - md) * k);
-                    }
-                }
-                st = wave_sum(st);
-                sd = wave_sum(sd);
-                if (lane == 0) {
-                    Mt[v] = mt; St[v] = st;
-                    Md[v] = md; Sd[v] = sd;
-                }
+                __syncthreads();
             }
         }
-        __syncthreads();
 
         // -- E. per node: p, q of its token under its parent's rows, the ratio, its two uniforms
         for (int v = t; v < n1; v += kThreads) {
@@ -545,12 +615,12 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                     const float zd = (v == t) ? gzd : Elem<T>::load(draft + (seq + pa) * V, tok[v]);
                     const double lp = (static_cast<double>(zt) - Mt[pa]) * invT;
                     const double lq = (static_cast<double>(zd) - Md[pa]) * invT;
-                    // the ratio that decides acceptance in fp64; p and q themselves (outputs, and q
-                    // for the residual bookkeeping) in fp32
+                    const double pd = exp(lp) / St[pa];
+                    const double qd = exp(lq) / Sd[pa];
                     pq[v] = exp(lp - lq) * (Sd[pa] / St[pa]);
-                    pv_ = expf(static_cast<float>(lp)) / static_cast<float>(St[pa]);
-                    qv_ = expf(static_cast<float>(lq)) / static_cast<float>(Sd[pa]);
-                    qx[v] = qv_;
+                    qx[v] = static_cast<float>(qd);
+                    pv_ = static_cast<float>(pd);
+                    qv_ = static_cast<float>(qd);
                 }
             }
             if (rank == 0) {
