@@ -50,6 +50,8 @@ constexpr int kWaveLoads = 16;              // 16-byte loads per lane per statis
 constexpr int kMaxVocab = 1 << 21;
 constexpr int kMaxTeam = 64;                // workgroups per sequence at most
 constexpr int kPassBatch = 4;               // tiles per batch of a range pass
+constexpr int kMaskNodes = 128;             // trees up to this size keep children bit masks
+constexpr int kMaskWords = kMaskNodes / 64;
 constexpr uint64_t kTimeoutTicks = 50000000ull;   // 0.5 s of the 100 MHz wall clock
 
 template <typename T>
@@ -255,6 +257,7 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
     __shared__ int32_t fch[kMaxNodes];      // first child (n1 if none)
     __shared__ int32_t nsib[kMaxNodes];     // next sibling (-1 if none)
     __shared__ int32_t dup[kMaxNodes];      // token repeats an earlier sibling's
+    __shared__ uint64_t cmask[kMaskNodes][kMaskWords];   // children of each node as a bit mask
     __shared__ int32_t ilist[kMaxNodes];    // internal rows in index order
     __shared__ float Mt[kMaxNodes], Md[kMaxNodes];
     __shared__ double St[kMaxNodes], Sd[kMaxNodes];
@@ -297,6 +300,7 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
             info[i] = 0;
             fch[i] = n1;
         }
+        for (int i = t; i < kMaskNodes * kMaskWords; i += kThreads) cmask[i / kMaskWords][i % kMaskWords] = 0;
         __syncthreads();
         for (int i = t; i < n1; i += kThreads) {
             const int p = parent[seq + i];
@@ -335,39 +339,68 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                 ures[v] = word_to_uniform(rnd.w[1]);
             }
         }
-        // next sibling (smallest i > c with the same parent) and repeated token (an earlier
-        // sibling with the same token): each wave walks all nodes 64 at a time, one LDS read per
-        // lane, the values handed to every lane by readlane, so no step waits on LDS
-        for (int c0 = 1 + wu * kWave; c0 < n1; c0 += kThreads) {     // wave-uniform
-            const int c = c0 + lane;
-            const bool valid = c < n1;
-            const int pa = valid ? par[c] : -3;
-            const int x = valid ? tok[c] : -1;
-            if (valid) {
-                info[pa] = 1;
-                atomicMin(&fch[pa], c);
-            }
-            int nx = INT_MAX, d = 0;
-            for (int base = 0; base < n1; base += kWave) {
-                const int i0 = base + lane;
-                const int pl = i0 < n1 ? par[i0] : -2;
-                const int tl = i0 < n1 ? tok[i0] : -1;
-                const int cnt = min(kWave, n1 - base);
-                for (int j = 0; j < cnt; ++j) {
-                    const int pi = __builtin_amdgcn_readlane(pl, j);
-                    const int ti = __builtin_amdgcn_readlane(tl, j);
-                    const int i = base + j;
-                    const bool same = pi == pa;
-                    nx = (same && i > c) ? min(nx, i) : nx;
-                    d |= (same && i < c && ti == x) ? 1 : 0;
+        // first child of every parent; for trees of at most kMaskNodes nodes also each parent's
+        // children as a bit mask, from which next siblings and repeated tokens follow after the
+        // barrier
+        const bool small = n1 <= kMaskNodes;
+        for (int c = 1 + t; c < n1; c += kThreads) {
+            const int pa = par[c];
+            info[pa] = 1;
+            atomicMin(&fch[pa], c);
+            if (small) atomicOr(&cmask[pa][c >> 6], 1ull << (c & 63));
+        }
+        if (!small) {
+            // larger trees: each wave walks all nodes 64 at a time, one LDS read per lane, the
+            // values handed to every lane by readlane; next sibling = smallest i > c with the same
+            // parent, repeated token = an earlier sibling with the same token
+            for (int c0 = 1 + wu * kWave; c0 < n1; c0 += kThreads) {     // wave-uniform
+                const int c = c0 + lane;
+                const bool valid = c < n1;
+                const int pa = valid ? par[c] : -3;
+                const int x = valid ? tok[c] : -1;
+                int nx = INT_MAX, d = 0;
+                for (int base = 0; base < n1; base += kWave) {
+                    const int i0 = base + lane;
+                    const int pl = i0 < n1 ? par[i0] : -2;
+                    const int tl = i0 < n1 ? tok[i0] : -1;
+                    const int cnt = min(kWave, n1 - base);
+                    for (int j = 0; j < cnt; ++j) {
+                        const int pi = __builtin_amdgcn_readlane(pl, j);
+                        const int ti = __builtin_amdgcn_readlane(tl, j);
+                        const int i = base + j;
+                        const bool same = pi == pa;
+                        nx = (same && i > c) ? min(nx, i) : nx;
+                        d |= (same && i < c && ti == x) ? 1 : 0;
+                    }
                 }
-            }
-            if (valid) {
-                nsib[c] = nx == INT_MAX ? -1 : nx;
-                dup[c] = d;
+                if (valid) {
+                    nsib[c] = nx == INT_MAX ? -1 : nx;
+                    dup[c] = d;
+                }
             }
         }
         __syncthreads();
+        if (small) {
+            for (int c = 1 + t; c < n1; c += kThreads) {
+                const int x = tok[c], pa = par[c], cw = c >> 6, cb = c & 63;
+                int nx = -1, d = 0;
+#pragma unroll
+                for (int q = kMaskWords - 1; q >= 0; --q) {
+                    const uint64_t m = cmask[pa][q];
+                    // siblings after c in this word (all of it if the word is past c's; cb <= 63,
+                    // so 2 << cb wraps to 0 only for cb == 63, leaving no bits)
+                    const uint64_t later = q > cw ? m : (q == cw ? m & ~((2ull << cb) - 1ull) : 0ull);
+                    if (later) nx = 64 * q + __builtin_ctzll(later);
+                    uint64_t earlier = q < cw ? m : (q == cw ? m & ((1ull << cb) - 1ull) : 0ull);
+                    while (earlier) {
+                        d |= tok[64 * q + __builtin_ctzll(earlier)] == x;
+                        earlier &= earlier - 1ull;
+                    }
+                }
+                nsib[c] = nx;
+                dup[c] = d;
+            }
+        }
         {   // compact list of internal rows, in index order
             int done = 0;
             for (int base = 0; base < n1; base += kThreads) {
