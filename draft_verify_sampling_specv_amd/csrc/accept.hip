@@ -50,6 +50,7 @@ constexpr int kWaveLoads = 16;              // 16-byte loads per lane per statis
 constexpr int kMaxVocab = 1 << 21;
 constexpr int kMaxTeam = 64;                // workgroups per sequence at most
 constexpr int kPassBatch = 4;               // tiles per batch of a range pass
+constexpr int kBufferWord3 = 0x00020000;    // raw buffer descriptor, word 3 (CDNA)
 constexpr int kMaskNodes = 128;             // trees up to this size keep children bit masks
 constexpr int kMaskWords = kMaskNodes / 64;
 constexpr uint64_t kTimeoutTicks = 50000000ull;   // 0.5 s of the 100 MHz wall clock
@@ -90,6 +91,34 @@ __device__ __forceinline__ float draw_weight(float zt, float zd, float mt, float
     const float p = __builtin_amdgcn_exp2f((zt - mt) * k) * p_scale;
     const float q = __builtin_amdgcn_exp2f((zd - md) * k) * q_scale;
     return fmaxf(p - q, 0.0f);
+}
+
+// The 16-byte words of one statistics item: lane l gets vectors u * 64 + l (u < kWaveLoads) of
+// the element range [lo, hi) of `row`.  Buffer loads: one descriptor per wave (row, lo and hi are
+// wave-uniform) and one offset register for all loads, the vector index in the immediate part,
+// so nothing per load stays live; vectors past hi come back as 0 from the range check (whole
+// vectors: V is a multiple of the vector length on this path) and are masked where used.
+template <typename T>
+__device__ __forceinline__ void load_item(const T* row, int lo, int hi, int lane, uint4 (&r)[kWaveLoads]) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(row + lo), 0, (hi - lo) * static_cast<int>(sizeof(T)), kBufferWord3);
+#pragma unroll
+    for (int u = 0; u < kWaveLoads; ++u) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, u * kWave * 16, 0);
+        r[u] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+}
+
+// A logit's raw bits in a 32-bit word, and back as fp32 (bf16: its bits in the high half; exact).
+__device__ __forceinline__ uint32_t raw_bits(float x) { return __float_as_uint(x); }
+__device__ __forceinline__ uint32_t raw_bits(uint16_t x) { return x; }
+template <typename T>
+__device__ __forceinline__ float widen(uint32_t b) { return __uint_as_float(sizeof(T) == 2 ? b << 16 : b); }
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations (and scalar
+// loads), not for its global loads still in flight, which __syncthreads would also wait for.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Publish / read a tagged 64-bit word (value in the low half, launch tag in the high half).
@@ -251,6 +280,10 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
     constexpr int kTile = kThreads * kVec;
     constexpr int kItem = item_elems<T>();
     constexpr int kMaxSeg = (kMaxVocab + kTile - 1) / kTile * kWaves;
+    // first statistics item loaded during A and B: bf16 logits only (with fp32 logits the longer
+    // live ranges make the compiler spill there, and waiting on the spill reloads would wait on
+    // the item anyway)
+    constexpr bool kPre = kVecOK && sizeof(T) == 2;
     __shared__ int32_t par[kMaxNodes];
     __shared__ int32_t tok[kMaxNodes];
     __shared__ int32_t info[kMaxNodes];     // greedy: argmax token of the row; else: has children
@@ -290,8 +323,12 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
         uint64_t* sw = statw + seq * nchunk * 4;
         uint64_t* pw = partw + static_cast<int64_t>(b) * (n1 + 1) * P;
 
-        // -- A. stage and validate the parent array and the draft tokens
-        __syncthreads();
+        // -- A. stage and validate the parent array and the draft tokens.  The barriers of A and
+        //    B order LDS only, so the loads of this wave's first statistics item, issued here when
+        //    it is a target-row chunk (those do not depend on the tree), stay in flight through A
+        //    and B.  Every thread first loads one parent and token (clamped index), so that waiting
+        //    for them does not mean waiting for the item.
+        lds_barrier();
         if (t == 0) {
             s_bad = 0;
             s_next = kWaves;      // the first kWaves takes of the statistics phase are by position
@@ -301,16 +338,31 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
             fch[i] = n1;
         }
         for (int i = t; i < kMaskNodes * kMaskWords; i += kThreads) cmask[i / kMaskWords][i % kMaskWords] = 0;
-        __syncthreads();
+        // (relaxed atomic loads: unlike loads of read-only arguments the compiler does not sink
+        // them below the barrier, so they are issued ahead of the item's loads)
+        const int pa0 = __hip_atomic_load(parent + seq + min(t, n1 - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const int xa0 = __hip_atomic_load(tokens + seq + min(t, n1 - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        asm volatile("" ::: "memory");
+        uint4 r[kWaveLoads];
+        const int it0 = rank * kWaves + wu;
+        const bool pre = kPre && it0 < n1 * nchunk;       // wave-uniform
+        if constexpr (kPre) {
+            // issued by every wave (branch-free, so the compiler's count of outstanding loads
+            // stays exact); a wave without a target-row first item gets an empty range, whose
+            // loads return without touching memory
+            const int i0 = min(it0, n1 * nchunk - 1), lo = (i0 % nchunk) * kItem;
+            load_item<T>(target + (seq + i0 / nchunk) * V, lo, pre ? min(V, lo + kItem) : lo, lane, r);
+        }
+        lds_barrier();
         for (int i = t; i < n1; i += kThreads) {
-            const int p = parent[seq + i];
-            const int x = tokens[seq + i];
+            const int p = i == t ? pa0 : parent[seq + i];
+            const int x = i == t ? xa0 : tokens[seq + i];
             par[i] = p;
             tok[i] = x;
             const bool ok = (i == 0) ? (p == -1) : (p >= 0 && p < i && x >= 0 && x < V);
             if (!ok) s_bad = 1;
         }
-        __syncthreads();
+        lds_barrier();
         if (s_bad) {
             if (rank == 0) {
                 for (int i = t; i < n1; i += kThreads) {
@@ -325,11 +377,12 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
         }
 
         // -- B. tree links, internal rows; gather every draft token's logits under its parent's rows
-        float gzt = 0.f, gzd = 0.f;
+        // (raw bits, made opaque and widened only in E, so that nothing waits for them before)
+        uint32_t gzt = 0, gzd = 0;
         if (!kGreedy && t > 0 && t < n1) {
             const int pa = par[t], x = tok[t];
-            gzt = Elem<T>::load(target + (seq + pa) * V, x);
-            gzd = Elem<T>::load(draft + (seq + pa) * V, x);
+            gzt = raw_bits(target[(seq + pa) * V + x]);
+            gzd = raw_bits(draft[(seq + pa) * V + x]);
         }
         // both uniforms of every node (Philox; computed while the gathers are in flight)
         if (!kGreedy) {
@@ -379,7 +432,7 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         if (small) {
             for (int c = 1 + t; c < n1; c += kThreads) {
                 const int x = tok[c], pa = par[c], cw = c >> 6, cb = c & 63;
@@ -408,7 +461,7 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                 const bool f = v < n1 && info[v] != 0;
                 const uint64_t m = __ballot(f);
                 if (lane == 0) wcount[w] = __popcll(m);
-                __syncthreads();
+                lds_barrier();
                 int before = 0, all = 0;
                 for (int i = 0; i < kWaves; ++i) {
                     if (i < w) before += wcount[i];
@@ -416,10 +469,10 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                 }
                 if (f) ilist[done + before + __popcll(m & ((1ull << lane) - 1ull))] = v;
                 done += all;
-                __syncthreads();
+                lds_barrier();
             }
             if (t == 0) s_ni = done;
-            __syncthreads();
+            lds_barrier();
         }
         const int ni = kGreedy ? 0 : s_ni;
 
@@ -429,7 +482,7 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
         //    not progress at the same rate (the older one is favoured at issue), which a fixed
         //    split would turn into idle waves at the end of the phase
         const int nitems = (n1 + ni) * nchunk;
-        for (int kk = w;;) {
+        for (int kk = wu;;) {     // (wave-uniform)
             const int it = rank * kWaves + (kk % kWaves) + (kk / kWaves) * (P * kWaves);
             if (it >= nitems) break;
             int nk = 0;
@@ -437,22 +490,15 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
             nk = __builtin_amdgcn_readfirstlane(nk);
             const bool isd = it >= n1 * nchunk;
             const int j = isd ? it - n1 * nchunk : it;
-            const int row = isd ? ilist[j / nchunk] : j / nchunk;
+            const int row = isd ? __builtin_amdgcn_readfirstlane(ilist[j / nchunk]) : j / nchunk;
             const int c = j % nchunk;
             const T* src = (isd ? draft : target) + (seq + row) * V;
             const int lo = c * kItem, hi = min(V, lo + kItem);
             uint64_t* slot = sw + (static_cast<int64_t>(row) * nchunk + c) * 4 + (isd ? 2 : 0);
             // values of load u are converted from the raw words when used (two passes: max, then
-            // sum of exp), so only the raw 16-byte words stay in registers
-            uint4 r[kWaveLoads];
-            if (kVecOK) {
-#pragma unroll
-                for (int u = 0; u < kWaveLoads; ++u) {
-                    const int base = lo + (u * kWave + lane) * kVec;
-                    r[u] = make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
-                    if (base < hi) r[u] = *reinterpret_cast<const uint4*>(src + base);
-                }
-            }
+            // sum of exp), so only the raw 16-byte words stay in registers.  (The wave's first
+            // item, kk == w, was loaded in A when `pre`.)
+            if (kVecOK && !(pre && kk == wu)) load_item<T>(src, lo, hi, lane, r);
             auto values = [&](int u, float* z) {
                 const int base = lo + (u * kWave + lane) * kVec;
                 if (kVecOK) {
@@ -639,13 +685,14 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
         }
 
         // -- E. per node: p, q of its token under its parent's rows, the ratio, its two uniforms
+        asm volatile("" : "+v"(gzt), "+v"(gzd));
         for (int v = t; v < n1; v += kThreads) {
             float pv_ = NAN, qv_ = NAN;
             if (!kGreedy) {
                 if (v > 0) {
                     const int pa = par[v];
-                    const float zt = (v == t) ? gzt : Elem<T>::load(target + (seq + pa) * V, tok[v]);
-                    const float zd = (v == t) ? gzd : Elem<T>::load(draft + (seq + pa) * V, tok[v]);
+                    const float zt = (v == t) ? widen<T>(gzt) : Elem<T>::load(target + (seq + pa) * V, tok[v]);
+                    const float zd = (v == t) ? widen<T>(gzd) : Elem<T>::load(draft + (seq + pa) * V, tok[v]);
                     const double lp = (static_cast<double>(zt) - Mt[pa]) * invT;
                     const double lq = (static_cast<double>(zd) - Md[pa]) * invT;
                     const double pd = exp(lp) / St[pa];
