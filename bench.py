@@ -213,6 +213,15 @@ def main():
     ms_greedy = timed(lambda i: specv.accept_resample(g_target, None, g_tokens, parent, 0.0, buffers=gbuf),
                       args.steps)
     ms_mask = timed(lambda i: specv.build_tree_mask(parent, out=mask_out), args.steps)
+    # the step after verify: KV-cache commit of the accepted paths (a chain's accepted rows are
+    # already in place, so this is the validation and bookkeeping cost), on a copy of the cache
+    res_c = specv.accept_resample(acc_sets[0]["target"], acc_sets[0]["draft"], acc_sets[0]["tokens"], parent, T,
+                                  seed=1234, offset=0)
+    kcc, vcc = attn_sets[0][1].clone(), attn_sets[0][2].clone()
+    new_ctx = torch.empty_like(ctx_len)
+    ms_commit = timed(lambda i: specv.kv_commit(kcc, vcc, ctx_len, res_c.accept_len, res_c.out_nodes, out=new_ctx),
+                      args.steps)
+    del kcc, vcc
 
     # measured streaming ceiling on this machine: device-to-device copy of 1 GiB (read + write bytes)
     big = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -260,6 +269,7 @@ def main():
         "accept_only_positions_per_s": positions / (ms_accept * 1e-3),
         "ms_mask": ms_mask,
         "ms_greedy_accept": ms_greedy,
+        "ms_kv_commit": ms_commit,
         "mean_accept_len": mean_len,
         "hbm_copy_gbs": copy_gbs,
     }
@@ -343,6 +353,14 @@ def measure_config(name, args, torch, specv, workloads):
                                                    buffers=cbuf), steps)
     r = specv.accept_resample(tl, dl, tok, par, w.T, seed=1, offset=0, buffers=cbuf)
     accept_len = r.accept_len.cpu().numpy()
+    out_nodes = r.out_nodes.cpu().numpy()
+    # KV-cache commit of the accepted paths (the step after the verify step, not part of it), on a
+    # copy of the cache; every call moves the same rows
+    kcc, vcc = kc.clone(), vc.clone()
+    new_ctx = torch.empty_like(cl)
+    ms_commit = timed(lambda i: specv.kv_commit(kcc, vcc, cl, r.accept_len, r.out_nodes, out=new_ctx), steps)
+    moved = sum(1 for b in range(B) for d in range(1, int(accept_len[b]) + 1) if out_nodes[b, d - 1] != d)
+    del kcc, vcc
 
     # algorithmic work
     pa = w.parent
@@ -367,6 +385,8 @@ def measure_config(name, args, torch, specv, workloads):
                       "arith_intensity": att_f / att_b},
         "accept": {"bytes": acc_b, "GBps": acc_b / (ms_acc * 1e-3) / 1e9,
                    "hbm_frac": acc_b / (ms_acc * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "kv_commit": {"ms": ms_commit, "rows_moved": moved,
+                      "bytes": moved * 2 * 2 * a.k_cache.shape[1] * a.q.shape[3] * (2 if a.dtype == "bf16" else 4)},
         "positions_per_s_accept_only": positions / (ms_acc * 1e-3),
         "positions_per_s_verify": positions / ((ms_mask + ms_attn + ms_acc) * 1e-3),
         "mean_tokens_per_step": float(np.mean(accept_len + 1)),

@@ -8,6 +8,7 @@ library has not been built this import fails.
   build_tree_mask(parent)                                  -> mask, depth, status
   tree_attn_verify(q, k_cache, v_cache, ctx_len, mask)     -> out, lse
   accept_resample(target, draft, tokens, parent, T, seed, offset) -> AcceptResult
+  kv_commit(k_cache, v_cache, ctx_len, accept_len, out_nodes)     -> new_ctx_len
 """
 
 from ._lib import (  # noqa: F401
@@ -20,6 +21,7 @@ from ._lib import (  # noqa: F401
     build_tree_mask,
     tree_attn_verify,
     accept_resample,
+    kv_commit,
     accept_workspace_bytes,
     attn_workspace_bytes,
 )

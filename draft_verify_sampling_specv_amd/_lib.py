@@ -46,6 +46,12 @@ lib.specv_accept_resample.argtypes = [
     ctypes.c_uint64, ctypes.c_uint64,
     _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 
+lib.specv_kv_commit.restype = ctypes.c_int
+lib.specv_kv_commit.argtypes = [
+    _vp, _vp, _vp, _vp, _vp,
+    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+    ctypes.c_int, _vp, _vp]
+
 
 class SpecvError(RuntimeError):
     def __init__(self, fn, status):
@@ -197,3 +203,25 @@ def accept_resample(target_logits, draft_logits, tokens, parent, temperature, se
         _ptr(r.p_tok) if with_probs else None, _ptr(r.q_tok) if with_probs else None,
         _ptr(bufs.workspace), bufs.workspace.numel(), _stream()))
     return r
+
+
+# ----------------------------------------------------------------------------- KV commit
+
+def kv_commit(k_cache, v_cache, ctx_len, accept_len, out_nodes, out=None):
+    """Move the accepted path's K/V rows in place; returns new_ctx_len[B] int32 (-1: invalid)."""
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor (it is updated in place)")
+    if k_cache.dtype != v_cache.dtype or k_cache.shape != v_cache.shape:
+        raise TypeError("k_cache and v_cache must match in dtype and shape")
+    ctx_len, accept_len = _dev(ctx_len, torch.int32), _dev(accept_len, torch.int32)
+    out_nodes = _dev(out_nodes, torch.int32)
+    B, Hkv, Lmax, D = k_cache.shape
+    n1 = out_nodes.shape[1]
+    if ctx_len.shape != (B,) or accept_len.shape != (B,) or out_nodes.shape != (B, n1):
+        raise ValueError("ctx_len, accept_len must be [B] and out_nodes [B][K+1]")
+    new_ctx = out if out is not None else torch.empty((B,), dtype=torch.int32, device=k_cache.device)
+    _check("specv_kv_commit", lib.specv_kv_commit(
+        _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), _ptr(accept_len), _ptr(out_nodes),
+        B, n1 - 1, Hkv, D, Lmax, _dtype_code(k_cache), _ptr(new_ctx), _stream()))
+    return new_ctx

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdint>
 #include <cstring>
 
 #include "../../include/specv.h"
@@ -128,6 +129,28 @@ specv_status specv_accept_resample(const void* target_logits, const void* draft_
                         logits_dtype == SPECV_BF16, tokens, parent, B, K + 1, V, temperature,
                         seed, offset, accept_len, out_tokens, out_nodes, p_tok, q_tok, workspace};
     return hip_status(specv::launch_accept(a, stream), "accept_resample");
+}
+
+specv_status specv_kv_commit(void* k_cache, void* v_cache, const int32_t* ctx_len,
+                             const int32_t* accept_len, const int32_t* out_nodes, int32_t B,
+                             int32_t K, int32_t Hkv, int32_t D, int32_t Lmax, specv_dtype dtype,
+                             int32_t* new_ctx_len, hipStream_t stream) {
+    if (B < 0) return fail(SPECV_ERR_INVALID_ARG, "B = %d < 0", B);
+    if (K < 0 || K + 1 > SPECV_MAX_NODES)
+        return fail(SPECV_ERR_INVALID_ARG, "K = %d outside [0, %d]", K, SPECV_MAX_NODES - 1);
+    if (Hkv <= 0) return fail(SPECV_ERR_INVALID_ARG, "Hkv = %d <= 0", Hkv);
+    if (Lmax < K + 1) return fail(SPECV_ERR_INVALID_ARG, "Lmax = %d < K + 1 = %d", Lmax, K + 1);
+    if (dtype != SPECV_F32 && dtype != SPECV_BF16)
+        return fail(SPECV_ERR_UNSUPPORTED, "dtype %d not supported", static_cast<int>(dtype));
+    if (D != 64 && D != 128) return fail(SPECV_ERR_UNSUPPORTED, "head size D = %d not in {64, 128}", D);
+    if (B == 0) return ok();
+    if (!k_cache || !v_cache || !ctx_len || !accept_len || !out_nodes || !new_ctx_len)
+        return fail(SPECV_ERR_INVALID_ARG, "NULL pointer argument");
+    if ((reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache)) & 15)
+        return fail(SPECV_ERR_INVALID_ARG, "k_cache and v_cache must be 16-byte aligned");
+    specv::KvCommitArgs a{k_cache, v_cache, ctx_len, accept_len, out_nodes, B, K + 1, Hkv, D, Lmax,
+                          dtype == SPECV_BF16, new_ctx_len};
+    return hip_status(specv::launch_kv_commit(a, stream), "kv_commit");
 }
 
 }  // extern "C"

@@ -60,8 +60,26 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const int Ltot = L + n1;
     const int ntiles = seq_ok ? (Ltot + kTileKeys - 1) / kTileKeys : 0;
 
-    // this lane's mask row in registers: the decode shape has at most 64 rows per KV head, so at
-    // most 64 nodes and two mask words
+    const uint16_t* kbase = kc + (static_cast<int64_t>(b) * Hkv + kv) * Lmax * D;
+    const uint16_t* vbase = vc + (static_cast<int64_t>(b) * Hkv + kv) * Lmax * D;
+
+    // Loads are unconditional: a key past the sequence reads its last key instead (finite data,
+    // masked out by the softmax; key 0 for an invalid sequence, whose output is NaN anyway).
+    // With no register loaded under a branch, the compiler's load counting stays exact, so a
+    // wait for one load is not a wait for the loads issued after it.
+    const int kmax = seq_ok ? Ltot - 1 : 0;
+    uint4 kn[kKS];
+    auto load_k = [&](int t) {
+        const int kkey = min(t * kTileKeys + col, kmax);
+#pragma unroll
+        for (int s2 = 0; s2 < kKS; ++s2)
+            kn[s2] = *reinterpret_cast<const uint4*>(kbase + static_cast<int64_t>(kkey) * D + 16 * s2 + 8 * h);
+    };
+
+    // Issue order: this lane's mask words and Q word, then the wave's first K tile, so the K
+    // stream starts before the Q operands are staged (the staging waits only for the Q word).
+    // The mask row stays in registers: the decode shape has at most 64 rows per KV head, so at
+    // most 64 nodes and two mask words.
     int rows[RBW];
     bool rok[RBW];
     uint64_t mbits[RBW];
@@ -71,35 +89,30 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         rok[j] = rows[j] < R;
         const int node = rok[j] ? rows[j] / G : 0;
         const uint32_t* mrow = mask + (static_cast<int64_t>(b) * n1 + node) * words;
-        mbits[j] = mrow[0] | (words > 1 ? static_cast<uint64_t>(mrow[1]) << 32 : 0ull);
+        const uint32_t w0 = mrow[0], w1 = mrow[words > 1 ? 1 : 0];
+        mbits[j] = w0 | (words > 1 ? static_cast<uint64_t>(w1) << 32 : 0ull);
     }
-    // stage Q^T operands: entry (j, s, lane) = Q[row j*32 + col][16 s + 8 h .. +8]
-    for (int e = threadIdx.x; e < RBW * kKS * kWave; e += KS * kWave) {
-        const int j = e / (kKS * kWave), s2 = (e / kWave) % kKS, ln = e % kWave;
-        const int row = (grp * RBW + j) * 32 + ln % 32;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (row < R) {
-            const int node = row / G, g = row - node * G;
-            v = *reinterpret_cast<const uint4*>(q + ((static_cast<int64_t>(b) * n1 + node) * Hq + kv * G + g) * D +
-                                                16 * s2 + 8 * (ln / 32));
-        }
-        sq[j][s2][ln] = v;
-    }
-    __syncthreads();
-
-    const uint16_t* kbase = kc + (static_cast<int64_t>(b) * Hkv + kv) * Lmax * D;
-    const uint16_t* vbase = vc + (static_cast<int64_t>(b) * Hkv + kv) * Lmax * D;
-
-    // Loads are unconditional: a key past the sequence reads its last key instead (finite data,
-    // masked out by the softmax).  With no register zeroed under a branch, the compiler's load
-    // counting stays exact and the next tile's K stays in flight while this tile is computed.
-    uint4 kn[kKS];
-    auto load_k = [&](int t) {
-        const int kkey = min(t * kTileKeys + col, Ltot - 1);
-#pragma unroll
-        for (int s2 = 0; s2 < kKS; ++s2)
-            kn[s2] = *reinterpret_cast<const uint4*>(kbase + static_cast<int64_t>(kkey) * D + 16 * s2 + 8 * h);
-    };
+    // Q^T operand entries (j, s, lane) = Q[row j*32 + col][16 s + 8 h .. +8]: one per thread
+    static_assert(RBW * kKS * kWave <= KS * kWave, "one Q^T entry per thread");
+    const int qe = threadIdx.x;
+    const bool qown = qe < RBW * kKS * kWave;
+    const int qj = qe / (kKS * kWave), qs = (qe / kWave) % kKS, qln = qe % kWave;
+    const int qrow = (grp * RBW + qj) * 32 + qln % 32;
+    const int qrc = min(qrow, R - 1);
+    const int qnode = qrc / G, qg = qrc - qnode * G;
+    // (relaxed atomic loads: the compiler keeps them ahead of the K loads, which it would
+    // otherwise be free to issue first, turning the wait for Q into a wait for K)
+    const uint64_t* qp = reinterpret_cast<const uint64_t*>(
+        q + ((static_cast<int64_t>(b) * n1 + qnode) * Hq + kv * G + qg) * D + 16 * qs + 8 * (qln / 32));
+    const uint64_t q0 = __hip_atomic_load(qp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint64_t q1 = __hip_atomic_load(qp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    asm volatile("" ::: "memory");
+    load_k(min(w, max(ntiles - 1, 0)));
+    const uint4 qv = make_uint4(static_cast<uint32_t>(q0), static_cast<uint32_t>(q0 >> 32),
+                                static_cast<uint32_t>(q1), static_cast<uint32_t>(q1 >> 32));
+    if (qown) sq[qj][qs][qln] = qrow < R ? qv : make_uint4(0, 0, 0, 0);
+    // LDS-only barrier: the K tile stays in flight
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
     f32x16_t o[RBW][kDB];
     float m[RBW], l[RBW];
@@ -111,7 +124,6 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         for (int i = 0; i < kDB; ++i) o[j][i] = f32x16_t{};
     }
 
-    if (w < ntiles) load_k(w);
     for (int t = w; t < ntiles; t += KS) {
         const int kb = t * kTileKeys;
         uint4 kcur[kKS];
@@ -123,7 +135,7 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int key = min(kb + 16 * ks + 8 * (e / 4) + 4 * h + (e % 4), Ltot - 1);
+                const int key = min(kb + 16 * ks + 8 * (e / 4) + 4 * h + (e % 4), kmax);
 #pragma unroll
                 for (int dh = 0; dh < kDH; ++dh)
                     vr[ks][dh][e] = *reinterpret_cast<const uint32_t*>(vbase + static_cast<int64_t>(key) * D + 64 * dh + 2 * col);

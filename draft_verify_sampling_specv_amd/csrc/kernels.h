@@ -46,6 +46,20 @@ struct AcceptArgs {
 size_t accept_workspace_bytes(int B, int n1, int V, bool bf16);
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
 
+// ------------------------------------------------------------------------------------ KV commit
+struct KvCommitArgs {
+    void* k_cache;
+    void* v_cache;
+    const int32_t* ctx_len;
+    const int32_t* accept_len;
+    const int32_t* out_nodes;
+    int B, n1, Hkv, D, Lmax;
+    bool bf16;
+    int32_t* new_ctx_len;
+};
+
+hipError_t launch_kv_commit(const KvCommitArgs& a, hipStream_t stream);
+
 // ------------------------------------------------------------------------------------ attention
 struct AttnArgs {
     const void* q;

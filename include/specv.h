@@ -1,7 +1,8 @@
 /*
  * specv -- the verify step of speculative decoding on AMD MI355X (gfx950).
  *
- * Three operations, each asynchronous on the caller's HIP stream:
+ * The verify step as three operations, each asynchronous on the caller's HIP
+ * stream:
  *
  *   specv_build_tree_mask   ancestor mask and depth of every draft node, from
  *                           a parent array;
@@ -10,7 +11,10 @@
  *                           committed context plus its own ancestors;
  *   specv_accept_resample   the exact accept / reject / resample rule over the
  *                           vocabulary, for chains and for trees, greedy at
- *                           temperature 0.
+ *                           temperature 0;
+ * and the step after them:
+ *   specv_kv_commit         keep the accepted path's KV-cache rows, drop the
+ *                           rejected branches'.
  *
  * Sources (web pages on speculative decoding):
  *   [SD-review] paper review of Leviathan, Kalman, Matias, "Fast Inference
@@ -196,6 +200,41 @@ specv_status specv_accept_resample(const void* target_logits, const void* draft_
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 size_t specv_accept_workspace_bytes(int32_t B, int32_t K, int32_t V, specv_dtype logits_dtype);
+
+/*
+ * KV-cache commit after a verify step: keep the accepted path, drop the rest.
+ *
+ * [SD-review] §4 (limitations): the cache entries of rejected drafts have to
+ * be rolled back; [SD-EAGLE] "Tree Attention Verification": the verify pass
+ * wrote one extra KV-cache entry per tree node, node j's at ctx_len[b] + j.
+ * With the accept rule's result (accept_len[b] = a, out_nodes[b] = n_1 < ...
+ * < n_a, n_d the accepted node at depth d), the committed sequence is the
+ * context, the root and that path: for d = 1 .. a the K and V rows at
+ * ctx_len[b] + n_d move to ctx_len[b] + d (rows already in place, n_d == d,
+ * are not touched), and the new context length is ctx_len[b] + 1 + a.  Rows
+ * at and after the new length are left unspecified (the next verify step
+ * writes its tree there).
+ *
+ *   k_cache, v_cache  [B][Hkv][Lmax][D] dtype, updated in place; 16-byte aligned
+ *   ctx_len           [B] int32: context length before the verify step
+ *   accept_len        [B] int32, out_nodes [B][K+1] int32: from
+ *                     specv_accept_resample on the same tree
+ *   dtype             SPECV_BF16 or SPECV_F32 (the cache's element type)
+ *   new_ctx_len       [B] int32: ctx_len + 1 + accept_len; -1 (and the
+ *                     sequence's cache untouched) if accept_len is outside
+ *                     [0, K], ctx_len < 0 or ctx_len + K + 1 > Lmax, or
+ *                     out_nodes[0 .. a-1] is not an increasing list with the
+ *                     depth-d entry in [d, K]
+ *
+ * Ownership: device memory owned by the caller; asynchronous on `stream`.
+ * Errors: SPECV_ERR_INVALID_ARG (NULL pointer, B < 0, K < 0,
+ * K + 1 > SPECV_MAX_NODES, Hkv <= 0, Lmax < K + 1, misaligned cache),
+ * SPECV_ERR_UNSUPPORTED (D not 64 or 128, unknown dtype), SPECV_ERR_HIP.
+ */
+specv_status specv_kv_commit(void* k_cache, void* v_cache, const int32_t* ctx_len,
+                             const int32_t* accept_len, const int32_t* out_nodes,
+                             int32_t B, int32_t K, int32_t Hkv, int32_t D, int32_t Lmax,
+                             specv_dtype dtype, int32_t* new_ctx_len, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* specv_status_string(specv_status s);

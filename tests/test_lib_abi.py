@@ -24,7 +24,7 @@ def test_header_declares_the_three_operations():
     names = declared_functions()
     for n in ("specv_build_tree_mask", "specv_tree_attn_verify", "specv_accept_resample",
               "specv_accept_workspace_bytes", "specv_attn_workspace_bytes", "specv_status_string",
-              "specv_last_error"):
+              "specv_last_error", "specv_kv_commit"):
         assert n in names
 
 
@@ -118,3 +118,26 @@ def test_attention_and_mask_host_validation(specv):
     assert lib.specv_build_tree_mask(v, -2, 3, v, v, v, None) == 1
     assert lib.specv_build_tree_mask(v, 2, 1024, v, v, v, None) == 1
     assert lib.specv_build_tree_mask(None, 0, 3, None, None, None, None) == 0
+
+
+def test_kv_commit_host_validation(specv):
+    lib = specv.lib
+    v = ctypes.c_void_p(16)
+
+    def commit(**kw):
+        a = dict(k=v, vv=v, B=2, K=5, Hkv=8, D=128, Lmax=64, dtype=1)
+        a.update(kw)
+        return lib.specv_kv_commit(a["k"], a["vv"], v, v, v, a["B"], a["K"], a["Hkv"], a["D"], a["Lmax"],
+                                   a["dtype"], v, None)
+
+    assert commit(B=-1) == 1
+    assert commit(K=-1) == 1
+    assert commit(K=1024) == 1
+    assert commit(Hkv=0) == 1
+    assert commit(Lmax=5) == 1
+    assert commit(D=96) == 2
+    assert commit(dtype=3) == 2
+    assert commit(k=None) == 1
+    assert commit(vv=ctypes.c_void_p(24)) == 1          # misaligned
+    assert b"aligned" in lib.specv_last_error()
+    assert commit(B=0) == 0
