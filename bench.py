@@ -57,8 +57,8 @@ ATTN_TRAFFIC = {
                 "draft_verify_sampling_specv_amd/csrc/attn_common.h",
                 "draft_verify_sampling_specv_amd/csrc/common.h",
                 "draft_verify_sampling_specv_amd/csrc/kernels.h"],
-    "sha256": "755c3b7e2771eb228f5a9e2a237692025abe602eb958fc1da2bc02576cf0a7c3",
-    "fetch_kib": 132488.7, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131084.0, "write_scale": 1.0,
+    "sha256": "9f314491e3dfb12dab0756aa7c0e2620ffcfae75c7be27cf37e433879e779425",
+    "fetch_kib": 132471.3, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131084.0, "write_scale": 1.0,
 }
 
 
