@@ -45,6 +45,13 @@ lib.specv_accept_resample.argtypes = [
     ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
     ctypes.c_uint64, ctypes.c_uint64,
     _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+lib.specv_accept_resample_rule.restype = ctypes.c_int
+lib.specv_accept_resample_rule.argtypes = [
+    _vp, _vp, ctypes.c_int, _vp, _vp,
+    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int,
+    ctypes.c_uint64, ctypes.c_uint64,
+    _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+SIBLING_RULES = {"without_replacement": 0, "iid": 1, "deterministic": 2}
 
 lib.specv_kv_commit.restype = ctypes.c_int
 lib.specv_kv_commit.argtypes = [
@@ -183,8 +190,10 @@ class AcceptBuffers:
 
 
 def accept_resample(target_logits, draft_logits, tokens, parent, temperature, seed=0, offset=0,
-                    buffers=None, with_probs=True):
-    """Exact accept / reject / resample.  draft_logits may be None iff temperature == 0."""
+                    buffers=None, with_probs=True, siblings="without_replacement"):
+    """Exact accept / reject / resample.  `siblings` names how the siblings of a node were
+    drafted ("without_replacement", "iid" or "deterministic"); draft_logits may be None at
+    temperature 0 or for deterministic siblings."""
     target_logits = _dev(target_logits)
     if draft_logits is not None:
         draft_logits = _dev(draft_logits)
@@ -196,9 +205,11 @@ def accept_resample(target_logits, draft_logits, tokens, parent, temperature, se
         raise ValueError("tokens and parent must be [B][K+1]")
     bufs = buffers or AcceptBuffers.allocate(B, n1, V, target_logits.dtype, target_logits.device)
     r = bufs.result
-    _check("specv_accept_resample", lib.specv_accept_resample(
+    if siblings not in SIBLING_RULES:
+        raise ValueError(f"siblings must be one of {sorted(SIBLING_RULES)}")
+    _check("specv_accept_resample_rule", lib.specv_accept_resample_rule(
         _ptr(target_logits), _ptr(draft_logits), _dtype_code(target_logits), _ptr(tokens), _ptr(parent),
-        B, n1 - 1, V, float(temperature), int(seed), int(offset),
+        B, n1 - 1, V, float(temperature), SIBLING_RULES[siblings], int(seed), int(offset),
         _ptr(r.accept_len), _ptr(r.out_tokens), _ptr(r.out_nodes),
         _ptr(r.p_tok) if with_probs else None, _ptr(r.q_tok) if with_probs else None,
         _ptr(bufs.workspace), bufs.workspace.numel(), _stream()))

@@ -51,6 +51,11 @@ constexpr int kMaxVocab = 1 << 21;
 constexpr int kMaxTeam = 64;                // workgroups per sequence at most
 constexpr int kPassBatch = 4;               // tiles per batch of a range pass
 constexpr int kBufferWord3 = 0x00020000;    // raw buffer descriptor, word 3 (CDNA)
+// how the siblings of a node were drafted (the walk is the recursive rejection rule with the
+// proposal each sibling was drawn from)
+constexpr int kRuleWithoutReplacement = 0;  // drawn without replacement from q_v
+constexpr int kRuleIid = 1;                 // drawn independently from q_v
+constexpr int kRuleDeterministic = 2;       // fixed candidates (a point mass each)
 constexpr int kMaskNodes = 128;             // trees up to this size keep children bit masks
 constexpr int kMaskWords = kMaskNodes / 64;
 constexpr uint64_t kTimeoutTicks = 50000000ull;   // 0.5 s of the 100 MHz wall clock
@@ -178,6 +183,17 @@ __device__ __forceinline__ void get_words(uint64_t* p, int n, uint32_t tag, int*
     for (int i = 0; i < N; ++i) v[i] = static_cast<uint32_t>(raw[i]);
 }
 
+// Bit e set iff token base + e is in the exclusion list (tokens whose weight is 0 in a draw:
+// the rejected candidates under the deterministic sibling rule; the list is short).
+__device__ __forceinline__ uint32_t excluded_in(const int32_t* excl, int nexcl, int base) {
+    uint32_t m = 0;
+    for (int j = 0; j < nexcl; ++j) {
+        const uint32_t d = static_cast<uint32_t>(excl[j] - base);
+        m |= (d < 32u) ? (1u << d) : 0u;
+    }
+    return m;
+}
+
 // Streaming pass over tiles [t0, t1) of one row pair with the draw weights.  Tile i covers
 // kThreads * kVec consecutive elements; within a tile wave ww owns the contiguous segment of
 // 64 * kVec elements at (ww * 64) * kVec.  Segment sums go to seg[(i - t0) * kWaves + ww] if seg is
@@ -186,6 +202,7 @@ __device__ __forceinline__ void get_words(uint64_t* p, int n, uint32_t tag, int*
 template <typename T, bool kVecOK>
 __device__ double range_pass(const T* __restrict__ trow, const T* __restrict__ drow, int V, int t0,
                              int t1, float mt, float md, float k, float p_scale, float q_scale,
+                             const int32_t* excl, int nexcl,
                              float* seg, double* red, uint4 (&rt)[kPassBatch], uint4 (&rd)[kPassBatch]) {
     constexpr int kVec = Elem<T>::kVec;
     constexpr int kTile = kThreads * kVec;
@@ -226,9 +243,11 @@ __device__ double range_pass(const T* __restrict__ trow, const T* __restrict__ d
                     }
                 }
             }
+            const uint32_t xm = excluded_in(excl, nexcl, base);
             float sum = 0.f;
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) sum += draw_weight(zt[e], zd[e], mt, md, k, p_scale, q_scale);
+            for (int e = 0; e < kVec; ++e)
+                sum += ((xm >> e) & 1u) ? 0.f : draw_weight(zt[e], zd[e], mt, md, k, p_scale, q_scale);
             sum = wave_sum(sum);
             if (seg && lane == 0) seg[(i0 + j - t0) * kWaves + w] = sum;
             acc += sum;
@@ -271,7 +290,7 @@ template <typename T, bool kGreedy, bool kVecOK>
 __global__ void __launch_bounds__(kThreads)
 accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
               const int32_t* __restrict__ tokens, const int32_t* __restrict__ parent, int B, int n1,
-              int V, int nchunk, int P, float k, double invT, uint64_t seed, uint64_t offset,
+              int V, int nchunk, int P, int rule, float k, double invT, uint64_t seed, uint64_t offset,
               uint32_t tag, uint64_t* __restrict__ statw, uint64_t* __restrict__ partw,
               uint32_t* __restrict__ err, int32_t* __restrict__ accept_len,
               int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_nodes,
@@ -305,7 +324,7 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
     __shared__ int wcount[kWaves];
     __shared__ float pv[kWaves];
     __shared__ int pi[kWaves];
-    __shared__ int s_bad, s_ni, s_cmd, s_row, s_n, s_sel, s_found, s_to, s_next;
+    __shared__ int s_bad, s_ni, s_cmd, s_row, s_n, s_sel, s_found, s_to, s_next, s_nexcl;
     __shared__ float s_ps, s_qs;
     __shared__ double s_R, s_base;
 
@@ -382,7 +401,7 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
         if (!kGreedy && t > 0 && t < n1) {
             const int pa = par[t], x = tok[t];
             gzt = raw_bits(target[(seq + pa) * V + x]);
-            gzd = raw_bits(draft[(seq + pa) * V + x]);
+            if (rule != kRuleDeterministic) gzd = raw_bits(draft[(seq + pa) * V + x]);
         }
         // both uniforms of every node (Philox; computed while the gathers are in flight)
         if (!kGreedy) {
@@ -474,7 +493,7 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
             if (t == 0) s_ni = done;
             lds_barrier();
         }
-        const int ni = kGreedy ? 0 : s_ni;
+        const int ni = (kGreedy || rule == kRuleDeterministic) ? 0 : s_ni;     // draft rows read
 
         // -- C. chunk statistics: one wave per item.  Workgroup `rank` of the team owns items
         //    rank * kWaves + j + m * P * kWaves (j < kWaves); its waves take them in that order
@@ -602,7 +621,7 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                 for (int j = 0; j < kStage; ++j) {
                     const int i = t + j * kThreads;
                     const int wi = i & 3;
-                    need[j] = i < nw && (wi < 2 || (!kGreedy && info[r0 + i / rw] != 0));
+                    need[j] = i < nw && (wi < 2 || (!kGreedy && rule != kRuleDeterministic && info[r0 + i / rw] != 0));
                     raw[j] = need[j] ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
                 }
                 auto missing = [&]() {
@@ -649,7 +668,7 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                         }
                         if (ok && cl == 0) info[v] = (bi >= 0 && bi < V) ? bi : 0;
                     } else {
-                        const bool dr = ok && info[v] != 0;
+                        const bool dr = ok && rule != kRuleDeterministic && info[v] != 0;
                         float mt = -INFINITY, md = -INFINITY;
                         if (ok)
                             for (int c = cl; c < nchunk; c += g) {
@@ -692,15 +711,21 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                 if (v > 0) {
                     const int pa = par[v];
                     const float zt = (v == t) ? widen<T>(gzt) : Elem<T>::load(target + (seq + pa) * V, tok[v]);
-                    const float zd = (v == t) ? widen<T>(gzd) : Elem<T>::load(draft + (seq + pa) * V, tok[v]);
                     const double lp = (static_cast<double>(zt) - Mt[pa]) * invT;
-                    const double lq = (static_cast<double>(zd) - Md[pa]) * invT;
                     const double pd = exp(lp) / St[pa];
-                    const double qd = exp(lq) / Sd[pa];
-                    pq[v] = exp(lp - lq) * (Sd[pa] / St[pa]);
-                    qx[v] = static_cast<float>(qd);
                     pv_ = static_cast<float>(pd);
-                    qv_ = static_cast<float>(qd);
+                    if (rule == kRuleDeterministic) {
+                        // a point-mass proposal: the ratio is p(x) itself (over the unrejected mass)
+                        pq[v] = pd;
+                        qx[v] = 1.f;
+                    } else {
+                        const float zd = (v == t) ? widen<T>(gzd) : Elem<T>::load(draft + (seq + pa) * V, tok[v]);
+                        const double lq = (static_cast<double>(zd) - Md[pa]) * invT;
+                        const double qd = exp(lq) / Sd[pa];
+                        pq[v] = exp(lp - lq) * (Sd[pa] / St[pa]);
+                        qx[v] = static_cast<float>(qd);
+                        qv_ = static_cast<float>(qd);
+                    }
                 }
             }
             if (rank == 0) {
@@ -741,8 +766,15 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                         if (nxt < 0) { cmd = 1; break; }
                         const int c = nxt;
                         nxt = nsib[c];
-                        if (dup[c]) continue;
-                        const double ratio = fmax(0.0, pq[c] - cs) * Q / R;
+                        // a repeated token: skipped when siblings are distinct draws (its test
+                        // cannot pass and, without replacement or as a fixed candidate, changes
+                        // nothing); an independent draw is tested like any other
+                        if (dup[c] && rule != kRuleIid) continue;
+                        // deterministic siblings: cs holds the rejected candidates' p mass and
+                        // the target is p without them, renormalised
+                        const double ratio = (rule == kRuleDeterministic)
+                                                 ? (cs < 1.0 ? pq[c] / (1.0 - cs) : pq[c])
+                                                 : fmax(0.0, pq[c] - cs) * Q / R;
                         if (uacc[c] < ratio) {
                             if (lane == 0) path[n] = c;
                             ++n;
@@ -751,8 +783,12 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                             nxt = fch[v] < n1 ? fch[v] : -1;
                             continue;
                         }
+                        if (rule == kRuleDeterministic) {
+                            cs += pq[c];
+                            continue;       // no residual pass: the draw excludes the rejected tokens
+                        }
                         const double cn = cs + R / Q;
-                        Q -= static_cast<double>(qx[c]);
+                        if (rule == kRuleWithoutReplacement) Q -= static_cast<double>(qx[c]);
                         if (nxt >= 0) {
                             pending = true;
                             pend = cn;
@@ -772,7 +808,13 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                         s_n = n;
                         if (cmd == 1) {
                             s_ps = static_cast<float>(1.0 / St[v]);
-                            s_qs = (cs > 0.0) ? static_cast<float>(cs / Sd[v]) : 0.f;
+                            s_qs = (cs > 0.0 && rule != kRuleDeterministic) ? static_cast<float>(cs / Sd[v]) : 0.f;
+                            // deterministic siblings: the draw excludes every child's token (all
+                            // were rejected, or repeat a rejected one); the list reuses ilist
+                            int ne = 0;
+                            if (rule == kRuleDeterministic)
+                                for (int c = fch[v] < n1 ? fch[v] : -1; c >= 0; c = nsib[c]) ilist[ne++] = tok[c];
+                            s_nexcl = ne;
                         }
                     }
                 }
@@ -780,7 +822,7 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                 if (s_cmd != 0) break;
                 const int64_t rr = (seq + s_row) * V;
                 const double mine = range_pass<T, kVecOK>(target + rr, draft + rr, V, my_t0, my_t1, Mt[s_row],
-                                                          Md[s_row], k, s_ps, s_qs, nullptr, red, rt, rd);
+                                                          Md[s_row], k, s_ps, s_qs, ilist, 0, nullptr, red, rt, rd);
                 double Rn = mine;
                 if (P > 1) {
                     double before_unused;
@@ -818,8 +860,9 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
         const int64_t rr = (seq + e) * V;
         const float mt = Mt[e], ps = s_ps, qs = s_qs;
         const float md = (qs != 0.f) ? Md[e] : 0.f;
+        const int nexcl = s_nexcl;
         const double mine = range_pass<T, kVecOK>(target + rr, draft + rr, V, my_t0, my_t1, mt, md, k, ps, qs,
-                                                  seg, red, rt, rd);
+                                                  ilist, nexcl, seg, red, rt, rd);
         double before = 0.0, W = mine;
         if (P > 1)
             team_exchange(pw + static_cast<int64_t>(npass) * P, P, rank, static_cast<float>(mine), tag, s_vals,
@@ -914,10 +957,11 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                             if (qs != 0.f) zd[i] = Elem<T>::load(draft + rr, base + i);
                         }
                 }
+                const uint32_t xm = excluded_in(ilist, nexcl, base);
                 float ls = 0.f;
 #pragma unroll
                 for (int i = 0; i < kVec; ++i) {
-                    wt[i] = draw_weight(zt[i], zd[i], mt, md, k, ps, qs);
+                    wt[i] = ((xm >> i) & 1u) ? 0.f : draw_weight(zt[i], zd[i], mt, md, k, ps, qs);
                     ls += wt[i];
                 }
                 double incl2 = ls;
@@ -1027,8 +1071,9 @@ hipError_t launch_kernel(const AcceptArgs& a, hipStream_t stream) {
     int32_t* out_nodes = a.out_nodes;
     float* p_tok = a.p_tok;
     float* q_tok = a.q_tok;
+    int rule = a.rule;
     hipLaunchKernelGGL((accept_kernel<T, kGreedy, kVecOK>), dim3(grid), dim3(kThreads), 0, stream, target, draft,
-                       tokens, parent, B, n1, V, nchunk, P, k, invT, seed, offset, tag, statw, partw, err,
+                       tokens, parent, B, n1, V, nchunk, P, rule, k, invT, seed, offset, tag, statw, partw, err,
                        accept_len, out_tokens, out_nodes, p_tok, q_tok);
     return hipGetLastError();
 }

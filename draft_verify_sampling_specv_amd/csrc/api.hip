@@ -101,13 +101,13 @@ size_t specv_accept_workspace_bytes(int32_t B, int32_t K, int32_t V, specv_dtype
     return specv::accept_workspace_bytes(B, K + 1, V, logits_dtype == SPECV_BF16);
 }
 
-specv_status specv_accept_resample(const void* target_logits, const void* draft_logits,
-                                   specv_dtype logits_dtype, const int32_t* tokens,
-                                   const int32_t* parent, int32_t B, int32_t K, int32_t V,
-                                   float temperature, uint64_t seed, uint64_t offset,
-                                   int32_t* accept_len, int32_t* out_tokens, int32_t* out_nodes,
-                                   float* p_tok, float* q_tok, void* workspace,
-                                   size_t workspace_bytes, hipStream_t stream) {
+specv_status specv_accept_resample_rule(const void* target_logits, const void* draft_logits,
+                                        specv_dtype logits_dtype, const int32_t* tokens,
+                                        const int32_t* parent, int32_t B, int32_t K, int32_t V,
+                                        float temperature, specv_sibling_rule rule, uint64_t seed,
+                                        uint64_t offset, int32_t* accept_len, int32_t* out_tokens,
+                                        int32_t* out_nodes, float* p_tok, float* q_tok, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
     if (B < 0) return fail(SPECV_ERR_INVALID_ARG, "B = %d < 0", B);
     if (K < 0 || K + 1 > SPECV_MAX_NODES)
         return fail(SPECV_ERR_INVALID_ARG, "K = %d outside [0, %d]", K, SPECV_MAX_NODES - 1);
@@ -115,20 +115,39 @@ specv_status specv_accept_resample(const void* target_logits, const void* draft_
         return fail(SPECV_ERR_INVALID_ARG, "V = %d outside [1, %d]", V, SPECV_MAX_VOCAB);
     if (!std::isfinite(temperature) || temperature < 0.f)
         return fail(SPECV_ERR_INVALID_ARG, "temperature must be finite and >= 0");
+    if (rule != SPECV_SIBLINGS_WITHOUT_REPLACEMENT && rule != SPECV_SIBLINGS_IID &&
+        rule != SPECV_SIBLINGS_DETERMINISTIC)
+        return fail(SPECV_ERR_INVALID_ARG, "sibling rule %d not in {0, 1, 2}", static_cast<int>(rule));
     if (logits_dtype != SPECV_F32 && logits_dtype != SPECV_BF16)
         return fail(SPECV_ERR_UNSUPPORTED, "dtype %d not supported", static_cast<int>(logits_dtype));
     if (B == 0) return ok();
     if (!target_logits || !tokens || !parent || !accept_len || !out_tokens || !out_nodes)
         return fail(SPECV_ERR_INVALID_ARG, "NULL pointer argument");
-    if (temperature > 0.f && !draft_logits)
-        return fail(SPECV_ERR_INVALID_ARG, "draft_logits may be NULL only at temperature 0");
+    const bool need_draft = temperature > 0.f && rule != SPECV_SIBLINGS_DETERMINISTIC;
+    if (need_draft && !draft_logits)
+        return fail(SPECV_ERR_INVALID_ARG,
+                    "draft_logits may be NULL only at temperature 0 or for deterministic siblings");
     const size_t need = specv::accept_workspace_bytes(B, K + 1, V, logits_dtype == SPECV_BF16);
     if (!workspace || workspace_bytes < need)
         return fail(SPECV_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
-    specv::AcceptArgs a{target_logits, temperature > 0.f ? draft_logits : nullptr,
+    specv::AcceptArgs a{target_logits, need_draft ? draft_logits : nullptr,
                         logits_dtype == SPECV_BF16, tokens, parent, B, K + 1, V, temperature,
-                        seed, offset, accept_len, out_tokens, out_nodes, p_tok, q_tok, workspace};
+                        static_cast<int>(rule), seed, offset, accept_len, out_tokens, out_nodes, p_tok, q_tok,
+                        workspace};
     return hip_status(specv::launch_accept(a, stream), "accept_resample");
+}
+
+specv_status specv_accept_resample(const void* target_logits, const void* draft_logits,
+                                   specv_dtype logits_dtype, const int32_t* tokens,
+                                   const int32_t* parent, int32_t B, int32_t K, int32_t V,
+                                   float temperature, uint64_t seed, uint64_t offset,
+                                   int32_t* accept_len, int32_t* out_tokens, int32_t* out_nodes,
+                                   float* p_tok, float* q_tok, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+    return specv_accept_resample_rule(target_logits, draft_logits, logits_dtype, tokens, parent, B, K, V,
+                                      temperature, SPECV_SIBLINGS_WITHOUT_REPLACEMENT, seed, offset,
+                                      accept_len, out_tokens, out_nodes, p_tok, q_tok, workspace,
+                                      workspace_bytes, stream);
 }
 
 specv_status specv_kv_commit(void* k_cache, void* v_cache, const int32_t* ctx_len,

@@ -34,6 +34,7 @@ struct AcceptArgs {
     const int32_t* parent;
     int B, n1, V;
     float temperature;     // 0 -> greedy
+    int rule;              // how siblings were drafted: 0 without replacement, 1 i.i.d., 2 fixed candidates
     uint64_t seed, offset;
     int32_t* accept_len;
     int32_t* out_tokens;

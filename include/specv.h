@@ -202,6 +202,45 @@ specv_status specv_accept_resample(const void* target_logits, const void* draft_
 size_t specv_accept_workspace_bytes(int32_t B, int32_t K, int32_t V, specv_dtype logits_dtype);
 
 /*
+ * How the siblings of a tree node were drafted.  The accept rule stays the
+ * recursive rejection rule; what changes is the proposal each sibling is
+ * taken to be drawn from, and the rule is exact only for the drafting it
+ * names.  [PTD] Method 4, "Acceptance Logic" (sampling without replacement);
+ * [SD-EAGLE] "EAGLE: tree drafting and feature reuse" (K candidates per depth).
+ */
+typedef enum {
+    /* drawn without replacement from q_v (the rule of specv_accept_resample):
+       after a rejection the draft loses the rejected token, renormalised; a
+       repeated token is skipped */
+    SPECV_SIBLINGS_WITHOUT_REPLACEMENT = 0,
+    /* drawn independently from q_v: the proposal stays q_v, so after i
+       rejections the target is (p - c_i q)+ / R_i with c_{i+1} = c_i + R_i;
+       repeated tokens are tested (and rejected) like any other */
+    SPECV_SIBLINGS_IID = 1,
+    /* fixed candidates (e.g. the draft's top-k), each a point mass: accept x
+       with probability p'(x); after a rejection p' is p without the rejected
+       tokens, renormalised, and the final draw is from it; the draft logits
+       are not read (may be NULL) and q_tok is NaN */
+    SPECV_SIBLINGS_DETERMINISTIC = 2
+} specv_sibling_rule;
+
+/*
+ * specv_accept_resample with the sibling rule given explicitly; the other
+ * arguments, outputs and errors are those of specv_accept_resample, except
+ * that draft_logits may also be NULL for SPECV_SIBLINGS_DETERMINISTIC, and
+ * SPECV_ERR_INVALID_ARG is returned for a rule outside the enum.  At T == 0
+ * the rule does not matter (greedy).
+ */
+specv_status specv_accept_resample_rule(const void* target_logits, const void* draft_logits,
+                                        specv_dtype logits_dtype,
+                                        const int32_t* tokens, const int32_t* parent,
+                                        int32_t B, int32_t K, int32_t V, float temperature,
+                                        specv_sibling_rule rule, uint64_t seed, uint64_t offset,
+                                        int32_t* accept_len, int32_t* out_tokens, int32_t* out_nodes,
+                                        float* p_tok, float* q_tok,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * KV-cache commit after a verify step: keep the accepted path, drop the rest.
  *
  * [SD-review] §4 (limitations): the cache entries of rejected drafts have to

@@ -38,6 +38,20 @@ Readings where the pages are silent, ambiguous or garbled:
   * The acceptance test is the strict "<" of the pages; q'(x) == 0 counts as
     ratio +inf (accept); a residual of zero mass leaves p' unchanged.
 
+Other ways the siblings may have been drafted ([PTD] Method 4 names sampling
+without replacement; [SD-EAGLE] "EAGLE: tree drafting and feature reuse" has
+the draft output K candidates per depth).  The walk is the same recursive
+rejection rule with the proposal each sibling was actually drawn from:
+  * "iid": siblings drawn independently from q_v (with replacement): the
+    proposal stays q_v, so q' is not renormalised and a repeated token is
+    tested like any other (after its first rejection p'(x) = 0, so it is
+    rejected again, and the residual update still applies);
+  * "deterministic": siblings are fixed candidates (for example the draft's
+    top-k), i.e. each is proposed by a point mass at its token: accept x with
+    probability p'(x); after a rejection p' <- (p' - delta_x)+ normalised, that
+    is p' without x, renormalised; a repeated token has p'(x) = 0 and changes
+    nothing, so it is skipped.  The draft logits are not used.
+
 Decision margins: every uniform-driven decision records how far the uniform
 was from flipping it (|u - ratio| for a ratio test; the distance of u * W from
 the nearer boundary of the chosen token's CDF interval, divided by W, for a
@@ -133,8 +147,11 @@ def children_of(parent):
     return kids
 
 
-def tree_accept(zt, zd, tokens, parent, T, u_acc, u_res, trace=None):
-    """The tree walk for one sequence.
+SIBLING_RULES = ("without_replacement", "iid", "deterministic")
+
+
+def tree_accept(zt, zd, tokens, parent, T, u_acc, u_res, trace=None, siblings="without_replacement"):
+    """The tree walk for one sequence, for siblings drafted as `siblings` says.
 
     Returns (accept_len, out_nodes, out_tokens, margin).  out_nodes lists the
     accepted nodes from the first level down; out_tokens their tokens followed
@@ -161,14 +178,18 @@ def tree_accept(zt, zd, tokens, parent, T, u_acc, u_res, trace=None):
                 trace.append(("greedy", v, y))
             return len(out_nodes), out_nodes, out_tokens, margin
         p = softmax_T(zt[v], T)
-        q = softmax_T(zd[v], T) if kids[v] else None
+        q = softmax_T(zd[v], T) if kids[v] and siblings != "deterministic" else None
         tried = set()
         accepted = None
         for c in kids[v]:
             x = int(tokens[c])
-            if x in tried:
-                continue
-            tried.add(x)
+            if siblings != "iid":
+                if x in tried:
+                    continue
+                tried.add(x)
+            if siblings == "deterministic":
+                q = np.zeros_like(p)
+                q[x] = 1.0
             ratio = _ratio(p, q, x)
             margin = min(margin, abs(u_acc[c] - ratio))
             ok = u_acc[c] < ratio
@@ -181,11 +202,12 @@ def tree_accept(zt, zd, tokens, parent, T, u_acc, u_res, trace=None):
             mass = residual.sum()
             if mass > 0.0:
                 p = residual / mass
-            qx = q[x]
-            q = q.copy()
-            q[x] = 0.0
-            if qx < 1.0:
-                q = q / (1.0 - qx)
+            if siblings == "without_replacement":
+                qx = q[x]
+                q = q.copy()
+                q[x] = 0.0
+                if qx < 1.0:
+                    q = q / (1.0 - qx)
         if accepted is not None:
             out_nodes.append(accepted)
             out_tokens.append(int(tokens[accepted]))
@@ -199,8 +221,9 @@ def tree_accept(zt, zd, tokens, parent, T, u_acc, u_res, trace=None):
         return len(out_nodes), out_nodes, out_tokens, margin
 
 
-def node_probs(zt, zd, tokens, parent, T):
-    """p_tok[v] = p_parent(v)(tokens[v]) and q_tok[v] likewise; NaN at v = 0 or T = 0."""
+def node_probs(zt, zd, tokens, parent, T, siblings="without_replacement"):
+    """p_tok[v] = p_parent(v)(tokens[v]) and q_tok[v] likewise; NaN at v = 0 or T = 0, and q_tok
+    NaN for deterministic siblings (no draft law)."""
     n1 = len(parent)
     p_tok = np.full(n1, np.nan)
     q_tok = np.full(n1, np.nan)
@@ -211,14 +234,16 @@ def node_probs(zt, zd, tokens, parent, T):
         if not kids[v]:
             continue
         p = softmax_T(zt[v], T)
-        q = softmax_T(zd[v], T)
+        q = softmax_T(zd[v], T) if siblings != "deterministic" else None
         for c in kids[v]:
             p_tok[c] = p[int(tokens[c])]
-            q_tok[c] = q[int(tokens[c])]
+            if q is not None:
+                q_tok[c] = q[int(tokens[c])]
     return p_tok, q_tok
 
 
-def accept_batch(target_logits, draft_logits, tokens, parent, T, u_acc, u_res, with_probs=True):
+def accept_batch(target_logits, draft_logits, tokens, parent, T, u_acc, u_res, with_probs=True,
+                 siblings="without_replacement"):
     """Batch driver: one tree walk per sequence.
 
     target_logits[B][N1][V], draft_logits[B][N1][V] (or None when T == 0),
@@ -245,12 +270,12 @@ def accept_batch(target_logits, draft_logits, tokens, parent, T, u_acc, u_res, w
             continue
         zt = target_logits[b]
         zd = draft_logits[b] if draft_logits is not None else None
-        n, nodes, toks, m = tree_accept(zt, zd, tokens[b], parent[b], T, u_acc[b], u_res[b])
+        n, nodes, toks, m = tree_accept(zt, zd, tokens[b], parent[b], T, u_acc[b], u_res[b], siblings=siblings)
         accept_len[b] = n
         out_nodes[b, :len(nodes)] = nodes
         out_tokens[b, :len(toks)] = toks
         margin[b] = m
         if with_probs:
-            p_tok[b], q_tok[b] = node_probs(zt, zd, tokens[b], parent[b], T)
+            p_tok[b], q_tok[b] = node_probs(zt, zd, tokens[b], parent[b], T, siblings)
     return dict(accept_len=accept_len, out_tokens=out_tokens, out_nodes=out_nodes,
                 p_tok=p_tok, q_tok=q_tok, margin=margin)

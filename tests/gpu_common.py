@@ -30,7 +30,7 @@ def logits_dtype(w):
     return torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
 
-def run_accept_gpu(w, seed=None, offset=None, draft=True):
+def run_accept_gpu(w, seed=None, offset=None, draft=True, siblings="without_replacement"):
     import draft_verify_sampling_specv_amd as specv
     dt = logits_dtype(w)
     tl = dev(w.target_logits, dt)
@@ -38,12 +38,12 @@ def run_accept_gpu(w, seed=None, offset=None, draft=True):
     tok = torch.from_numpy(np.ascontiguousarray(w.tokens, dtype=np.int32)).cuda()
     par = torch.from_numpy(np.ascontiguousarray(w.parent, dtype=np.int32)).cuda()
     r = specv.accept_resample(tl, dl, tok, par, w.T, w.seed if seed is None else seed,
-                              w.offset if offset is None else offset)
+                              w.offset if offset is None else offset, siblings=siblings)
     torch.cuda.synchronize()
     return {k: getattr(r, k).cpu().numpy() for k in ("accept_len", "out_tokens", "out_nodes", "p_tok", "q_tok")}
 
 
-def run_accept_oracle(w, seqs=None, seed=None, offset=None, with_probs=True):
+def run_accept_oracle(w, seqs=None, seed=None, offset=None, with_probs=True, siblings="without_replacement"):
     seed = w.seed if seed is None else seed
     offset = w.offset if offset is None else offset
     seqs = range(w.B) if seqs is None else seqs
@@ -55,7 +55,8 @@ def run_accept_oracle(w, seqs=None, seed=None, offset=None, with_probs=True):
         ur.append(list(r_b))
     tl = np.asarray(w.target_logits[seqs], dtype=np.float64)
     dl = np.asarray(w.draft_logits[seqs], dtype=np.float64) if w.T > 0 else None
-    return o_accept.accept_batch(tl, dl, w.tokens[seqs], w.parent[seqs], w.T, ua, ur, with_probs=with_probs)
+    return o_accept.accept_batch(tl, dl, w.tokens[seqs], w.parent[seqs], w.T, ua, ur, with_probs=with_probs,
+                                 siblings=siblings)
 
 
 def compare_accept(gpu, ora, seqs=None, check_probs=True, name=""):

@@ -271,3 +271,36 @@ def test_attn_invalid_context_length_gives_nan():
     out, lse = _attn_gpu(a)
     assert np.isnan(out[1]).all() and np.isnan(out[2]).all() and np.isnan(lse[1:]).all()
     assert np.isfinite(out[0]).all()
+
+
+# ----------------------------------------------------------------------------- sibling rules
+
+@pytest.mark.parametrize("siblings", ["iid", "deterministic"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_accept_sibling_rules_random_shapes(siblings, dtype):
+    # siblings drafted the way the rule says (independent draws, or the draft's top tokens); the
+    # deterministic rule runs without draft logits
+    rng = np.random.default_rng(31 if dtype == "f32" else 32)
+    for case in range(16):
+        n1 = int(rng.choice([2, 3, 6, 9, 17, 33, 65, 130]))
+        V = int(rng.choice([3, 7, 64, 333, 1000, 4097, 8193, 20000]))
+        T = float(rng.choice([0.5, 1.0, 2.0]))
+        B = int(rng.integers(1, 9))
+        w = workloads.random_case(int(rng.integers(1 << 30)), B, n1, V, T, dtype=dtype, max_children=min(4, V),
+                                  siblings=siblings)
+        w.seed, w.offset = int(rng.integers(1 << 62)), int(rng.integers(1 << 40))
+        log(f"accept ({siblings}): random case {case}: B={B} N1={n1} V={V} T={T} {dtype}")
+        gpu = run_accept_gpu(w, draft=(siblings != "deterministic"), siblings=siblings)
+        compare_accept(gpu, run_accept_oracle(w, siblings=siblings), name=f"{siblings}{case}")
+
+
+@pytest.mark.parametrize("siblings", ["iid", "deterministic"])
+def test_accept_sibling_rules_eagle_shape(siblings):
+    # the EAGLE-style tree shape and vocabulary (B=16, 60 drafts, V=128256 bf16, T=0.7), its tokens
+    # redrawn the way the rule says
+    w0 = workloads.eagle_config()
+    w = workloads.make_accept("eagle-" + siblings, w0.parent, w0.V, w0.T, "bf16", 3.0, workloads.SIGMA_EAGLE, 3100,
+                              siblings=siblings)
+    log(f"accept ({siblings}): eagle-shaped trees B=16 N=60 V=128256 bf16 T=0.7")
+    gpu = run_accept_gpu(w, draft=(siblings != "deterministic"), siblings=siblings)
+    compare_accept(gpu, run_accept_oracle(w, siblings=siblings), name=f"eagle-{siblings}")

@@ -141,3 +141,20 @@ def test_kv_commit_host_validation(specv):
     assert commit(vv=ctypes.c_void_p(24)) == 1          # misaligned
     assert b"aligned" in lib.specv_last_error()
     assert commit(B=0) == 0
+
+
+def test_accept_rule_host_validation(specv):
+    lib = specv.lib
+    v = ctypes.c_void_p(16)
+
+    def call(rule, draft=v, T=1.0):
+        return lib.specv_accept_resample_rule(v, draft, 1, v, v, 2, 3, 100, T, rule, 0, 0, v, v, v, None, None,
+                                              v, 1 << 30, None)
+
+    assert call(3) == 1
+    assert call(-1) == 1
+    assert b"rule" in lib.specv_last_error()
+    assert call(0, draft=None) == 1          # draft needed without replacement at T > 0
+    assert call(1, draft=None) == 1          # and for i.i.d. siblings
+    assert lib.specv_accept_resample_rule(v, None, 1, v, v, 0, 3, 100, 1.0, 2, 0, 0, v, v, v, None, None,
+                                          v, 1 << 30, None) == 0      # B == 0: no launch

@@ -149,10 +149,48 @@ def walk_law(walk, parent, tokens, zt, zd, T):
     return law
 
 
-def full_law(parent, model, T, walk=None):
+def enumerate_iid_draws(parent, model, T):
+    """All draft token assignments with siblings drawn independently (with replacement) from the
+    draft law of their parent's prefix, with their probabilities."""
+    n1 = len(parent)
+    kids = accept.children_of(parent)
+    internal = [v for v in range(n1) if kids[v]]
+    tokens = np.zeros(n1, dtype=np.int64)
+
+    def rec(idx, prob):
+        if idx == len(internal):
+            yield tokens.copy(), prob
+            return
+        v = internal[idx]
+        q = softmax(model.get(path_prefix(parent, tokens, v))[1] / T)
+        for tup in itertools.product(range(model.V), repeat=len(kids[v])):
+            for c, x in zip(kids[v], tup):
+                tokens[c] = x
+            yield from rec(idx + 1, prob * float(np.prod([q[x] for x in tup])))
+
+    yield from rec(0, 1.0)
+
+
+def fixed_candidates(order):
+    """Deterministic drafting: the children of a node get the first tokens of `order(zt, zd)`
+    (distinct), a function of the prefix only; one assignment, probability 1."""
+    def draws(parent, model, T):
+        n1 = len(parent)
+        kids = accept.children_of(parent)
+        tokens = np.zeros(n1, dtype=np.int64)
+        for v in range(n1):                      # parents come before children
+            if kids[v]:
+                zt, zd = model.get(path_prefix(parent, tokens, v))
+                for c, x in zip(kids[v], order(zt, zd)):
+                    tokens[c] = int(x)
+        yield tokens, 1.0
+    return draws
+
+
+def full_law(parent, model, T, walk=None, draws=enumerate_draws):
     walk = walk or accept.tree_accept
     law = {}
-    for tokens, p_draw in enumerate_draws(parent, model, T):
+    for tokens, p_draw in draws(parent, model, T):
         zt = np.stack([model.get(path_prefix(parent, tokens, v))[0] for v in range(len(parent))])
         zd = np.stack([model.get(path_prefix(parent, tokens, v))[1] for v in range(len(parent))])
         for seq, pr in walk_law(walk, parent, tokens, zt, zd, T).items():
@@ -195,6 +233,57 @@ def test_exact_law_tree(parent, V, T, seed):
     assert law_error(full_law(parent, model, T), model, T) < 1e-12
 
 
+def _rule(name):
+    return lambda *a, **kw: accept.tree_accept(*a, siblings=name, **kw)
+
+
+# (vocabularies of 5-6: with fewer tokens the residual after one rejection is often a point mass,
+# which makes several different rules agree)
+SIBLING_TREES = [
+    (workloads.TREE6, 4, 1.0, 21),
+    (np.array([-1, 0, 0, 0]), 6, 0.8, 22),               # three siblings at the root
+    (np.array([-1, 0, 0, 0, 0]), 5, 1.3, 23),            # four siblings
+    (np.array([-1, 0, 0, 1]), 5, 1.0, 24),               # a fork, then one more level
+]
+
+
+@pytest.mark.parametrize("parent,V,T,seed", SIBLING_TREES)
+def test_exact_law_iid_siblings(parent, V, T, seed):
+    # siblings drawn independently from q (repeated tokens included): the walk with the
+    # unrenormalised proposal keeps the target law
+    model = PrefixModel(V, seed, T=T)
+    assert law_error(full_law(parent, model, T, walk=_rule("iid"), draws=enumerate_iid_draws), model, T) < 1e-12
+    # the without-replacement walk is exact for i.i.d. draws too: skipping a repeated token makes
+    # the next test one whose proposal, given that its token is new, is q without the rejected ones
+    assert law_error(full_law(parent, model, T, draws=enumerate_iid_draws), model, T) < 1e-12
+
+
+@pytest.mark.parametrize("order", ["draft_top", "target_bottom"])
+@pytest.mark.parametrize("parent,V,T,seed", SIBLING_TREES)
+def test_exact_law_deterministic_siblings(parent, V, T, seed, order):
+    # fixed candidates -- the draft's top tokens, or the target's least likely ones: either way
+    # the emitted sequence follows the target law
+    pick = {"draft_top": lambda zt, zd: np.argsort(-zd, kind="stable"),
+            "target_bottom": lambda zt, zd: np.argsort(zt, kind="stable")}[order]
+    model = PrefixModel(V + 1, seed, T=T)
+    law = full_law(parent, model, T, walk=_rule("deterministic"), draws=fixed_candidates(pick))
+    assert law_error(law, model, T) < 1e-12
+
+
+def test_sibling_rules_are_not_interchangeable():
+    # each rule is exact only for the drafting it describes
+    model = PrefixModel(6, 25, T=1.0)
+    tree = np.array([-1, 0, 0, 0])
+    top = fixed_candidates(lambda zt, zd: np.argsort(-zd, kind="stable"))
+    wrong = [
+        (_rule("iid"), enumerate_draws),                  # without-replacement draws, proposal kept as q
+        (accept.tree_accept, top),                        # fixed candidates treated as draws from q
+        (_rule("iid"), top),
+    ]
+    for walk, draws in wrong:
+        assert law_error(full_law(tree, model, 1.0, walk=walk, draws=draws), model, 1.0) > 1e-4
+
+
 # ----------------------------------------------------------------------------- mutation tests
 
 def _mutant(old, new):
@@ -213,7 +302,8 @@ def _mutant(old, new):
     # target row of the wrong node (off by one along the path)
     ("p = softmax_T(zt[v], T)", "p = softmax_T(zt[max(v - 1, 0)], T)"),
     # temperature dropped on the draft side
-    ("q = softmax_T(zd[v], T) if kids[v] else None", "q = softmax_T(zd[v], 1.0) if kids[v] else None"),
+    ('q = softmax_T(zd[v], T) if kids[v] and siblings != "deterministic" else None',
+     'q = softmax_T(zd[v], 1.0) if kids[v] and siblings != "deterministic" else None'),
     # residual taken against the original p instead of the running p'
     ("residual = np.maximum(p - q, 0.0)", "residual = np.maximum(softmax_T(zt[v], T) - q, 0.0)"),
 ])
@@ -221,6 +311,26 @@ def test_exact_law_catches_planted_mistakes(old, new):
     walk = _mutant(old, new)
     model = PrefixModel(4, 6, T=0.8)
     assert law_error(full_law(workloads.TREE6, model, 0.8, walk=walk), model, 0.8) > 1e-4
+
+
+def test_iid_rule_catches_skipping_repeated_tokens():
+    walk = _mutant('if siblings != "iid":', "if True:")
+    model = PrefixModel(6, 26, T=1.0)
+    law = full_law(np.array([-1, 0, 0, 0]), model, 1.0, walk=lambda *a, **kw: walk(*a, siblings="iid", **kw),
+                   draws=enumerate_iid_draws)
+    assert law_error(law, model, 1.0) > 1e-4
+
+
+def test_deterministic_rule_catches_a_residual_against_the_draft_law():
+    # the deterministic walk must subtract the point mass, not the draft's softmax
+    walk = _mutant("""            if siblings == "deterministic":
+                q = np.zeros_like(p)
+                q[x] = 1.0""", """            if siblings == "deterministic":
+                q = softmax_T(zd[v], T)""")
+    model = PrefixModel(6, 27, T=1.0)
+    law = full_law(np.array([-1, 0, 0, 0]), model, 1.0, walk=lambda *a, **kw: walk(*a, siblings="deterministic", **kw),
+                   draws=fixed_candidates(lambda zt, zd: np.argsort(-zd, kind="stable")))
+    assert law_error(law, model, 1.0) > 1e-4
 
 
 # ----------------------------------------------------------------------------- E[tokens]

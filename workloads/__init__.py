@@ -165,15 +165,27 @@ def draw_children_tokens(rng, draft_row, T, k):
     return top[np.argsort(-keys[top], kind="stable")].astype(np.int32)
 
 
-def draw_tree_tokens(rng, parent, draft_logits_b, T, V):
+def draw_iid_tokens(rng, draft_row, T, k):
+    """k tokens drawn independently (with replacement) from softmax(draft_row / T), each by
+    Gumbel-max."""
+    z = np.asarray(draft_row, dtype=np.float64) / T
+    return np.array([int(np.argmax(z + gumbel(rng, z.shape))) for _ in range(k)], dtype=np.int32)
+
+
+def draw_tree_tokens(rng, parent, draft_logits_b, T, V, siblings="without_replacement"):
     """Tokens for every node: the root token is uniform in [0, V); the children
-    of v are drawn without replacement from draft row v."""
+    of v are drawn from draft row v -- without replacement (Gumbel-top-k),
+    independently ("iid"), or as the row's top tokens ("deterministic")."""
     kids = children_lists(parent)
     tok = np.zeros(len(parent), dtype=np.int32)
     tok[0] = rng.integers(V)
     for v, ks in enumerate(kids):
         if ks:
-            tok[ks] = draw_children_tokens(rng, draft_logits_b[v], T, len(ks))
+            if siblings == "iid" and T > 0:
+                tok[ks] = draw_iid_tokens(rng, draft_logits_b[v], T, len(ks))
+            else:
+                tok[ks] = draw_children_tokens(rng, draft_logits_b[v], 0 if siblings == "deterministic" else T,
+                                               len(ks))
     return tok
 
 
@@ -184,7 +196,7 @@ def draft_from_target(rng, target, sigma):
 
 
 def make_accept(name, parent, V, T, dtype, target_std, draft_sigma, seed_base,
-                independent_draft=False, tokens_T=None, greedy_tokens=False):
+                independent_draft=False, tokens_T=None, greedy_tokens=False, siblings="without_replacement"):
     """Generic generator: per-node target rows ~ N(0, target_std), draft rows =
     target + N(0, draft_sigma) (or an independent N(0, target_std)), draft
     tokens drawn from the draft rows along the given parent arrays."""
@@ -199,7 +211,7 @@ def make_accept(name, parent, V, T, dtype, target_std, draft_sigma, seed_base,
     target = as_dtype(target, dtype)
     draft = as_dtype(draft, dtype)
     tT = T if tokens_T is None else tokens_T
-    tokens = np.stack([draw_tree_tokens(r_tok, parent[b], draft[b], 0 if greedy_tokens else tT, V)
+    tokens = np.stack([draw_tree_tokens(r_tok, parent[b], draft[b], 0 if greedy_tokens else tT, V, siblings)
                        for b in range(B)])
     return AcceptInputs(name, target, draft, tokens, np.ascontiguousarray(parent, dtype=np.int32),
                         float(T), dtype, seed=seed_base, offset=0)
@@ -368,10 +380,10 @@ def ptd_attention(parent, seed_base=5001):
 
 
 def random_case(seed, B, n1, V, T, dtype="f32", max_children=3, max_depth=None,
-                target_std=2.0, draft_sigma=0.7):
+                target_std=2.0, draft_sigma=0.7, siblings="without_replacement"):
     """Small random tree case for parity sweeps."""
     rng = np.random.default_rng(seed)
     md = n1 if max_depth is None else max_depth
     parent = np.stack([random_tree(rng, n1 - 1, max_children, md) for _ in range(B)])
     return make_accept(f"random-{seed}", parent, V, T, dtype, target_std, draft_sigma, seed + 7,
-                       greedy_tokens=(T == 0))
+                       greedy_tokens=(T == 0), siblings=siblings)
