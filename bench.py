@@ -351,6 +351,14 @@ def measure_config(name, args, torch, specv, workloads):
                     steps)
     ms_acc = timed(lambda i: specv.accept_resample(*sets_acc[i % len(sets_acc)], w.T, seed=1, offset=i,
                                                    buffers=cbuf), steps)
+    # the accept rule for the other sibling draftings, same inputs (the time does not depend on how
+    # the tokens were drafted beyond the walk's path; fixed candidates read no draft rows)
+    ms_acc_rule = {}
+    if n1 > 2 and w.T > 0:
+        for rule in ("iid", "deterministic"):
+            ms_acc_rule[rule] = timed(lambda i: specv.accept_resample(
+                sets_acc[i % len(sets_acc)][0], None if rule == "deterministic" else sets_acc[i % len(sets_acc)][1],
+                *sets_acc[i % len(sets_acc)][2:], w.T, seed=1, offset=i, buffers=cbuf, siblings=rule), steps)
     r = specv.accept_resample(tl, dl, tok, par, w.T, seed=1, offset=0, buffers=cbuf)
     accept_len = r.accept_len.cpu().numpy()
     out_nodes = r.out_nodes.cpu().numpy()
@@ -385,6 +393,10 @@ def measure_config(name, args, torch, specv, workloads):
                       "arith_intensity": att_f / att_b},
         "accept": {"bytes": acc_b, "GBps": acc_b / (ms_acc * 1e-3) / 1e9,
                    "hbm_frac": acc_b / (ms_acc * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "accept_other_sibling_rules": {rule: {"ms": ms, "bytes": (B * n1 + (internal if rule == "iid" else 0)) * V * elem,
+                                              "hbm_frac": (B * n1 + (internal if rule == "iid" else 0)) * V * elem
+                                              / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                                       for rule, ms in ms_acc_rule.items()},
         "kv_commit": {"ms": ms_commit, "rows_moved": moved,
                       "bytes": moved * 2 * 2 * a.k_cache.shape[1] * a.q.shape[3] * (2 if a.dtype == "bf16" else 4)},
         "positions_per_s_accept_only": positions / (ms_acc * 1e-3),

@@ -23,8 +23,12 @@ Modules
              Attention Verification"; [PTD] Method 4, "Verification").
   accept     temperature softmax, the chain accept/reject/resample rule
              ([SD-review] §2; [SD-EAGLE] "The Exactness Rule" and "Build
-             it"), the tree rule ([PTD] Method 4, "Acceptance Logic") and
-             the greedy rule ([SD-EAGLE] "The Exactness Rule", greedy case).
+             it"), the tree rule ([PTD] Method 4, "Acceptance Logic") for
+             siblings drawn without replacement, i.i.d., or as fixed
+             candidates, and the greedy rule ([SD-EAGLE] "The Exactness
+             Rule", greedy case).
+  kv_commit  the KV-cache commit after a verify step ([SD-review] §4;
+             [SD-EAGLE] "Tree Attention Verification").
 
 Pins (tests marked "not gpu" check each function against something other than
 itself): Philox known-answer vectors and numpy's independent Philox; the
@@ -33,6 +37,7 @@ torch's causal scaled-dot-product attention; tree attention == causal attention
 over each root-to-node path; the exact output law of the accept rule (== p, to
 1e-12, by enumeration of draws and decision branches); the closed form
 E[tokens] = (1 - a^(K+1)) / (1 - a); empirical TV / chi-square tests; the
-greedy rule; inverse CDF == numpy.searchsorted.  No function here is
-"parity unpinned".
+greedy rule; inverse CDF == numpy.searchsorted; attention over the committed
+cache prefix == the tree-masked verify rows.  No function here is "parity
+unpinned".
 """
