@@ -5,7 +5,11 @@
 // is accepted draw a bonus token from p of the last node; greedy at T = 0.  [PTD] Method 4,
 // "Acceptance Logic": on a tree the children of a node are tested in index order as draws without
 // replacement from q; after i rejections the target is (p - c_i q)+ / R_i with c_0 = 0,
-// R_0 = Q_0 = 1, c_{i+1} = c_i + R_i / Q_i (Q: draft mass not yet rejected).
+// R_0 = Q_0 = 1, c_{i+1} = c_i + R_i / Q_i (Q: draft mass not yet rejected).  Other sibling
+// draftings take the same rule with their own proposal: i.i.d. draws keep q (Q stays 1, repeated
+// tokens are tested); fixed candidates ([SD-EAGLE] "EAGLE: tree drafting and feature reuse",
+// K candidates per depth) are point masses: x is accepted with probability p'(x) and dropped
+// from p' when rejected, and the final draw excludes the rejected candidates.
 //
 // One launch whose grid never exceeds the number of workgroups the device holds at once (one per
 // CU here: the LDS tables need about 100 KB), so on a device running this kernel alone every
