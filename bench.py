@@ -351,6 +351,29 @@ def measure_config(name, args, torch, specv, workloads):
                     steps)
     ms_acc = timed(lambda i: specv.accept_resample(*sets_acc[i % len(sets_acc)], w.T, seed=1, offset=i,
                                                    buffers=cbuf), steps)
+    # one level of draft-tree construction at this configuration's vocabulary: 16 frontier rows
+    # per sequence, k = 3 (EAGLE) or 4 (the PTD width cap), 16 kept; rotated sets of resident rows
+    expand_info = None
+    elem = 2 if w.dtype == "bf16" else 4
+    if name in ("eagle", "ptd"):
+        kx, FX = (3 if name == "eagle" else 4), 16
+        row_bytes = B * FX * V * elem
+        nsets = max(1, min(8, int((512 << 20) // row_bytes) + 1))
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(11)
+        xsets = [(torch.randn((B, FX, V), generator=gen, device="cuda") * 3.0).to(ldt) for _ in range(nsets)]
+        xtree = specv.DraftTree.with_roots(torch.zeros(B, dtype=torch.int32, device="cuda"), 1024)
+        xtree.n_nodes.fill_(1 + FX)
+        xfront = torch.arange(1, FX + 1, dtype=torch.int32, device="cuda").repeat(B, 1).contiguous()
+        xout = torch.empty((B, FX), dtype=torch.int32, device="cuda")
+        xws = torch.empty((specv.tree_expand_workspace_bytes(B, FX),), dtype=torch.uint8, device="cuda")
+        ms_x = timed(lambda i: specv.tree_expand(xsets[i % nsets], xfront, xtree, kx, w.T, FX, new_frontier=xout,
+                                                 workspace=xws), steps)
+        expand_info = {"ms": ms_x, "frontier_rows": B * FX, "k": kx, "bytes": row_bytes,
+                       "GBps": row_bytes / (ms_x * 1e-3) / 1e9,
+                       "hbm_frac": row_bytes / (ms_x * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del xsets
+
     # the accept rule for the other sibling draftings, same inputs (the time does not depend on how
     # the tokens were drafted beyond the walk's path; fixed candidates read no draft rows)
     ms_acc_rule = {}
@@ -397,6 +420,7 @@ def measure_config(name, args, torch, specv, workloads):
                                               "hbm_frac": (B * n1 + (internal if rule == "iid" else 0)) * V * elem
                                               / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
                                        for rule, ms in ms_acc_rule.items()},
+        "tree_expand": expand_info,
         "kv_commit": {"ms": ms_commit, "rows_moved": moved,
                       "bytes": moved * 2 * 2 * a.k_cache.shape[1] * a.q.shape[3] * (2 if a.dtype == "bf16" else 4)},
         "positions_per_s_accept_only": positions / (ms_acc * 1e-3),

@@ -9,6 +9,7 @@ library has not been built this import fails.
   tree_attn_verify(q, k_cache, v_cache, ctx_len, mask)     -> out, lse
   accept_resample(target, draft, tokens, parent, T, seed, offset) -> AcceptResult
   kv_commit(k_cache, v_cache, ctx_len, accept_len, out_nodes)     -> new_ctx_len
+  tree_expand(draft_logits, frontier, tree, k, T, keep)           -> new_frontier (tree updated)
 """
 
 from ._lib import (  # noqa: F401
@@ -22,6 +23,9 @@ from ._lib import (  # noqa: F401
     tree_attn_verify,
     accept_resample,
     kv_commit,
+    DraftTree,
+    tree_expand,
+    tree_expand_workspace_bytes,
     accept_workspace_bytes,
     attn_workspace_bytes,
 )

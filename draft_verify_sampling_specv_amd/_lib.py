@@ -53,6 +53,13 @@ lib.specv_accept_resample_rule.argtypes = [
     _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 SIBLING_RULES = {"without_replacement": 0, "iid": 1, "deterministic": 2}
 
+lib.specv_tree_expand_workspace_bytes.restype = ctypes.c_size_t
+lib.specv_tree_expand_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
+lib.specv_tree_expand.restype = ctypes.c_int
+lib.specv_tree_expand.argtypes = [
+    _vp, ctypes.c_int, _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+    ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+
 lib.specv_kv_commit.restype = ctypes.c_int
 lib.specv_kv_commit.argtypes = [
     _vp, _vp, _vp, _vp, _vp,
@@ -236,3 +243,53 @@ def kv_commit(k_cache, v_cache, ctx_len, accept_len, out_nodes, out=None):
         _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), _ptr(accept_len), _ptr(out_nodes),
         B, n1 - 1, Hkv, D, Lmax, _dtype_code(k_cache), _ptr(new_ctx), _stream()))
     return new_ctx
+
+
+# ----------------------------------------------------------------------------- tree expansion
+
+@dataclass
+class DraftTree:
+    parent: torch.Tensor         # [B][nmax] int32
+    tokens: torch.Tensor         # [B][nmax] int32
+    score: torch.Tensor          # [B][nmax] float64, cumulative draft log-probability
+    n_nodes: torch.Tensor        # [B] int32
+
+    @staticmethod
+    def with_roots(root_tokens, nmax):
+        """A tree per sequence holding only its root (node 0, score 0)."""
+        root_tokens = _dev(root_tokens, torch.int32)
+        B = root_tokens.shape[0]
+        dev = root_tokens.device
+        parent = torch.full((B, nmax), -1, dtype=torch.int32, device=dev)
+        tokens = torch.full((B, nmax), -1, dtype=torch.int32, device=dev)
+        tokens[:, 0] = root_tokens
+        return DraftTree(parent, tokens, torch.zeros((B, nmax), dtype=torch.float64, device=dev),
+                         torch.ones((B,), dtype=torch.int32, device=dev))
+
+
+def tree_expand_workspace_bytes(B, F):
+    return int(lib.specv_tree_expand_workspace_bytes(B, F))
+
+
+def tree_expand(draft_logits, frontier, tree, k, temperature, keep, new_frontier=None, workspace=None):
+    """One level of top-k expansion of `tree` (updated in place); returns new_frontier[B][keep]."""
+    draft_logits = _dev(draft_logits)
+    frontier = _dev(frontier, torch.int32)
+    B, F, V = draft_logits.shape
+    nmax = tree.parent.shape[1]
+    if frontier.shape != (B, F):
+        raise ValueError("frontier must be [B][F] matching draft_logits")
+    for name, t, dt in (("parent", tree.parent, torch.int32), ("tokens", tree.tokens, torch.int32),
+                        ("score", tree.score, torch.float64)):
+        if t.shape != (B, nmax) or t.dtype != dt or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"tree.{name} must be a contiguous [B][nmax] {dt} GPU tensor")
+    if new_frontier is None:
+        new_frontier = torch.empty((B, keep), dtype=torch.int32, device=draft_logits.device)
+    if workspace is None:
+        workspace = torch.empty((max(tree_expand_workspace_bytes(B, F), 1),), dtype=torch.uint8,
+                                device=draft_logits.device)
+    _check("specv_tree_expand", lib.specv_tree_expand(
+        _ptr(draft_logits), _dtype_code(draft_logits), _ptr(frontier), B, F, V, int(k), float(temperature),
+        int(keep), nmax, _ptr(tree.parent), _ptr(tree.tokens), _ptr(tree.score), _ptr(tree.n_nodes),
+        _ptr(new_frontier), _ptr(workspace), workspace.numel(), _stream()))
+    return new_frontier

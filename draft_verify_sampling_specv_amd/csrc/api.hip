@@ -10,6 +10,10 @@
 #include "../../include/specv.h"
 #include "kernels.h"
 
+static_assert(specv::kExpandMaxK == SPECV_EXPAND_MAX_K, "expansion width limit");
+static_assert(specv::kExpandMaxCand == SPECV_EXPAND_MAX_CANDIDATES, "expansion candidate limit");
+static_assert(specv::kMaxNodes == SPECV_MAX_NODES, "node limit");
+
 namespace {
 
 thread_local char g_last_error[256] = "";
@@ -148,6 +152,44 @@ specv_status specv_accept_resample(const void* target_logits, const void* draft_
                                       temperature, SPECV_SIBLINGS_WITHOUT_REPLACEMENT, seed, offset,
                                       accept_len, out_tokens, out_nodes, p_tok, q_tok, workspace,
                                       workspace_bytes, stream);
+}
+
+size_t specv_tree_expand_workspace_bytes(int32_t B, int32_t F) {
+    if (B <= 0 || F <= 0) return 0;
+    return specv::tree_expand_workspace_bytes(B, F);
+}
+
+specv_status specv_tree_expand(const void* draft_logits, specv_dtype dtype, const int32_t* frontier,
+                               int32_t B, int32_t F, int32_t V, int32_t k, float temperature,
+                               int32_t keep, int32_t nmax, int32_t* parent, int32_t* tokens,
+                               double* score, int32_t* n_nodes, int32_t* new_frontier, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+    if (B < 0) return fail(SPECV_ERR_INVALID_ARG, "B = %d < 0", B);
+    if (F < 1) return fail(SPECV_ERR_INVALID_ARG, "F = %d < 1", F);
+    if (V < 1 || V > SPECV_MAX_VOCAB)
+        return fail(SPECV_ERR_INVALID_ARG, "V = %d outside [1, %d]", V, SPECV_MAX_VOCAB);
+    if (k < 1 || k > SPECV_EXPAND_MAX_K)
+        return fail(SPECV_ERR_INVALID_ARG, "k = %d outside [1, %d]", k, SPECV_EXPAND_MAX_K);
+    if (static_cast<int64_t>(F) * k > SPECV_EXPAND_MAX_CANDIDATES)
+        return fail(SPECV_ERR_INVALID_ARG, "F * k = %lld > %d", static_cast<long long>(F) * k,
+                    SPECV_EXPAND_MAX_CANDIDATES);
+    if (!std::isfinite(temperature) || temperature <= 0.f)
+        return fail(SPECV_ERR_INVALID_ARG, "temperature must be finite and > 0");
+    if (keep < 1 || keep > SPECV_MAX_NODES)
+        return fail(SPECV_ERR_INVALID_ARG, "keep = %d outside [1, %d]", keep, SPECV_MAX_NODES);
+    if (nmax < 1 || nmax > SPECV_MAX_NODES)
+        return fail(SPECV_ERR_INVALID_ARG, "nmax = %d outside [1, %d]", nmax, SPECV_MAX_NODES);
+    if (dtype != SPECV_F32 && dtype != SPECV_BF16)
+        return fail(SPECV_ERR_UNSUPPORTED, "dtype %d not supported", static_cast<int>(dtype));
+    if (B == 0) return ok();
+    if (!draft_logits || !frontier || !parent || !tokens || !score || !n_nodes || !new_frontier)
+        return fail(SPECV_ERR_INVALID_ARG, "NULL pointer argument");
+    const size_t need = specv::tree_expand_workspace_bytes(B, F);
+    if (!workspace || workspace_bytes < need)
+        return fail(SPECV_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    specv::TreeExpandArgs a{draft_logits, dtype == SPECV_BF16, frontier, B, F, V, k, temperature, keep, nmax,
+                            parent, tokens, score, n_nodes, new_frontier, workspace};
+    return hip_status(specv::launch_tree_expand(a, stream), "tree_expand");
 }
 
 specv_status specv_kv_commit(void* k_cache, void* v_cache, const int32_t* ctx_len,

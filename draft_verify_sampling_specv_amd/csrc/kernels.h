@@ -47,6 +47,28 @@ struct AcceptArgs {
 size_t accept_workspace_bytes(int B, int n1, int V, bool bf16);
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
 
+// ------------------------------------------------------------------------------------ tree expansion
+constexpr int kExpandMaxK = 16;        // children per frontier node at most
+constexpr int kExpandMaxCand = 1024;   // frontier rows x k per sequence at most
+
+struct TreeExpandArgs {
+    const void* logits;
+    bool bf16;
+    const int32_t* frontier;
+    int B, F, V, k;
+    float temperature;
+    int keep, nmax;
+    int32_t* parent;
+    int32_t* tokens;
+    double* score;
+    int32_t* n_nodes;
+    int32_t* new_frontier;
+    void* workspace;
+};
+
+size_t tree_expand_workspace_bytes(int B, int F);
+hipError_t launch_tree_expand(const TreeExpandArgs& a, hipStream_t stream);
+
 // ------------------------------------------------------------------------------------ KV commit
 struct KvCommitArgs {
     void* k_cache;

@@ -12,7 +12,9 @@
  *   specv_accept_resample   the exact accept / reject / resample rule over the
  *                           vocabulary, for chains and for trees, greedy at
  *                           temperature 0;
- * and the step after them:
+ * and the steps around them:
+ *   specv_tree_expand       one level of draft-tree construction (top-k
+ *                           children kept by cumulative draft probability);
  *   specv_kv_commit         keep the accepted path's KV-cache rows, drop the
  *                           rejected branches'.
  *
@@ -274,6 +276,57 @@ specv_status specv_kv_commit(void* k_cache, void* v_cache, const int32_t* ctx_le
                              const int32_t* accept_len, const int32_t* out_nodes,
                              int32_t B, int32_t K, int32_t Hkv, int32_t D, int32_t Lmax,
                              specv_dtype dtype, int32_t* new_ctx_len, hipStream_t stream);
+
+/*
+ * One level of draft-tree expansion (EAGLE-style top-k children, kept by
+ * cumulative draft probability).
+ *
+ * [SD-EAGLE] "EAGLE: tree drafting and feature reuse": the draft outputs K
+ * candidates per depth (exercise 4: the top 3 branches at every depth), and
+ * EAGLE-2 grows the tree wide where the draft is unsure, narrow where it is
+ * confident; [PTD] Method 2, "Progressive Expansion & Pruning": each step
+ * drafts children for all current leaves in one pass, width control caps the
+ * children per parent.  For each sequence b:
+ *   - every frontier row f whose node u = frontier[b][f] is a node of the tree
+ *     (0 <= u < n_nodes[b]) proposes the min(k, V) tokens of largest draft
+ *     logit (ties: lower token id), child score = score[u] + log q(token),
+ *     q = softmax(draft_logits[b][f] / T);
+ *   - of all candidates, the `keep` of highest score survive (ties: earlier
+ *     row, then better rank), fewer when the tree reaches nmax nodes;
+ *   - survivors are appended as nodes n_nodes[b], n_nodes[b] + 1, ... in row
+ *     order, then rank order (parent, token and score written), n_nodes[b]
+ *     grows by their number, and their ids go to new_frontier[b] (then -1).
+ * Node ids stay topological, so parent[b][0 .. n_nodes) is a valid parent
+ * array for specv_build_tree_mask; the tokens of a tree built this way are
+ * fixed candidates (SPECV_SIBLINGS_DETERMINISTIC).
+ *
+ *   draft_logits  [B][F][V] dtype; row f belongs to frontier[b][f]
+ *   frontier      [B][F] int32 (entries that are not nodes: no row)
+ *   k             children per frontier node, 1 .. SPECV_EXPAND_MAX_K;
+ *                 F * k <= SPECV_EXPAND_MAX_CANDIDATES
+ *   temperature   T > 0, finite (only the scores depend on it)
+ *   keep          survivors per sequence at most, 1 .. SPECV_MAX_NODES (fewer
+ *                 when there are fewer candidates)
+ *   nmax          capacity of the tree arrays, <= SPECV_MAX_NODES
+ *   parent, tokens [B][nmax] int32; score [B][nmax] float64 (cumulative
+ *                 draft log-probability; the root's is usually 0); n_nodes [B]
+ *                 int32; all read and updated in place
+ *   new_frontier  [B][keep] int32
+ *   workspace / workspace_bytes: at least specv_tree_expand_workspace_bytes(B, F)
+ *
+ * Errors: SPECV_ERR_INVALID_ARG (NULL pointer, sizes out of range, T <= 0),
+ * SPECV_ERR_UNSUPPORTED (dtype), SPECV_ERR_WORKSPACE, SPECV_ERR_HIP.
+ */
+#define SPECV_EXPAND_MAX_K 16
+#define SPECV_EXPAND_MAX_CANDIDATES 1024
+
+specv_status specv_tree_expand(const void* draft_logits, specv_dtype dtype, const int32_t* frontier,
+                               int32_t B, int32_t F, int32_t V, int32_t k, float temperature,
+                               int32_t keep, int32_t nmax, int32_t* parent, int32_t* tokens,
+                               double* score, int32_t* n_nodes, int32_t* new_frontier,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+size_t specv_tree_expand_workspace_bytes(int32_t B, int32_t F);
 
 /* Static description of a status code. */
 const char* specv_status_string(specv_status s);

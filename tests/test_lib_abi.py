@@ -158,3 +158,27 @@ def test_accept_rule_host_validation(specv):
     assert call(1, draft=None) == 1          # and for i.i.d. siblings
     assert lib.specv_accept_resample_rule(v, None, 1, v, v, 0, 3, 100, 1.0, 2, 0, 0, v, v, v, None, None,
                                           v, 1 << 30, None) == 0      # B == 0: no launch
+
+
+def test_tree_expand_host_validation(specv):
+    lib = specv.lib
+    v = ctypes.c_void_p(16)
+
+    def call(**kw):
+        a = dict(B=2, F=4, V=100, k=3, T=1.0, keep=5, nmax=32, dtype=1, ws=v, wsb=1 << 20)
+        a.update(kw)
+        return lib.specv_tree_expand(v, a["dtype"], v, a["B"], a["F"], a["V"], a["k"], a["T"], a["keep"], a["nmax"],
+                                     v, v, v, v, v, a["ws"], a["wsb"], None)
+
+    assert call(k=0) == 1
+    assert call(k=17) == 1
+    assert call(F=100, k=16) == 1                        # F * k > 1024
+    assert call(T=0.0) == 1
+    assert call(keep=0) == 1
+    assert call(nmax=1025) == 1
+    assert call(V=0) == 1
+    assert call(dtype=4) == 2
+    assert call(ws=None) == 3
+    assert call(wsb=8) == 3
+    assert call(B=0) == 0
+    assert specv.tree_expand_workspace_bytes(2, 4) > 0
