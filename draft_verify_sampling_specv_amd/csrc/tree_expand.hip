@@ -8,10 +8,12 @@
 // each step drafts children for all current leaves in one pass; width control caps the children
 // per parent.
 //
-//   expand_topk_kernel   one workgroup per frontier row: one coalesced pass over the row keeps a
-//                        per-thread top-k (registers) and the online (max, sum of exp) of z / T;
-//                        the workgroup merges the per-thread lists in LDS (k rounds of a
-//                        wave-wide argmax over the lists' heads).  HBM-bound: each row is read once.
+//   expand_topk_kernel   one 16-wave workgroup per frontier row: one coalesced pass over the row
+//                        (batches of four 16-byte loads per thread) keeps a per-thread top-k in
+//                        registers -- a batch is examined only if its max would enter -- and the
+//                        online (max, sum of exp) of z / T, one rescale per vector; k rounds of a
+//                        wave-wide argmax over the lanes' list heads merge each wave, and one wave
+//                        merges the waves' lists through LDS.  HBM-bound: each row is read once.
 //   expand_select_kernel one workgroup per sequence: the rank of every candidate (score, then
 //                        frontier row, then rank within the row) by counting, the `keep` best
 //                        survive (fewer at the node capacity) and are appended in frontier / rank
@@ -28,8 +30,9 @@
 namespace specv {
 namespace {
 
-constexpr int kTopThreads = 256;
+constexpr int kTopThreads = 1024;           // 16 waves per row: enough loads in flight
 constexpr int kTopWaves = kTopThreads / kWave;
+constexpr int kBatch = 4;                   // 16-byte vectors per thread loaded together
 constexpr int kSelThreads = 512;
 
 struct RowTop {              // per-row result in the workspace
@@ -40,19 +43,46 @@ struct RowTop {              // per-row result in the workspace
     int32_t pad;
 };
 
+// The elements of one 16-byte vector as fp32 (bf16: its bits in the high half of a word; exact).
+template <typename T>
+__device__ __forceinline__ void unpack16(const uint4& r, float* out);
+template <>
+__device__ __forceinline__ void unpack16<float>(const uint4& r, float* out) {
+    out[0] = __uint_as_float(r.x); out[1] = __uint_as_float(r.y);
+    out[2] = __uint_as_float(r.z); out[3] = __uint_as_float(r.w);
+}
+template <>
+__device__ __forceinline__ void unpack16<uint16_t>(const uint4& r, float* out) {
+    out[0] = bf16_lo(r.x); out[1] = bf16_hi(r.x); out[2] = bf16_lo(r.y); out[3] = bf16_hi(r.y);
+    out[4] = bf16_lo(r.z); out[5] = bf16_hi(r.z); out[6] = bf16_lo(r.w); out[7] = bf16_hi(r.w);
+}
+
 // (value, index) order: larger value first, then lower index
 __device__ __forceinline__ bool better(float v, int i, float v2, int i2) {
     return v > v2 || (v == v2 && i < i2);
 }
 
-template <typename T>
+// The kk-th largest of v over the wave (counting repeats): kk rounds, each removing the largest
+// (one lane at a time).
+__device__ __forceinline__ float wave_kth_largest(float v, int kk, int lane) {
+    float cur = -INFINITY;
+    for (int r = 0; r < kk; ++r) {
+        cur = wave_max(v);
+        const uint64_t at = __ballot(v == cur);
+        if (at && lane == __ffsll(static_cast<unsigned long long>(at)) - 1) v = -INFINITY;
+    }
+    return cur;
+}
+
+// K: capacity of the per-thread lists (k <= K); a list keeps its thread's K best entered elements
+template <typename T, int K>
 __global__ void __launch_bounds__(kTopThreads)
 expand_topk_kernel(const T* __restrict__ logits, const int32_t* __restrict__ frontier,
                    const int32_t* __restrict__ n_nodes, int F, int V, int k, int nmax, float kexp2,
                    double invT, RowTop* __restrict__ rows) {
-    __shared__ float sv[kExpandMaxK][kTopThreads];
-    __shared__ int si[kExpandMaxK][kTopThreads];
-    __shared__ int head[kTopThreads];
+    constexpr int kVec = Elem<T>::kVec;
+    __shared__ float lv[kTopWaves][K];
+    __shared__ int li[kTopWaves][K];
     __shared__ float wm[kTopWaves], ws[kTopWaves];
     const int row = blockIdx.x, b = row / F;
     const int t = threadIdx.x, lane = t % kWave, w = t / kWave;
@@ -63,88 +93,154 @@ expand_topk_kernel(const T* __restrict__ logits, const int32_t* __restrict__ fro
         return;
     }
     const T* z = logits + static_cast<int64_t>(row) * V;
+    const int kk = min(k, V);
 
-    // per-thread top-k, sorted (value desc, index asc); this thread's elements come in increasing
-    // index order, so a strictly larger value is needed to enter
-    float tv[kExpandMaxK];
-    int ti[kExpandMaxK];
+    // per-thread list of the K best entered elements, sorted (value desc, index asc); this
+    // thread's elements come in increasing index order, so a strictly larger value is needed to
+    // displace the K-th
+    float tv[K];
+    int ti[K];
 #pragma unroll
-    for (int j = 0; j < kExpandMaxK; ++j) { tv[j] = -INFINITY; ti[j] = INT_MAX; }
-    float thr = -INFINITY;               // the current k-th value (entry k-1) once k are held
+    for (int j = 0; j < K; ++j) { tv[j] = -INFINITY; ti[j] = INT_MAX; }
+    float wthr = -INFINITY;              // the wave-wide entry bound (see below)
     int held = 0;
     float m = -INFINITY, s = 0.f;        // online max and sum of exp2((x - m) kexp2)
-    auto take = [&](float x, int xi) {
-        const float mn = fmaxf(m, x);
-        const float ref = (mn == -INFINITY) ? 0.f : mn;
-        s = s * __builtin_amdgcn_exp2f((m - ref) * kexp2) + __builtin_amdgcn_exp2f((x - ref) * kexp2);
-        m = mn;
-        if (held < k || x > thr) {
-            ++held;
-            // insert: shift the worse entries down one place
-            float cv = x;
-            int ci = xi;
+    auto insert = [&](float x, int xi) {
+        ++held;
+        float cv = x;
+        int ci = xi;
 #pragma unroll
-            for (int j = 0; j < kExpandMaxK; ++j) {
-                const bool go = j < k && better(cv, ci, tv[j], ti[j]);
-                const float ov = tv[j];
-                const int oi = ti[j];
-                tv[j] = go ? cv : ov;
-                ti[j] = go ? ci : oi;
-                cv = go ? ov : cv;
-                ci = go ? oi : ci;
-            }
-            float nt = tv[0];
-#pragma unroll
-            for (int j = 1; j < kExpandMaxK; ++j) nt = (j == k - 1) ? tv[j] : nt;
-            thr = nt;
+        for (int j = 0; j < K; ++j) {
+            const bool go = better(cv, ci, tv[j], ti[j]);
+            const float ov = tv[j];
+            const int oi = ti[j];
+            tv[j] = go ? cv : ov;
+            ti[j] = go ? ci : oi;
+            cv = go ? ov : cv;
+            ci = go ? oi : ci;
         }
     };
-    constexpr int kVec = Elem<T>::kVec;
-    if ((V % kVec) == 0 && (reinterpret_cast<uintptr_t>(z) & 15) == 0) {
-        for (int base = t * kVec; base < V; base += kTopThreads * kVec) {
-            float x[kVec];
-            Elem<T>::load_vec(z, base, x);
+    // batches of kBatch vectors per thread: loads first, then the values (elements past V are -inf)
+    constexpr int kStep = kTopThreads * kVec;
+    const bool vec = (V % kVec) == 0 && (reinterpret_cast<uintptr_t>(z) & 15) == 0;
+    for (int b0 = 0; b0 < V; b0 += kBatch * kStep) {
+        float x[kBatch][kVec];
+        if (vec) {
+            uint4 r[kBatch];
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) take(x[e], base + e);
+            for (int q = 0; q < kBatch; ++q) {
+                const int base = b0 + q * kStep + t * kVec;
+                r[q] = make_uint4(0, 0, 0, 0);
+                if (base < V) r[q] = *reinterpret_cast<const uint4*>(z + base);
+            }
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                const int base = b0 + q * kStep + t * kVec;
+                float y[kVec];
+                unpack16<T>(r[q], y);
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) x[q][e] = base < V ? y[e] : -INFINITY;
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q)
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) {
+                    const int i = b0 + q * kStep + t * kVec + e;
+                    x[q][e] = i < V ? Elem<T>::load(z, i) : -INFINITY;
+                }
         }
-    } else {
-        for (int i = t; i < V; i += kTopThreads) take(Elem<T>::load(z, i), i);
+        float bmax = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            float vm = x[q][0];
+#pragma unroll
+            for (int e = 1; e < kVec; ++e) vm = fmaxf(vm, x[q][e]);
+            // online log-sum-exp, one rescale per vector
+            const float mn = fmaxf(m, vm);
+            const float ref = (mn == -INFINITY) ? 0.f : mn;
+            float add = 0.f;
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) add += __builtin_amdgcn_exp2f((x[q][e] - ref) * kexp2);
+            s = s * __builtin_amdgcn_exp2f((m - ref) * kexp2) + add;
+            m = mn;
+            bmax = fmaxf(bmax, vm);
+        }
+        // wave-wide entry bound: the kk-th largest of the lanes' batch maxima -- kk elements at
+        // or above it exist, so anything below it cannot be in the wave's top-k (equal values may
+        // still be, on index); it only grows
+        wthr = fmaxf(wthr, wave_kth_largest(bmax, kk, lane));
+        if (bmax >= wthr) {
+            const float thr = tv[K - 1];          // -inf while the list is not full
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q)
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) {
+                    const int i = b0 + q * kStep + t * kVec + e;
+                    if (i < V && x[q][e] >= wthr && (held < K || x[q][e] > thr)) insert(x[q][e], i);
+                }
+        }
     }
 
-    // workgroup log-sum-exp (fp64 above the per-thread sums)
+    // per wave: kk rounds, each taking the best head of the lanes' sorted lists (the winning lane
+    // shifts its list up by one)
     wave_max_sum(m, s, kexp2);
     if (lane == 0) { wm[w] = m; ws[w] = s; }
+    for (int r = 0; r < kk; ++r) {
+        float bv = tv[0];
+        int bi = ti[0], bl = (ti[0] == INT_MAX) ? -1 : lane;
 #pragma unroll
-    for (int j = 0; j < kExpandMaxK; ++j) { sv[j][t] = tv[j]; si[j][t] = ti[j]; }
-    head[t] = 0;
+        for (int o = 32; o > 0; o >>= 1) {
+            const float v2 = __shfl_xor(bv, o);
+            const int i2 = __shfl_xor(bi, o), l2 = __shfl_xor(bl, o);
+            if (l2 >= 0 && (bl < 0 || better(v2, i2, bv, bi))) { bv = v2; bi = i2; bl = l2; }
+        }
+        if (lane == bl) {
+#pragma unroll
+            for (int j = 0; j + 1 < K; ++j) { tv[j] = tv[j + 1]; ti[j] = ti[j + 1]; }
+            tv[K - 1] = -INFINITY;
+            ti[K - 1] = INT_MAX;
+        }
+        if (lane == 0) {
+            lv[w][r] = bv;
+            li[w][r] = bl >= 0 ? bi : INT_MAX;
+        }
+    }
     __syncthreads();
     if (w == 0) {
-        // merge: k rounds, each taking the best head among the 256 sorted lists
-        const int kk = min(k, V);
+        // across waves: up to kTopWaves x kk candidates, kTopWaves * kExpandMaxK / 64 per lane
+        constexpr int kPer = (kTopWaves * K + kWave - 1) / kWave;
+        float cv[kPer];
+        int ci[kPer];
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int e = q * kWave + lane, ww = e / K, rr = e % K;
+            const bool ok = ww < kTopWaves && rr < kk;
+            cv[q] = ok ? lv[min(ww, kTopWaves - 1)][rr] : -INFINITY;
+            ci[q] = ok ? li[min(ww, kTopWaves - 1)][rr] : INT_MAX;
+        }
         for (int r = 0; r < kk; ++r) {
             float bv = -INFINITY;
-            int bi = INT_MAX, bl = -1;
+            int bi = INT_MAX, bq = -1;
 #pragma unroll
-            for (int q = 0; q < kTopThreads / kWave; ++q) {
-                const int l = q * kWave + lane;
-                const int h = head[l];
-                const float v = h < k ? sv[h][l] : -INFINITY;
-                const int i = h < k ? si[h][l] : INT_MAX;
-                if (i != INT_MAX && (bl < 0 || better(v, i, bv, bi))) { bv = v; bi = i; bl = l; }
-            }
+            for (int q = 0; q < kPer; ++q)
+                if (ci[q] != INT_MAX && (bq < 0 || better(cv[q], ci[q], bv, bi))) { bv = cv[q]; bi = ci[q]; bq = q; }
+            int bl = bq >= 0 ? lane : -1;
 #pragma unroll
             for (int o = 32; o > 0; o >>= 1) {
                 const float v2 = __shfl_xor(bv, o);
                 const int i2 = __shfl_xor(bi, o), l2 = __shfl_xor(bl, o);
                 if (l2 >= 0 && (bl < 0 || better(v2, i2, bv, bi))) { bv = v2; bi = i2; bl = l2; }
             }
-            if (lane == 0 && bl >= 0) {
+            if (lane == bl) {
+#pragma unroll
+                for (int q = 0; q < kPer; ++q)
+                    if (q == bq) ci[q] = INT_MAX;
+            }
+            if (lane == 0) {
                 out->tok[r] = bi;
                 out->z[r] = bv;
-                head[bl] += 1;
             }
-            __builtin_amdgcn_s_waitcnt(0);   // (the head update is read by the next round)
-            __builtin_amdgcn_wave_barrier();
         }
         if (lane == 0) {
             float M = -INFINITY;
@@ -225,6 +321,12 @@ expand_select_kernel(const RowTop* __restrict__ rows, const int32_t* __restrict_
     if (t == 0) n_nodes[b] = n + M;
 }
 
+template <typename T, int K>
+void launch_topk(const TreeExpandArgs& a, const T* z, float kexp2, double invT, RowTop* rows, hipStream_t stream) {
+    hipLaunchKernelGGL((expand_topk_kernel<T, K>), dim3(a.B * a.F), dim3(kTopThreads), 0, stream, z, a.frontier,
+                       a.n_nodes, a.F, a.V, a.k, a.nmax, kexp2, invT, rows);
+}
+
 }  // namespace
 
 size_t tree_expand_workspace_bytes(int B, int F) { return sizeof(RowTop) * static_cast<size_t>(B) * F; }
@@ -233,14 +335,17 @@ hipError_t launch_tree_expand(const TreeExpandArgs& a, hipStream_t stream) {
     RowTop* rows = static_cast<RowTop*>(a.workspace);
     const double invT = 1.0 / static_cast<double>(a.temperature);
     const float kexp2 = static_cast<float>(1.4426950408889634 * invT);
-    if (a.bf16)
-        hipLaunchKernelGGL(expand_topk_kernel<uint16_t>, dim3(a.B * a.F), dim3(kTopThreads), 0, stream,
-                           static_cast<const uint16_t*>(a.logits), a.frontier, a.n_nodes, a.F, a.V, a.k, a.nmax,
-                           kexp2, invT, rows);
-    else
-        hipLaunchKernelGGL(expand_topk_kernel<float>, dim3(a.B * a.F), dim3(kTopThreads), 0, stream,
-                           static_cast<const float*>(a.logits), a.frontier, a.n_nodes, a.F, a.V, a.k, a.nmax,
-                           kexp2, invT, rows);
+    if (a.bf16) {
+        const uint16_t* z = static_cast<const uint16_t*>(a.logits);
+        if (a.k <= 4) launch_topk<uint16_t, 4>(a, z, kexp2, invT, rows, stream);
+        else if (a.k <= 8) launch_topk<uint16_t, 8>(a, z, kexp2, invT, rows, stream);
+        else launch_topk<uint16_t, 16>(a, z, kexp2, invT, rows, stream);
+    } else {
+        const float* z = static_cast<const float*>(a.logits);
+        if (a.k <= 4) launch_topk<float, 4>(a, z, kexp2, invT, rows, stream);
+        else if (a.k <= 8) launch_topk<float, 8>(a, z, kexp2, invT, rows, stream);
+        else launch_topk<float, 16>(a, z, kexp2, invT, rows, stream);
+    }
     hipLaunchKernelGGL(expand_select_kernel, dim3(a.B), dim3(kSelThreads), 0, stream, rows, a.frontier, a.F, a.k,
                        a.keep, a.nmax, invT, a.parent, a.tokens, a.score, a.n_nodes, a.new_frontier);
     return hipGetLastError();
