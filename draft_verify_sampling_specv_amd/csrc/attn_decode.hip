@@ -15,7 +15,8 @@ using namespace attn;
 // head with two row blocks gets two workgroups, placed on one XCD so that the second one's K/V
 // reads hit that XCD's L2; its KS waves split the key tiles round-robin, each wave computing the
 // workgroup's row blocks for its tiles, and the waves' partial softmax states are merged through
-// LDS at the end, so the final output is written directly (no partials in HBM).
+// LDS at the end (one round: scaled states published, each wave sums and stores one slice), so the
+// final output is written directly (no partials in HBM).
 //   * every K/V load is unconditional, its key index clamped to the last valid key (masked in
 //     the softmax), so the compiler never waits for the prefetch before it is needed;
 //   * each lane keeps its query row's tree-mask words (at most two) in registers.
@@ -35,7 +36,7 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     constexpr int kKS = D / 16;        // k-steps of S^T = K Q^T
     constexpr int kDH = D / 64;        // 64-feature halves: MFMA blocks 2 dh (even) and 2 dh + 1 (odd)
     constexpr int kDB = D / 32;
-    extern __shared__ float xs[];      // merge buffer: (KS / 2) x RBW x kDB x 16 x 64 floats + m, l
+    extern __shared__ float xs[];      // merge buffer: KS x RBW x kDB x 16 x 64 floats + m, l
     __shared__ uint4 sq[RBW][kKS][kWave];   // Q^T operands of the workgroup's row blocks
 
     // block id -> (unit = (sequence, KV head), row group of RBW blocks); with xcd_map the row
@@ -210,73 +211,70 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
             }
     }
 
-    // ---- merge the KS waves' states: halving tree through LDS
+    // ---- merge the KS waves' states in one round through LDS: every wave publishes (m, l), then
+    //      its O scaled to the common max; each wave then sums one slice of the registers over the
+    //      KS waves and stores that slice of the output (one 16-byte store per lane)
     constexpr int kRegs = RBW * kDB * 16;
-    float* ml = xs + (KS / 2) * kRegs * kWave;
-    for (int half = KS / 2; half >= 1; half /= 2) {
-        if (w >= half && w < 2 * half) {
-            float* dst = xs + (w - half) * kRegs * kWave;
+    float* ml = xs + KS * kRegs * kWave;                 // [KS][RBW][m, l][lane]
 #pragma unroll
-            for (int j = 0; j < RBW; ++j) {
-#pragma unroll
-                for (int i = 0; i < kDB; ++i)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) dst[((j * kDB + i) * 16 + r) * kWave + lane] = o[j][i][r];
-                ml[((w - half) * RBW + j) * 2 * kWave + lane] = m[j];
-                ml[((w - half) * RBW + j) * 2 * kWave + kWave + lane] = l[j];
-            }
-        }
-        __syncthreads();
-        if (w < half) {
-            const float* src = xs + w * kRegs * kWave;
-#pragma unroll
-            for (int j = 0; j < RBW; ++j) {
-                const float m2 = ml[(w * RBW + j) * 2 * kWave + lane];
-                const float l2 = ml[(w * RBW + j) * 2 * kWave + kWave + lane];
-                const float M = fmaxf(m[j], m2);
-                const float a1 = (m[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[j] - M);
-                const float a2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
-#pragma unroll
-                for (int i = 0; i < kDB; ++i)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        o[j][i][r] = a1 * o[j][i][r] + a2 * src[((j * kDB + i) * 16 + r) * kWave + lane];
-                l[j] = a1 * l[j] + a2 * l2;
-                m[j] = M;
-            }
-        }
-        __syncthreads();
+    for (int j = 0; j < RBW; ++j) {
+        ml[((w * RBW + j) * 2) * kWave + lane] = m[j];
+        ml[((w * RBW + j) * 2 + 1) * kWave + lane] = l[j];
     }
-
-    if (w == 0) {
+    __syncthreads();
+    float Mx[RBW], Lx[RBW];
 #pragma unroll
-        for (int j = 0; j < RBW; ++j) {
-            if (!rok[j]) continue;
-            const int node = rows[j] / G, g = rows[j] - (rows[j] / G) * G;
+    for (int j = 0; j < RBW; ++j) {
+        float M = -INFINITY;
+        for (int q = 0; q < KS; ++q) M = fmaxf(M, ml[((q * RBW + j) * 2) * kWave + lane]);
+        float L = 0.f;
+        for (int q = 0; q < KS; ++q) {
+            const float mq = ml[((q * RBW + j) * 2) * kWave + lane];
+            if (mq != -INFINITY) L += __builtin_amdgcn_exp2f(mq - M) * ml[((q * RBW + j) * 2 + 1) * kWave + lane];
+        }
+        Mx[j] = M;
+        Lx[j] = L;
+        const float aw = (m[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[j] - M);
+        float* dst = xs + w * kRegs * kWave;
+#pragma unroll
+        for (int i = 0; i < kDB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dst[((j * kDB + i) * 16 + r) * kWave + lane] = aw * o[j][i][r];
+    }
+    __syncthreads();
+    // slice sl = (j, dh, rr): registers 4 rr .. 4 rr + 3 of blocks 2 dh (even features) and 2 dh + 1
+    // (odd), i.e. feature slots i = 8 rr + 4 h + 0..3: features 64 dh + 2 i and 64 dh + 2 i + 1
+    for (int sl = w; sl < RBW * kDH * 4; sl += KS) {
+        const int j = sl / (kDH * 4), dh = (sl / 4) % kDH, rr = sl % 4;
+        float ev[4] = {0.f, 0.f, 0.f, 0.f}, od[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < KS; ++q) {
+            const float* src = xs + q * kRegs * kWave;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ev[e] += src[((j * kDB + 2 * dh) * 16 + 4 * rr + e) * kWave + lane];
+                od[e] += src[((j * kDB + 2 * dh + 1) * 16 + 4 * rr + e) * kWave + lane];
+            }
+        }
+        const int row = (grp * RBW + j) * 32 + col;
+        if (row < R) {
+            const int node = row / G, g = row - node * G;
             const int64_t orow = (static_cast<int64_t>(b) * n1 + node) * Hq + kv * G + g;
-            uint16_t* op = out + orow * D;
-            const float inv = seq_ok ? 1.f / l[j] : NAN;
-#pragma unroll
-            for (int dh = 0; dh < kDH; ++dh)
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    // registers 4 rr .. 4 rr + 3 hold feature slots i = 8 rr + 4 h + 0..3, i.e.
-                    // features 64 dh + 2 i (even block) and 64 dh + 2 i + 1 (odd block)
-                    uint4 st;
-                    st.x = pack_bf16x2(o[j][2 * dh][4 * rr + 0] * inv, o[j][2 * dh + 1][4 * rr + 0] * inv);
-                    st.y = pack_bf16x2(o[j][2 * dh][4 * rr + 1] * inv, o[j][2 * dh + 1][4 * rr + 1] * inv);
-                    st.z = pack_bf16x2(o[j][2 * dh][4 * rr + 2] * inv, o[j][2 * dh + 1][4 * rr + 2] * inv);
-                    st.w = pack_bf16x2(o[j][2 * dh][4 * rr + 3] * inv, o[j][2 * dh + 1][4 * rr + 3] * inv);
-                    *reinterpret_cast<uint4*>(op + 64 * dh + 2 * (8 * rr + 4 * h)) = st;
-                }
-            if (lse && h == 0) lse[orow] = seq_ok ? (m[j] + log2f(l[j])) * kLn2 : NAN;
+            const float inv = seq_ok ? 1.f / Lx[j] : NAN;
+            uint4 st;
+            st.x = pack_bf16x2(ev[0] * inv, od[0] * inv);
+            st.y = pack_bf16x2(ev[1] * inv, od[1] * inv);
+            st.z = pack_bf16x2(ev[2] * inv, od[2] * inv);
+            st.w = pack_bf16x2(ev[3] * inv, od[3] * inv);
+            *reinterpret_cast<uint4*>(out + orow * D + 64 * dh + 2 * (8 * rr + 4 * h)) = st;
+            if (lse && h == 0 && dh == 0 && rr == 0)
+                lse[orow] = seq_ok ? (Mx[j] + log2f(Lx[j])) * kLn2 : NAN;
         }
     }
 }
 
 template <int D, int KS, int RBW>
 void launch_decode(const AttnArgs& a, int ngroups, hipStream_t stream) {
-    const size_t lds = sizeof(float) * (size_t(KS / 2) * RBW * (D / 32) * 16 * kWave + size_t(KS / 2) * RBW * 2 * kWave);
+    const size_t lds = sizeof(float) * (size_t(KS) * RBW * (D / 32) * 16 * kWave + size_t(KS) * RBW * 2 * kWave);
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&attn_decode_kernel<D, KS, RBW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
