@@ -29,6 +29,12 @@ Modules
              Rule", greedy case).
   kv_commit  the KV-cache commit after a verify step ([SD-review] §4;
              [SD-EAGLE] "Tree Attention Verification").
+  tree_expand  one level of draft-tree construction ([SD-EAGLE] "EAGLE: tree
+             drafting and feature reuse"; [PTD] Method 2).
+  layer      one target-model layer over the draft nodes: norm, q/k/v
+             projection, rotary encoding at depth positions, tree attention,
+             output projection, gated MLP ([SD-EAGLE] "Two-Model Setup" step
+             2; [PTD] Method 4, "Verification").
 
 Pins (tests marked "not gpu" check each function against something other than
 itself): Philox known-answer vectors and numpy's independent Philox; the
@@ -38,6 +44,8 @@ over each root-to-node path; the exact output law of the accept rule (== p, to
 1e-12, by enumeration of draws and decision branches); the closed form
 E[tokens] = (1 - a^(K+1)) / (1 - a); empirical TV / chi-square tests; the
 greedy rule; inverse CDF == numpy.searchsorted; attention over the committed
-cache prefix == the tree-masked verify rows.  No function here is "parity
+cache prefix == the tree-masked verify rows; the layer over a chain == a plain
+causal layer written with torch, and over a tree == that layer on each
+root-to-node path.  No function here is "parity
 unpinned".
 """
