@@ -11,7 +11,10 @@ Prints ONE JSON line.  Extra legs:
                 on the launch stream); the accept call's figure is reported beside it;
   cpu_baseline  the oracle (numpy fp64) on a bounded sample of the same workload, host cores.
 
-  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--copy-probe]
+  verify_layer  one whole target layer over the same 192 rows (specv_verify_layer): its time,
+                the attention call's share of it, and the weight-streaming rate of the rest.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-layer] [--copy-probe]
 --copy-probe only runs a device-to-device copy of known size (to calibrate HBM byte counters).
 """
 
@@ -57,8 +60,8 @@ ATTN_TRAFFIC = {
                 "draft_verify_sampling_specv_amd/csrc/attn_common.h",
                 "draft_verify_sampling_specv_amd/csrc/common.h",
                 "draft_verify_sampling_specv_amd/csrc/kernels.h"],
-    "sha256": "9f314491e3dfb12dab0756aa7c0e2620ffcfae75c7be27cf37e433879e779425",
-    "fetch_kib": 132471.3, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131084.0, "write_scale": 1.0,
+    "sha256": "d203da3aa7222441216328ff801a8ddc0de040f9a8667abeea591ae3c271e9de",
+    "fetch_kib": 132442.5, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131084.0, "write_scale": 1.0,
 }
 
 
@@ -85,6 +88,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline leg")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--no-layer", action="store_true", help="skip the one-layer measurement")
     ap.add_argument("--config", default=None, choices=sorted(CONFIGS),
                     help="measure every kernel on one configuration (prints a per-config JSON line "
                          "instead of the headline line)")
@@ -231,6 +235,7 @@ def main():
     copy_gbs = 2 * (1 << 30) / (ms_copy * 1e-3) / 1e9
     del big, big2
 
+    acc_sets0_w = acc_sets[0]["w"]
     # acceptance statistics of the timed configuration (set 0)
     res = specv.accept_resample(acc_sets[0]["target"], acc_sets[0]["draft"], acc_sets[0]["tokens"], parent, T,
                                 seed=1234, offset=0)
@@ -274,9 +279,76 @@ def main():
         "hbm_copy_gbs": copy_gbs,
     }
 
+    del attn_sets, acc_sets
+    torch.cuda.empty_cache()
+    if not args.no_layer:
+        out["verify_layer"] = measure_layer(torch, specv, max(10, args.steps // 4))
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(acc_sets[0]["w"], a0)
+        out["cpu_baseline"] = cpu_baseline(acc_sets0_w, a0)
     print(json.dumps(out))
+
+
+LAYER_INTER = 14336
+
+
+def measure_layer(torch, specv, steps):
+    """One target layer over the chain step's 192 rows (specv_verify_layer): hidden 4096 (32/8
+    heads of 128), MLP width 14336, random-init bf16 weights rotated over two sets (> the
+    Infinity Cache), context 2048.  Reports the layer time, the attention call alone on the same
+    shape and the weight-streaming rate of the rest (projections + their epilogues)."""
+    n1 = K + 1
+    hd = HQ * D
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+
+    def lin(rows, cols):
+        return (torch.randn(rows, cols, generator=gen, device="cuda") / math.sqrt(cols)).to(torch.bfloat16)
+
+    def gain():
+        return (1 + 0.2 * torch.randn(hd, generator=gen, device="cuda")).to(torch.bfloat16)
+
+    sets = [specv.LayerWeights(lin((HQ + 2 * HKV) * D, hd), lin(hd, hd), lin(2 * LAYER_INTER, hd),
+                               lin(hd, LAYER_INTER), gain(), gain()) for _ in range(2)]
+    wbytes = 2 * ((HQ + 2 * HKV) * D * hd + hd * hd + 2 * LAYER_INTER * hd + hd * LAYER_INTER + 2 * hd)
+    x = torch.randn(B, n1, hd, generator=gen, device="cuda").to(torch.bfloat16)
+    lmax = CTX + n1
+    kc = torch.randn(B, HKV, lmax, D, generator=gen, device="cuda").to(torch.bfloat16)
+    vc = torch.randn(B, HKV, lmax, D, generator=gen, device="cuda").to(torch.bfloat16)
+    ctx = torch.full((B,), CTX, dtype=torch.int32, device="cuda")
+    parent = torch.arange(-1, K, dtype=torch.int32, device="cuda").repeat(B, 1)
+    mask, depth, _ = specv.build_tree_mask(parent)
+    ws = torch.empty((specv.verify_layer_workspace_bytes(B, K, HQ, HKV, D, lmax, LAYER_INTER),), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty_like(x)
+    q = torch.randn(B, n1, HQ, D, generator=gen, device="cuda").to(torch.bfloat16)
+    abuf = specv.AttnBuffers.allocate(q, kc)
+
+    def run(i):
+        specv.verify_layer(x, sets[i % 2], kc, vc, ctx, mask, depth, HQ, out=out, workspace=ws)
+
+    def timed(fn, n):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(n):
+            fn(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n
+
+    for i in range(4):
+        run(i)
+    ms_layer = timed(run, steps)
+    ms_attn = timed(lambda i: specv.tree_attn_verify(q, kc, vc, ctx, mask, buffers=abuf), steps)
+    rest = max(ms_layer - ms_attn, 1e-9)
+    gbs = wbytes / (rest * 1e-3) / 1e9
+    del sets, kc, vc, ws
+    torch.cuda.empty_cache()
+    return {"workload": "chain step as one layer: 192 rows, hidden 4096 (32/8 heads of 128), MLP 14336, "
+                        "ctx 2048, bf16 random-init weights",
+            "ms": ms_layer, "ms_attention_alone": ms_attn, "attention_share": ms_attn / ms_layer,
+            "weight_bytes": wbytes, "weights_gbs_outside_attention": gbs,
+            "weights_hbm_frac_outside_attention": gbs / HBM_PEAK_GBS}
 
 
 def measure_config(name, args, torch, specv, workloads):

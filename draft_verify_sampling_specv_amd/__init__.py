@@ -10,6 +10,7 @@ library has not been built this import fails.
   accept_resample(target, draft, tokens, parent, T, seed, offset) -> AcceptResult
   kv_commit(k_cache, v_cache, ctx_len, accept_len, out_nodes)     -> new_ctx_len
   tree_expand(draft_logits, frontier, tree, k, T, keep)           -> new_frontier (tree updated)
+  verify_layer(x, weights, k_cache, v_cache, ctx_len, mask, depth, Hq) -> out (caches written)
 """
 
 from ._lib import (  # noqa: F401
@@ -28,4 +29,7 @@ from ._lib import (  # noqa: F401
     tree_expand_workspace_bytes,
     accept_workspace_bytes,
     attn_workspace_bytes,
+    LayerWeights,
+    verify_layer,
+    verify_layer_workspace_bytes,
 )

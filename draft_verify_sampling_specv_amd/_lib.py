@@ -66,6 +66,12 @@ lib.specv_kv_commit.argtypes = [
     ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
     ctypes.c_int, _vp, _vp]
 
+lib.specv_verify_layer_workspace_bytes.restype = ctypes.c_size_t
+lib.specv_verify_layer_workspace_bytes.argtypes = [ctypes.c_int32] * 7
+lib.specv_verify_layer.restype = ctypes.c_int
+lib.specv_verify_layer.argtypes = (
+    [_vp] * 7 + [ctypes.c_float, ctypes.c_float] + [_vp] * 5 + [ctypes.c_int32] * 7 + [_vp, _vp, ctypes.c_size_t, _vp])
+
 
 class SpecvError(RuntimeError):
     def __init__(self, fn, status):
@@ -293,3 +299,59 @@ def tree_expand(draft_logits, frontier, tree, k, temperature, keep, new_frontier
         int(keep), nmax, _ptr(tree.parent), _ptr(tree.tokens), _ptr(tree.score), _ptr(tree.n_nodes),
         _ptr(new_frontier), _ptr(workspace), workspace.numel(), _stream()))
     return new_frontier
+
+
+# ----------------------------------------------------------------------------- verify layer
+
+@dataclass
+class LayerWeights:
+    """bf16 GPU tensors in the [out][in] layout of a linear map."""
+    w_qkv: torch.Tensor          # [(Hq + 2 Hkv) D][Hq D]: query, key, value rows
+    w_o: torch.Tensor            # [Hq D][Hq D]
+    w_gate_up: torch.Tensor      # [2 inter][Hq D]: gate rows, then up rows
+    w_down: torch.Tensor         # [Hq D][inter]
+    attn_norm: torch.Tensor      # [Hq D]
+    mlp_norm: torch.Tensor       # [Hq D]
+
+
+def verify_layer_workspace_bytes(B, K, Hq, Hkv, D, Lmax, inter):
+    return int(lib.specv_verify_layer_workspace_bytes(B, K, Hq, Hkv, D, Lmax, inter))
+
+
+def verify_layer(x, weights, k_cache, v_cache, ctx_len, mask, depth, Hq, eps=1e-5, theta=10000.0, out=None,
+                 workspace=None):
+    """One target layer over the draft nodes: x[B][K+1][Hq D] bf16 -> out (same shape); the nodes'
+    rotated keys and values are written to the caches at ctx_len + node."""
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a contiguous bf16 GPU tensor (it is written in place)")
+    x = _dev(x)
+    w = weights
+    for name in ("w_qkv", "w_o", "w_gate_up", "w_down", "attn_norm", "mlp_norm"):
+        t = getattr(w, name)
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"weights.{name} must be a contiguous bf16 GPU tensor")
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bf16")
+    ctx_len, mask, depth = _dev(ctx_len, torch.int32), _dev(mask), _dev(depth, torch.int32)
+    B, n1, hd = x.shape
+    _, Hkv, Lmax, D = k_cache.shape
+    inter = w.w_down.shape[1]
+    if hd != Hq * D or k_cache.shape != (B, Hkv, Lmax, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("x must be [B][K+1][Hq D] and the caches [B][Hkv][Lmax][D]")
+    shapes = {"w_qkv": ((Hq + 2 * Hkv) * D, hd), "w_o": (hd, hd), "w_gate_up": (2 * inter, hd),
+              "w_down": (hd, inter), "attn_norm": (hd,), "mlp_norm": (hd,)}
+    for name, shp in shapes.items():
+        if tuple(getattr(w, name).shape) != shp:
+            raise ValueError(f"weights.{name} must be {shp}")
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = torch.empty((max(verify_layer_workspace_bytes(B, n1 - 1, Hq, Hkv, D, Lmax, inter), 1),),
+                                dtype=torch.uint8, device=x.device)
+    _check("specv_verify_layer", lib.specv_verify_layer(
+        _ptr(x), _ptr(w.w_qkv), _ptr(w.w_o), _ptr(w.w_gate_up), _ptr(w.w_down), _ptr(w.attn_norm),
+        _ptr(w.mlp_norm), float(eps), float(theta), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), _ptr(mask),
+        _ptr(depth), B, n1 - 1, Hq, Hkv, D, Lmax, inter, _ptr(out), _ptr(workspace), workspace.numel(),
+        _stream()))
+    return out

@@ -214,4 +214,49 @@ specv_status specv_kv_commit(void* k_cache, void* v_cache, const int32_t* ctx_le
     return hip_status(specv::launch_kv_commit(a, stream), "kv_commit");
 }
 
+size_t specv_verify_layer_workspace_bytes(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
+                                          int32_t Lmax, int32_t inter) {
+    if (B <= 0 || K < 0 || K + 1 > SPECV_MAX_NODES || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 ||
+        (D != 64 && D != 128) || Lmax < K + 1 || inter <= 0 || inter % 64 != 0)
+        return 0;
+    return specv::layer_workspace_bytes(B, K + 1, Hq, Hkv, D, Lmax, inter);
+}
+
+specv_status specv_verify_layer(const void* x, const void* w_qkv, const void* w_o, const void* w_gate_up,
+                                const void* w_down, const void* attn_norm, const void* mlp_norm,
+                                float rms_eps, float rope_theta, void* k_cache, void* v_cache,
+                                const int32_t* ctx_len, const uint32_t* mask, const int32_t* depth,
+                                int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D, int32_t Lmax,
+                                int32_t inter, void* out, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+    if (B < 0) return fail(SPECV_ERR_INVALID_ARG, "B = %d < 0", B);
+    if (K < 0 || K + 1 > SPECV_MAX_NODES)
+        return fail(SPECV_ERR_INVALID_ARG, "K = %d outside [0, %d]", K, SPECV_MAX_NODES - 1);
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+        return fail(SPECV_ERR_INVALID_ARG, "Hq = %d, Hkv = %d: need Hq a positive multiple of Hkv", Hq, Hkv);
+    if (Lmax < K + 1) return fail(SPECV_ERR_INVALID_ARG, "Lmax = %d < K + 1 = %d", Lmax, K + 1);
+    if (inter <= 0 || inter % 64 != 0)
+        return fail(SPECV_ERR_INVALID_ARG, "inter = %d is not a positive multiple of 64", inter);
+    if (!(std::isfinite(rms_eps) && rms_eps > 0.f)) return fail(SPECV_ERR_INVALID_ARG, "rms_eps must be > 0");
+    if (!(std::isfinite(rope_theta) && rope_theta > 1.f))
+        return fail(SPECV_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
+    if (D != 64 && D != 128) return fail(SPECV_ERR_UNSUPPORTED, "head size D = %d not in {64, 128}", D);
+    if (B == 0) return ok();
+    const void* ptrs[] = {x, w_qkv, w_o, w_gate_up, w_down, attn_norm, mlp_norm, k_cache, v_cache, out};
+    for (const void* p : ptrs) {
+        if (!p) return fail(SPECV_ERR_INVALID_ARG, "NULL pointer argument");
+        if (reinterpret_cast<uintptr_t>(p) & 15)
+            return fail(SPECV_ERR_INVALID_ARG, "weights, activations and caches must be 16-byte aligned");
+    }
+    if (!ctx_len || !mask || !depth) return fail(SPECV_ERR_INVALID_ARG, "NULL pointer argument");
+    const size_t need = specv::layer_workspace_bytes(B, K + 1, Hq, Hkv, D, Lmax, inter);
+    if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255))
+        return fail(SPECV_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", need,
+                    workspace_bytes);
+    specv::LayerArgs a{x, w_qkv, w_o, w_gate_up, w_down, attn_norm, mlp_norm, rms_eps, rope_theta,
+                       k_cache, v_cache, ctx_len, mask, depth, B, K + 1, Hq, Hkv, D, Lmax, inter, out,
+                       workspace};
+    return hip_status(specv::launch_verify_layer(a, stream), "verify_layer");
+}
+
 }  // extern "C"

@@ -101,6 +101,29 @@ struct AttnArgs {
 size_t attn_workspace_bytes(int B, int n1, int Hq, int Hkv, int D, int Lmax);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
 
+// ------------------------------------------------------------------------------------ verify layer
+struct LayerArgs {
+    const void* x;             // [B n1][Hq D] bf16
+    const void* w_qkv;         // [(Hq + 2 Hkv) D][Hq D]
+    const void* w_o;           // [Hq D][Hq D]
+    const void* w_gate_up;     // [2 inter][Hq D]
+    const void* w_down;        // [Hq D][inter]
+    const void* attn_norm;     // [Hq D]
+    const void* mlp_norm;      // [Hq D]
+    float eps, theta;
+    void* k_cache;
+    void* v_cache;
+    const int32_t* ctx_len;
+    const uint32_t* mask;
+    const int32_t* depth;
+    int B, n1, Hq, Hkv, D, Lmax, inter;
+    void* out;
+    void* workspace;
+};
+
+size_t layer_workspace_bytes(int B, int n1, int Hq, int Hkv, int D, int Lmax, int inter);
+hipError_t launch_verify_layer(const LayerArgs& a, hipStream_t stream);
+
 // the three paths behind launch_attention
 size_t attn_tree_workspace_bytes(int B, int n1, int Hq, int Hkv, int D, int Lmax);
 hipError_t launch_attn_tree(const AttnArgs& a, hipStream_t stream);

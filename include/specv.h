@@ -16,7 +16,10 @@
  *   specv_tree_expand       one level of draft-tree construction (top-k
  *                           children kept by cumulative draft probability);
  *   specv_kv_commit         keep the accepted path's KV-cache rows, drop the
- *                           rejected branches'.
+ *                           rejected branches';
+ *   specv_verify_layer      one whole target-model layer over the draft nodes
+ *                           (projections, rotary encoding at the tree
+ *                           positions, the tree attention above, gated MLP).
  *
  * Sources (web pages on speculative decoding):
  *   [SD-review] paper review of Leviathan, Kalman, Matias, "Fast Inference
@@ -327,6 +330,66 @@ specv_status specv_tree_expand(const void* draft_logits, specv_dtype dtype, cons
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 size_t specv_tree_expand_workspace_bytes(int32_t B, int32_t F);
+
+/*
+ * One target-model layer over the draft nodes (bf16).
+ *
+ * [SD-EAGLE] "Two-Model Setup" step 2: the target runs one forward pass over
+ * all K + 1 positions at once; [PTD] Method 4, "Verification": all tree nodes
+ * are verified in one pass that uses the tree mask and the matching position
+ * encoding.  The pages name no architecture; this is a pre-norm decoder layer
+ * of the common open-model shape, with T = B (K + 1) rows (b, node):
+ *   h   = x / sqrt(mean(x^2) + eps) * attn_norm
+ *   q, k, v = split(h w_qkv^T)                 (Hq, Hkv, Hkv heads of D)
+ *   q, k rotated at position ctx_len[b] + depth[b][i]: the pair (j, j + D/2)
+ *        of a head turns by pos * theta^(-2j/D)
+ *   k, v written to the caches at ctx_len[b] + i
+ *   a   = specv_tree_attn_verify(q, caches, ctx_len, mask)   (scale 1/sqrt(D))
+ *   y   = x + a w_o^T
+ *   g, u = split(rms(y) * mlp_norm  w_gate_up^T)
+ *   out = y + (silu(g) * u) w_down^T
+ * Activations are stored in bf16 between the steps; products and norms
+ * accumulate in fp32; the rotation angle is formed in fp64.
+ *
+ *   x                [B][K+1][Hq*D] bf16 hidden states of the nodes
+ *   w_qkv            [(Hq + 2 Hkv) D][Hq D]: query rows, then key, then value
+ *   w_o              [Hq D][Hq D]
+ *   w_gate_up        [2 inter][Hq D]: gate rows, then up rows
+ *   w_down           [Hq D][inter]
+ *   attn_norm, mlp_norm  [Hq D] gains
+ *   rms_eps > 0, rope_theta > 1
+ *   k_cache, v_cache [B][Hkv][Lmax][D] bf16: context rows read, the nodes'
+ *                    rows [ctx_len, ctx_len + K + 1) written
+ *   ctx_len          [B] int32
+ *   mask, depth      from specv_build_tree_mask on the same parent array
+ *   inter            MLP width, a multiple of 64
+ *   out              [B][K+1][Hq*D] bf16; may be x itself
+ *   workspace        specv_verify_layer_workspace_bytes(...) bytes, 256-byte
+ *                    aligned
+ * A sequence with ctx_len < 0, ctx_len + K + 1 > Lmax or an invalid tree
+ * (depth -1) gets NaN outputs and its cache is not written.
+ *
+ * Ownership: device memory owned by the caller; asynchronous on `stream`;
+ * every pointer 16-byte aligned.
+ * Errors: SPECV_ERR_INVALID_ARG (NULL pointer, B < 0, K < 0,
+ * K + 1 > SPECV_MAX_NODES, Hq not a positive multiple of Hkv, Lmax < K + 1,
+ * inter not a positive multiple of 64, eps or theta out of range, misaligned
+ * pointer), SPECV_ERR_UNSUPPORTED (D not 64 or 128), SPECV_ERR_WORKSPACE,
+ * SPECV_ERR_HIP.
+ */
+specv_status specv_verify_layer(const void* x, const void* w_qkv, const void* w_o,
+                                const void* w_gate_up, const void* w_down,
+                                const void* attn_norm, const void* mlp_norm,
+                                float rms_eps, float rope_theta,
+                                void* k_cache, void* v_cache, const int32_t* ctx_len,
+                                const uint32_t* mask, const int32_t* depth,
+                                int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
+                                int32_t Lmax, int32_t inter, void* out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes of specv_verify_layer (0 for invalid sizes). */
+size_t specv_verify_layer_workspace_bytes(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
+                                          int32_t Lmax, int32_t inter);
 
 /* Static description of a status code. */
 const char* specv_status_string(specv_status s);

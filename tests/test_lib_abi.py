@@ -182,3 +182,37 @@ def test_tree_expand_host_validation(specv):
     assert call(wsb=8) == 3
     assert call(B=0) == 0
     assert specv.tree_expand_workspace_bytes(2, 4) > 0
+
+
+def test_verify_layer_host_validation(specv):
+    lib = specv.lib
+    v = ctypes.c_void_p(256)
+
+    def call(**kw):
+        a = dict(x=v, B=2, K=5, Hq=4, Hkv=2, D=64, Lmax=64, inter=128, eps=1e-5, theta=10000.0, ws=v,
+                 wsb=1 << 40)
+        a.update(kw)
+        return lib.specv_verify_layer(a["x"], v, v, v, v, v, v, a["eps"], a["theta"], v, v, v, v, v,
+                                      a["B"], a["K"], a["Hq"], a["Hkv"], a["D"], a["Lmax"], a["inter"], v,
+                                      a["ws"], a["wsb"], None)
+
+    assert call(B=-1) == 1
+    assert call(K=-1) == 1
+    assert call(K=1024) == 1
+    assert call(Hq=6, Hkv=4) == 1
+    assert call(Lmax=5) == 1
+    assert call(inter=100) == 1
+    assert call(eps=0.0) == 1
+    assert call(theta=1.0) == 1
+    assert call(theta=float("nan")) == 1
+    assert call(D=96) == 2
+    assert call(x=None) == 1
+    assert call(x=ctypes.c_void_p(264)) == 1            # misaligned
+    assert b"aligned" in lib.specv_last_error()
+    assert call(ws=None) == 3
+    assert call(wsb=16) == 3
+    assert call(ws=ctypes.c_void_p(272)) == 3           # workspace not 256-byte aligned
+    assert call(B=0) == 0
+    assert specv.verify_layer_workspace_bytes(32, 5, 32, 8, 128, 2054, 14336) > 0
+    assert specv.verify_layer_workspace_bytes(32, 5, 32, 8, 128, 2054, 100) == 0
+    assert "specv_verify_layer" in declared_functions()

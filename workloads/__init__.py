@@ -30,6 +30,9 @@ Recipes (std-dev readings of N(0, s)):
   ptd    B=4, 64-node tree grown at random under caps of 4 children and depth 8,
          V=128256 bf16, draft noise 0.6407 (alpha ~ 0.75), T=1; context 32768,
          64/8 heads.
+  layer  the chain verify as one target layer: hidden 4096 (32/8 heads of 128),
+         MLP width 14336, random-init bf16 weights N(0, 1/fan_in), norm gains
+         1 + N(0, 0.2), hidden states N(0, 1); context 2048.
 """
 
 from dataclasses import dataclass, field
@@ -229,6 +232,47 @@ def make_attention(name, parent, ctx_len, Hq, Hkv, D, dtype, seed_base, extra_sl
     return AttnInputs(name, q, k, v, ctx_len, np.ascontiguousarray(parent, dtype=np.int32), dtype)
 
 
+@dataclass
+class LayerInputs:
+    name: str
+    x: np.ndarray                  # [B][N1][Hq D] float32 (bf16 values)
+    w_qkv: np.ndarray              # [(Hq + 2 Hkv) D][Hq D]
+    w_o: np.ndarray                # [Hq D][Hq D]
+    w_gate_up: np.ndarray          # [2 inter][Hq D]
+    w_down: np.ndarray             # [Hq D][inter]
+    attn_norm: np.ndarray          # [Hq D]
+    mlp_norm: np.ndarray           # [Hq D]
+    k_cache: np.ndarray            # [B][Hkv][Lmax][D]
+    v_cache: np.ndarray
+    ctx_len: np.ndarray            # [B] int32
+    parent: np.ndarray             # [B][N1] int32
+    Hq: int
+    Hkv: int
+
+
+def make_layer(name, parent, ctx_len, Hq, Hkv, D, inter, seed_base, extra_slack=0):
+    """Random-init weights of a pre-norm decoder layer: projections ~ N(0, 1/fan_in), norm gains
+    1 + N(0, 0.2); hidden states and cache entries ~ N(0, 1); all rounded to bf16."""
+    ss = np.random.SeedSequence(seed_base)
+    rs = [np.random.default_rng(s) for s in ss.spawn(9)]
+    B, n1 = parent.shape
+    hd = Hq * D
+    ctx_len = np.asarray(ctx_len, dtype=np.int32)
+    lmax = int(ctx_len.max()) + n1 + extra_slack
+
+    def lin(r, rows, cols):
+        return round_bf16(r.standard_normal((rows, cols), dtype=np.float32) / np.float32(math.sqrt(cols)))
+
+    return LayerInputs(
+        name, round_bf16(rs[0].standard_normal((B, n1, hd), dtype=np.float32)),
+        lin(rs[1], (Hq + 2 * Hkv) * D, hd), lin(rs[2], hd, hd), lin(rs[3], 2 * inter, hd), lin(rs[4], hd, inter),
+        round_bf16(1 + 0.2 * rs[5].standard_normal(hd, dtype=np.float32)),
+        round_bf16(1 + 0.2 * rs[6].standard_normal(hd, dtype=np.float32)),
+        round_bf16(rs[7].standard_normal((B, Hkv, lmax, D), dtype=np.float32)),
+        round_bf16(rs[8].standard_normal((B, Hkv, lmax, D), dtype=np.float32)),
+        ctx_len, np.ascontiguousarray(parent, dtype=np.int32), Hq, Hkv)
+
+
 # ----------------------------------------------------------------------------- the configurations
 
 SIGMA_CHAIN = 0.5285   # alpha ~ 0.80 at V=32000, N(0,3), T=1 (workloads/tune_sigma.py)
@@ -273,6 +317,12 @@ def chain_config(T=1.0, seed_base=2000):
 
 def chain_attention(seed_base=2001, B=32):
     return make_attention("chain-attn", chain_parent(B, 5), [2048] * B, 32, 8, 128, "bf16", seed_base)
+
+
+def chain_layer(seed_base=2002, B=32, inter=14336):
+    """The chain verify as one layer of a 4096-wide model: 32/8 heads of 128 (the attention
+    shape above), MLP width 14336 (the common open-model size at that width)."""
+    return make_layer("chain-layer", chain_parent(B, 5), [2048] * B, 32, 8, 128, inter, seed_base)
 
 
 def eagle_tree(rng, draft_rows_fn, T, n_keep=60, branch=3, max_depth=6):
