@@ -60,8 +60,8 @@ ATTN_TRAFFIC = {
                 "draft_verify_sampling_specv_amd/csrc/attn_common.h",
                 "draft_verify_sampling_specv_amd/csrc/common.h",
                 "draft_verify_sampling_specv_amd/csrc/kernels.h"],
-    "sha256": "d203da3aa7222441216328ff801a8ddc0de040f9a8667abeea591ae3c271e9de",
-    "fetch_kib": 132442.5, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131084.0, "write_scale": 1.0,
+    "sha256": "a2dac72e04e760332d810f258a750dad4ac07ec39c475ea52030987636234508",
+    "fetch_kib": 132440.1, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131084.0, "write_scale": 1.0,
 }
 
 

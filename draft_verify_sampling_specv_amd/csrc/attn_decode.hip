@@ -10,10 +10,12 @@ namespace {
 using namespace attn;
 
 // ------------------------------------------------------------------------------------------
-// Decode-shaped case (at most two 32-row blocks per KV head, e.g. chains with small G): the
-// workgroup owns RBW row blocks of one (sequence, KV head) -- the launch uses RBW = 1, so a KV
-// head with two row blocks gets two workgroups, placed on one XCD so that the second one's K/V
-// reads hit that XCD's L2; its KS waves split the key tiles round-robin, each wave computing the
+// Decode-shaped case (at most two 32-row blocks per KV head, e.g. chains with small G): one
+// workgroup owns all RBW row blocks of one (sequence, KV head), so every K/V byte is read into one
+// CU once (eight waves for one block; four waves holding both blocks' accumulators, a wave per
+// SIMD, for two -- measured on the low-acceptance chain shape, 45 rows per KV head: 68 us against
+// 80 us for a workgroup per block sharing the stream through L2, or for two groups of four waves
+// reading each tile twice); its KS waves split the key tiles round-robin, each wave computing the
 // workgroup's row blocks for its tiles, and the waves' partial softmax states are merged through
 // LDS at the end (one round: scaled states published, each wave sums and stores one slice), so the
 // final output is written directly (no partials in HBM).
@@ -93,25 +95,36 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         const uint32_t w0 = mrow[0], w1 = mrow[words > 1 ? 1 : 0];
         mbits[j] = w0 | (words > 1 ? static_cast<uint64_t>(w1) << 32 : 0ull);
     }
-    // Q^T operand entries (j, s, lane) = Q[row j*32 + col][16 s + 8 h .. +8]: one per thread
-    static_assert(RBW * kKS * kWave <= KS * kWave, "one Q^T entry per thread");
-    const int qe = threadIdx.x;
-    const bool qown = qe < RBW * kKS * kWave;
-    const int qj = qe / (kKS * kWave), qs = (qe / kWave) % kKS, qln = qe % kWave;
-    const int qrow = (grp * RBW + qj) * 32 + qln % 32;
-    const int qrc = min(qrow, R - 1);
-    const int qnode = qrc / G, qg = qrc - qnode * G;
+    // Q^T operand entries (j, s, lane) = Q[row j*32 + col][16 s + 8 h .. +8], kQPer per thread
+    constexpr int kQE = RBW * kKS * kWave;
+    constexpr int kQPer = (kQE + KS * kWave - 1) / (KS * kWave);
+    uint64_t q0[kQPer], q1[kQPer];
     // (relaxed atomic loads: the compiler keeps them ahead of the K loads, which it would
     // otherwise be free to issue first, turning the wait for Q into a wait for K)
-    const uint64_t* qp = reinterpret_cast<const uint64_t*>(
-        q + ((static_cast<int64_t>(b) * n1 + qnode) * Hq + kv * G + qg) * D + 16 * qs + 8 * (qln / 32));
-    const uint64_t q0 = __hip_atomic_load(qp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    const uint64_t q1 = __hip_atomic_load(qp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+    for (int i = 0; i < kQPer; ++i) {
+        const int qe = min(static_cast<int>(threadIdx.x) + i * KS * kWave, kQE - 1);
+        const int qj = qe / (kKS * kWave), qs = (qe / kWave) % kKS, qln = qe % kWave;
+        const int qrc = min((grp * RBW + qj) * 32 + qln % 32, R - 1);
+        const int qnode = qrc / G, qg = qrc - qnode * G;
+        const uint64_t* qp = reinterpret_cast<const uint64_t*>(
+            q + ((static_cast<int64_t>(b) * n1 + qnode) * Hq + kv * G + qg) * D + 16 * qs + 8 * (qln / 32));
+        q0[i] = __hip_atomic_load(qp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        q1[i] = __hip_atomic_load(qp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
     asm volatile("" ::: "memory");
     load_k(min(w, max(ntiles - 1, 0)));
-    const uint4 qv = make_uint4(static_cast<uint32_t>(q0), static_cast<uint32_t>(q0 >> 32),
-                                static_cast<uint32_t>(q1), static_cast<uint32_t>(q1 >> 32));
-    if (qown) sq[qj][qs][qln] = qrow < R ? qv : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kQPer; ++i) {
+        const int qe = static_cast<int>(threadIdx.x) + i * KS * kWave;
+        if (qe < kQE) {
+            const int qj = qe / (kKS * kWave), qs = (qe / kWave) % kKS, qln = qe % kWave;
+            const int qrow = (grp * RBW + qj) * 32 + qln % 32;
+            const uint4 qv = make_uint4(static_cast<uint32_t>(q0[i]), static_cast<uint32_t>(q0[i] >> 32),
+                                        static_cast<uint32_t>(q1[i]), static_cast<uint32_t>(q1[i] >> 32));
+            sq[qj][qs][qln] = qrow < R ? qv : make_uint4(0, 0, 0, 0);
+        }
+    }
     // LDS-only barrier: the K tile stays in flight
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
@@ -290,11 +303,16 @@ void launch_decode(const AttnArgs& a, int ngroups, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t stream) {
-    // one row block: one workgroup per (sequence, KV head); two: one workgroup per row block (the
-    // pair shares the K/V stream through L2), which keeps each wave to one block's accumulators
+    // one workgroup per (sequence, KV head), so every K/V byte enters one CU: one row block with
+    // eight waves, two row blocks with four waves of both blocks' accumulators (a wave per SIMD)
     const int RB = ((a.Hq / a.Hkv) * a.n1 + 31) / 32;
-    if (a.D == 64) launch_decode<64, 8, 1>(a, RB, stream);
-    else launch_decode<128, 8, 1>(a, RB, stream);
+    if (RB == 1) {
+        if (a.D == 64) launch_decode<64, 8, 1>(a, 1, stream);
+        else launch_decode<128, 8, 1>(a, 1, stream);
+    } else {
+        if (a.D == 64) launch_decode<64, 4, 2>(a, 1, stream);
+        else launch_decode<128, 4, 2>(a, 1, stream);
+    }
     return hipGetLastError();
 }
 
