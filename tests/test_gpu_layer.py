@@ -91,13 +91,17 @@ def _compare(li, gpu, ora, name, rows=None):
     (3, 7, 3, 1, 64, 320, 90),
     (2, 13, 4, 2, 128, 256, 70),
     (40, 7, 4, 2, 64, 128, 40),
-    # a tree on the MFMA tree-attention path (G n1 = 80 rows per KV head)
+    # a tree on the MFMA tree-attention path (G n1 = 80 rows per KV head), with D = 128 and 64
     (2, 40, 4, 2, 128, 192, 150),
+    (2, 37, 4, 2, 64, 128, 120),
+    # the root alone (K = 0), and plain multi-head attention (Hq = Hkv)
+    (5, 1, 4, 2, 64, 128, 30),
+    (3, 9, 4, 4, 64, 192, 50),
 ])
 def test_layer_random_trees(shape):
     B, n1, Hq, Hkv, D, inter, ctx = shape
     rng = np.random.default_rng(hash(shape) % 2**32)
-    parent = np.stack([workloads.random_tree(rng, n1 - 1, 3, 6) for _ in range(B)])
+    parent = np.stack([workloads.random_tree(rng, n1 - 1, 3, 6) for _ in range(B)]).reshape(B, n1)
     parent[0] = np.arange(-1, n1 - 1)                     # one chain
     ctxs = rng.integers(ctx // 2, ctx + 1, size=B)
     li = workloads.make_layer("layer", parent, ctxs, Hq, Hkv, D, inter, seed_base=int(rng.integers(1 << 30)),
