@@ -504,28 +504,42 @@ def measure_config(name, args, torch, specv, workloads):
 
 def cpu_baseline(w, a):
     """Oracle (numpy fp64) on a bounded sample of the same workload: the whole verify step
-    (mask, attention, accept) for as many sequences as fit in about 15 s."""
-    from threadpoolctl import threadpool_info
+    (mask, attention, accept) for as many sequences as fit in about 15 s on all the host threads
+    numpy uses, then about 5 s on one thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import accept as o_accept, attention as o_attn, philox as o_philox, tree as o_tree
 
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    t0 = time.time()
-    done = 0
-    while time.time() - t0 < 15.0:
-        b = done % w.B
-        mask, _, _ = o_tree.build_tree_mask_batch(a.parent[b:b + 1])
-        o_attn.tree_attention(a.q[b:b + 1], a.k_cache[b:b + 1], a.v_cache[b:b + 1], a.ctx_len[b:b + 1], mask,
-                              a.scale)
-        ua, ur = o_philox.uniforms(1234, 0, 1, w.N1)
-        o_accept.accept_batch(np.asarray(w.target_logits[b:b + 1], np.float64),
-                              np.asarray(w.draft_logits[b:b + 1], np.float64),
-                              w.tokens[b:b + 1], w.parent[b:b + 1], w.T, ua, ur)
-        done += 1
-    dt = time.time() - t0
+
+    def run(seconds):
+        t0 = time.time()
+        done = 0
+        while time.time() - t0 < seconds:
+            b = done % w.B
+            mask, _, _ = o_tree.build_tree_mask_batch(a.parent[b:b + 1])
+            o_attn.tree_attention(a.q[b:b + 1], a.k_cache[b:b + 1], a.v_cache[b:b + 1], a.ctx_len[b:b + 1], mask,
+                                  a.scale)
+            ua, ur = o_philox.uniforms(1234, 0, 1, w.N1)
+            o_accept.accept_batch(np.asarray(w.target_logits[b:b + 1], np.float64),
+                                  np.asarray(w.draft_logits[b:b + 1], np.float64),
+                                  w.tokens[b:b + 1], w.parent[b:b + 1], w.T, ua, ur)
+            done += 1
+        return done, time.time() - t0
+
+    done, dt = run(15.0)
+    with threadpool_limits(limits=1):
+        done1, dt1 = run(5.0)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": done * K / dt, "unit": "positions/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} sequences (cycling over the {w.B} of the timed workload), whole verify "
-                      f"step (mask, attention, accept) in numpy fp64, {dt:.1f} s"}
+                      f"step (mask, attention, accept) in numpy fp64, {dt:.1f} s",
+            "value_one_thread": done1 * K / dt1, "cpu_model": model}
 
 
 if __name__ == "__main__":
