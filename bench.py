@@ -123,7 +123,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the verify step shards by sequence and KV head with no exchange; see DESIGN.md)",
+              "(the verify step shards by sequence and KV head with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 
