@@ -134,3 +134,25 @@ def test_layer_chain_workload_sampled_rows():
     log(f"verify_layer: chain workload B={B} N1={n1} hidden 4096 inter 14336, {len(rows)} sampled rows")
     gpu = _run_gpu(li)
     _compare(li, gpu, _oracle(li, rows=rows), "chain layer", rows=rows)
+
+
+def test_layer_output_may_overwrite_its_input():
+    # out == x: the input is last read before the final residual product, so the result is the same
+    specv = _specv()
+    rng = np.random.default_rng(12)
+    B, n1 = 3, 7
+    parent = np.stack([workloads.random_tree(rng, n1 - 1, 3, 4) for _ in range(B)])
+    li = workloads.make_layer("layer-inplace", parent, [40, 50, 60], 4, 2, 64, 192, seed_base=21)
+    w = specv.LayerWeights(_bf(li.w_qkv), _bf(li.w_o), _bf(li.w_gate_up), _bf(li.w_down), _bf(li.attn_norm),
+                           _bf(li.mlp_norm))
+    mask, depth, _ = specv.build_tree_mask(torch.from_numpy(parent).cuda())
+    ctx = torch.from_numpy(li.ctx_len).cuda()
+    outs = []
+    for inplace in (False, True):
+        kc, vc = _bf(li.k_cache), _bf(li.v_cache)
+        x = _bf(li.x)
+        out = specv.verify_layer(x, w, kc, vc, ctx, mask, depth, li.Hq, out=x if inplace else None)
+        torch.cuda.synchronize()
+        outs.append(out.float().cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+    log("verify_layer: in-place output matches")
