@@ -58,10 +58,6 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int h = lane / 32, col = lane % 32;
     const int words = (n1 + 31) >> 5;
-    const int L = ctx_len[b];
-    const bool seq_ok = L >= 0 && L + n1 <= Lmax;
-    const int Ltot = L + n1;
-    const int ntiles = seq_ok ? (Ltot + kTileKeys - 1) / kTileKeys : 0;
 
     const uint16_t* kbase = kc + (static_cast<int64_t>(b) * Hkv + kv) * Lmax * D;
     const uint16_t* vbase = vc + (static_cast<int64_t>(b) * Hkv + kv) * Lmax * D;
@@ -70,10 +66,14 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     // masked out by the softmax; key 0 for an invalid sequence, whose output is NaN anyway).
     // With no register loaded under a branch, the compiler's load counting stays exact, so a
     // wait for one load is not a wait for the loads issued after it.
-    const int kmax = seq_ok ? Ltot - 1 : 0;
+    // The wave's first K tile is the exception: it is clamped to the cache's last row instead, so
+    // that its loads need not wait for ctx_len.  Keys it reads past the sequence hold arbitrary
+    // cache contents, but K only enters the scores, and the scores of those keys are replaced by
+    // -inf with a select before any arithmetic uses them (V, which is multiplied by p = 0, is
+    // always clamped to a real key).
     uint4 kn[kKS];
-    auto load_k = [&](int t) {
-        const int kkey = min(t * kTileKeys + col, kmax);
+    auto load_k = [&](int t, int kclamp) {
+        const int kkey = min(t * kTileKeys + col, kclamp);
 #pragma unroll
         for (int s2 = 0; s2 < kKS; ++s2)
             kn[s2] = *reinterpret_cast<const uint4*>(kbase + static_cast<int64_t>(kkey) * D + 16 * s2 + 8 * h);
@@ -83,6 +83,10 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     // stream starts before the Q operands are staged (the staging waits only for the Q word).
     // The mask row stays in registers: the decode shape has at most 64 rows per KV head, so at
     // most 64 nodes and two mask words.
+    // ctx_len first, as a vector load: read as a scalar load it would be waited for together with
+    // the kernel arguments, before any of the loads below were issued; issued first, waiting for
+    // it leaves the loads after it in flight
+    const int L0 = __hip_atomic_load(ctx_len + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     int rows[RBW];
     bool rok[RBW];
     uint64_t mbits[RBW];
@@ -113,7 +117,12 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         q1[i] = __hip_atomic_load(qp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     asm volatile("" ::: "memory");
-    load_k(min(w, max(ntiles - 1, 0)));
+    load_k(w, Lmax - 1);
+    const int L = __builtin_amdgcn_readfirstlane(L0);
+    const bool seq_ok = L >= 0 && L + n1 <= Lmax;
+    const int Ltot = L + n1;
+    const int ntiles = seq_ok ? (Ltot + kTileKeys - 1) / kTileKeys : 0;
+    const int kmax = seq_ok ? Ltot - 1 : 0;
 #pragma unroll
     for (int i = 0; i < kQPer; ++i) {
         const int qe = static_cast<int>(threadIdx.x) + i * KS * kWave;
@@ -154,7 +163,7 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                 for (int dh = 0; dh < kDH; ++dh)
                     vr[ks][dh][e] = *reinterpret_cast<const uint32_t*>(vbase + static_cast<int64_t>(key) * D + 64 * dh + 2 * col);
             }
-        load_k(min(t + KS, ntiles - 1));
+        load_k(min(t + KS, ntiles - 1), kmax);
 
         bf16x8_t pb[RBW][2];
 #pragma unroll

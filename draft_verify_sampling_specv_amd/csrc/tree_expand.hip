@@ -62,12 +62,37 @@ __device__ __forceinline__ bool better(float v, int i, float v2, int i2) {
     return v > v2 || (v == v2 && i < i2);
 }
 
+// Maximum over the wave through DPP: rows of 16 lanes reduce with quad permutations and row
+// rotations (every lane of a row ends with the row's maximum), then the four row maxima are read
+// as scalars.  Unlike a shuffle through the LDS crossbar, no step waits on a memory counter.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    auto step = [](float x, int ctrl_sel) {
+        int y;
+        switch (ctrl_sel) {       // (the control must be a constant)
+            case 0: y = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false); break;   // quad_perm 1,0,3,2
+            case 1: y = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false); break;   // quad_perm 2,3,0,1
+            case 2: y = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, false); break;  // row_ror 4
+            default: y = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false); break; // row_ror 8
+        }
+        return fmaxf(x, __int_as_float(y));
+    };
+    v = step(v, 0);
+    v = step(v, 1);
+    v = step(v, 2);
+    v = step(v, 3);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 // The kk-th largest of v over the wave (counting repeats): kk rounds, each removing the largest
 // (one lane at a time).
 __device__ __forceinline__ float wave_kth_largest(float v, int kk, int lane) {
     float cur = -INFINITY;
     for (int r = 0; r < kk; ++r) {
-        cur = wave_max(v);
+        cur = wave_max_dpp(v);
         const uint64_t at = __ballot(v == cur);
         if (at && lane == __ffsll(static_cast<unsigned long long>(at)) - 1) v = -INFINITY;
     }
@@ -86,14 +111,32 @@ expand_topk_kernel(const T* __restrict__ logits, const int32_t* __restrict__ fro
     __shared__ float wm[kTopWaves], ws[kTopWaves];
     const int row = blockIdx.x, b = row / F;
     const int t = threadIdx.x, lane = t % kWave, w = t / kWave;
-    const int u = frontier[row], n = n_nodes[b];
     RowTop* out = rows + row;
+    const T* z = logits + static_cast<int64_t>(row) * V;
+    const int kk = min(k, V);
+    constexpr int kStep = kTopThreads * kVec;
+    constexpr int kBatchElems = kBatch * kStep;
+    const bool vec = (V % kVec) == 0 && (reinterpret_cast<uintptr_t>(z) & 15) == 0;
+    // batches whose vectors all lie inside the row: loaded unconditionally, no bounds selects
+    const int nfull = vec ? V / kBatchElems : 0;
+    uint4 r[kBatch];
+    auto load_full = [&](int b0) {
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) r[q] = *reinterpret_cast<const uint4*>(z + b0 + q * kStep + t * kVec);
+    };
+    // the first full batch is requested before the frontier entry and the node count, so that
+    // their round trip overlaps it (a row that is no node has then loaded it for nothing; it lies
+    // inside the logits either way).  Those two are vector loads issued after it: read as scalar
+    // loads they would be waited for before anything else is issued.
+    if (nfull > 0) load_full(0);
+    const int u = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(frontier + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+    const int n = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(n_nodes + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
     if (!(u >= 0 && u < min(n, nmax))) { // (workgroup-uniform) not a node: no row
         if (t == 0) out->count = 0;
         return;
     }
-    const T* z = logits + static_cast<int64_t>(row) * V;
-    const int kk = min(k, V);
 
     // per-thread list of the K best entered elements, sorted (value desc, index asc); this
     // thread's elements come in increasing index order, so a strictly larger value is needed to
@@ -120,13 +163,54 @@ expand_topk_kernel(const T* __restrict__ logits, const int32_t* __restrict__ fro
             ci = go ? oi : ci;
         }
     };
-    // batches of kBatch vectors per thread: loads first, then the values (elements past V are -inf)
-    constexpr int kStep = kTopThreads * kVec;
-    const bool vec = (V % kVec) == 0 && (reinterpret_cast<uintptr_t>(z) & 15) == 0;
-    for (int b0 = 0; b0 < V; b0 += kBatch * kStep) {
+    // one batch of kBatch vectors per thread: the online log-sum-exp, the wave-wide entry bound,
+    // and the insertions.  tail: the batch may reach past V (its elements there are -inf).
+    auto process = [&](int b0, float (&x)[kBatch][kVec], bool tail) {
+        float vm[kBatch];
+        float bmax = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            vm[q] = x[q][0];
+#pragma unroll
+            for (int e = 1; e < kVec; ++e) vm[q] = fmaxf(vm[q], x[q][e]);
+            // online log-sum-exp, one rescale per vector
+            const float mn = fmaxf(m, vm[q]);
+            const float ref = (mn == -INFINITY) ? 0.f : mn;
+            float add = 0.f;
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) add += __builtin_amdgcn_exp2f((x[q][e] - ref) * kexp2);
+            s = s * __builtin_amdgcn_exp2f((m - ref) * kexp2) + add;
+            m = mn;
+            bmax = fmaxf(bmax, vm[q]);
+        }
+        // wave-wide entry bound: the kk-th largest of the lanes' batch maxima -- kk elements at
+        // or above it exist, so anything below it cannot be in the wave's top-k (equal values may
+        // still be, on index); it only grows.  A vector is scanned only if its maximum reaches it.
+        wthr = fmaxf(wthr, wave_kth_largest(bmax, kk, lane));
+        if (bmax >= wthr) {
+            const float thr = tv[K - 1];          // -inf while the list is not full
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q)
+                if (vm[q] >= wthr) {
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) {
+                        const int i = b0 + q * kStep + t * kVec + e;
+                        if ((!tail || i < V) && x[q][e] >= wthr && (held < K || x[q][e] > thr)) insert(x[q][e], i);
+                    }
+                }
+        }
+    };
+    for (int bi = 0; bi < nfull; ++bi) {
+        if (bi > 0) load_full(bi * kBatchElems);
+        float x[kBatch][kVec];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) unpack16<T>(r[q], x[q]);
+        process(bi * kBatchElems, x, false);
+    }
+    // the rest of the row (and every batch of a row without 16-byte vectors): bounds-checked
+    for (int b0 = nfull * kBatchElems; b0 < V; b0 += kBatchElems) {
         float x[kBatch][kVec];
         if (vec) {
-            uint4 r[kBatch];
 #pragma unroll
             for (int q = 0; q < kBatch; ++q) {
                 const int base = b0 + q * kStep + t * kVec;
@@ -150,36 +234,7 @@ expand_topk_kernel(const T* __restrict__ logits, const int32_t* __restrict__ fro
                     x[q][e] = i < V ? Elem<T>::load(z, i) : -INFINITY;
                 }
         }
-        float bmax = -INFINITY;
-#pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
-            float vm = x[q][0];
-#pragma unroll
-            for (int e = 1; e < kVec; ++e) vm = fmaxf(vm, x[q][e]);
-            // online log-sum-exp, one rescale per vector
-            const float mn = fmaxf(m, vm);
-            const float ref = (mn == -INFINITY) ? 0.f : mn;
-            float add = 0.f;
-#pragma unroll
-            for (int e = 0; e < kVec; ++e) add += __builtin_amdgcn_exp2f((x[q][e] - ref) * kexp2);
-            s = s * __builtin_amdgcn_exp2f((m - ref) * kexp2) + add;
-            m = mn;
-            bmax = fmaxf(bmax, vm);
-        }
-        // wave-wide entry bound: the kk-th largest of the lanes' batch maxima -- kk elements at
-        // or above it exist, so anything below it cannot be in the wave's top-k (equal values may
-        // still be, on index); it only grows
-        wthr = fmaxf(wthr, wave_kth_largest(bmax, kk, lane));
-        if (bmax >= wthr) {
-            const float thr = tv[K - 1];          // -inf while the list is not full
-#pragma unroll
-            for (int q = 0; q < kBatch; ++q)
-#pragma unroll
-                for (int e = 0; e < kVec; ++e) {
-                    const int i = b0 + q * kStep + t * kVec + e;
-                    if (i < V && x[q][e] >= wthr && (held < K || x[q][e] > thr)) insert(x[q][e], i);
-                }
-        }
+        process(b0, x, true);
     }
 
     // per wave: kk rounds, each taking the best head of the lanes' sorted lists (the winning lane
