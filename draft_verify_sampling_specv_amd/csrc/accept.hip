@@ -367,7 +367,7 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
         const int xa0 = __hip_atomic_load(tokens + seq + min(t, n1 - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         asm volatile("" ::: "memory");
         uint4 r[kWaveLoads];
-        const int it0 = rank * kWaves + wu;
+        const int it0 = rank + wu * P;
         const bool pre = kPre && it0 < n1 * nchunk;       // wave-uniform
         if constexpr (kPre) {
             // issued by every wave (branch-free, so the compiler's count of outstanding loads
@@ -500,13 +500,14 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
         const int ni = (kGreedy || rule == kRuleDeterministic) ? 0 : s_ni;     // draft rows read
 
         // -- C. chunk statistics: one wave per item.  Workgroup `rank` of the team owns items
-        //    rank * kWaves + j + m * P * kWaves (j < kWaves); its waves take them in that order
-        //    from a workgroup counter in LDS as they finish, since the two waves sharing a SIMD do
-        //    not progress at the same rate (the older one is favoured at issue), which a fixed
-        //    split would turn into idle waves at the end of the phase
+        //    rank + m * P (dealt one at a time, so the workgroups' counts differ by at most one);
+        //    its waves take them in that order from a workgroup counter in LDS as they finish,
+        //    since the two waves sharing a SIMD do not progress at the same rate (the older one is
+        //    favoured at issue), which a fixed split would turn into idle waves at the end of the
+        //    phase
         const int nitems = (n1 + ni) * nchunk;
         for (int kk = wu;;) {     // (wave-uniform)
-            const int it = rank * kWaves + (kk % kWaves) + (kk / kWaves) * (P * kWaves);
+            const int it = rank + kk * P;
             if (it >= nitems) break;
             int nk = 0;
             if (lane == 0) nk = atomicAdd(&s_next, 1);
