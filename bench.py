@@ -61,7 +61,7 @@ ATTN_TRAFFIC = {
                 "draft_verify_sampling_specv_amd/csrc/common.h",
                 "draft_verify_sampling_specv_amd/csrc/kernels.h"],
     "sha256": "96874cbf6e4baf38366ddaa35773e398801dff37bb4f2d359c9b0824e053f94d",
-    "fetch_kib": 132447.1, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131084.0, "write_scale": 1.0,
+    "fetch_kib": 132448.5, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131084.0, "write_scale": 1.0,
 }
 
 
