@@ -259,36 +259,79 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* p, const float* f) {
     *reinterpret_cast<uint2*>(p) = make_uint2(attn::pack_bf16x2(f[0], f[1]), attn::pack_bf16x2(f[2], f[3]));
 }
 
-// h[t] = rms(x[t]) g  (one workgroup per row, four columns per thread and pass)
-__global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const uint16_t* __restrict__ x,
-                                                           const uint16_t* __restrict__ g, int hd, float eps,
-                                                           uint16_t* __restrict__ h) {
-    __shared__ float red[kThreads / kWave];
+// The row-wise kernels (norms) run one 1024-thread workgroup per row and keep the first
+// 4 kNormThreads kNormPasses columns of the row in registers between the sum of squares and the
+// scaling, so the row is read once; columns past that (rows wider than 8192) are read again.
+constexpr int kNormThreads = 1024;
+constexpr int kNormPasses = 2;
+
+// bf16 rounding of v, back in fp32 (the value a bf16 store and reload would give)
+__device__ __forceinline__ float round_bf16(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+
+// h[t] = rms(x[t]) g.  Also the rotary (cos, sin) of row t's position ctx_len + depth for every
+// frequency j < D/2, with the angle formed in fp64: once per row here instead of once per head in
+// the q/k/v epilogue.
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ g, int hd, float eps,
+                                                               uint16_t* __restrict__ h, int n1, int D,
+                                                               const int32_t* __restrict__ ctx_len,
+                                                               const int32_t* __restrict__ depth, float theta,
+                                                               float2* __restrict__ rot) {
+    __shared__ float red[kNormThreads / kWave];
     const int64_t row = blockIdx.x;
     const uint16_t* xr = x + row * hd;
+    float xv[kNormPasses][4], gv[kNormPasses][4];
     float ss = 0.f;
-    for (int c = 4 * threadIdx.x; c < hd; c += 4 * kThreads) {
+#pragma unroll
+    for (int i = 0; i < kNormPasses; ++i) {
+        const int c = 4 * (threadIdx.x + i * kNormThreads);
+        if (c < hd) {
+            load_bf16x4(xr + c, xv[i]);
+            load_bf16x4(g + c, gv[i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kNormPasses; ++i)
+        if (4 * (threadIdx.x + i * kNormThreads) < hd)
+            ss += xv[i][0] * xv[i][0] + xv[i][1] * xv[i][1] + xv[i][2] * xv[i][2] + xv[i][3] * xv[i][3];
+    for (int c = 4 * (threadIdx.x + kNormPasses * kNormThreads); c < hd; c += 4 * kNormThreads) {
         float f[4];
         load_bf16x4(xr + c, f);
         ss += f[0] * f[0] + f[1] * f[1] + f[2] * f[2] + f[3] * f[3];
     }
     const float inv = 1.f / sqrtf(block_sum(ss, red) / hd + eps);
-    for (int c = 4 * threadIdx.x; c < hd; c += 4 * kThreads) {
+#pragma unroll
+    for (int i = 0; i < kNormPasses; ++i) {
+        const int c = 4 * (threadIdx.x + i * kNormThreads);
+        if (c < hd) {
+            float f[4];
+            for (int e = 0; e < 4; ++e) f[e] = xv[i][e] * inv * gv[i][e];
+            store_bf16x4(h + row * hd + c, f);
+        }
+    }
+    for (int c = 4 * (threadIdx.x + kNormPasses * kNormThreads); c < hd; c += 4 * kNormThreads) {
         float f[4], gg[4];
         load_bf16x4(xr + c, f);
         load_bf16x4(g + c, gg);
         for (int e = 0; e < 4; ++e) f[e] = f[e] * inv * gg[e];
         store_bf16x4(h + row * hd + c, f);
     }
+    const int j = threadIdx.x;
+    if (j < D / 2) {
+        const int b = static_cast<int>(row) / n1;
+        const double ang = static_cast<double>(ctx_len[b] + depth[row]) * pow(static_cast<double>(theta), -2.0 * j / D);
+        rot[row * (D / 2) + j] = make_float2(static_cast<float>(cos(ang)), static_cast<float>(sin(ang)));
+    }
 }
 
 // q/k/v of row t = m0 + blockIdx.y, head blockIdx.x (query heads, then key, then value heads),
-// one rotary pair (j, j + D/2) per thread: add the splits, rotate q and k at ctx_len + depth, write
+// one rotary pair (j, j + D/2) per thread: add the splits, rotate q and k at ctx_len + depth (the
+// (cos, sin) table of rmsnorm_kernel), write
 // q to qrot[t] and k, v to the cache at ctx_len + node.  A row of an invalid sequence (a bad tree,
 // or no room in the cache) writes NaN queries (its attention output is NaN) and nothing else.
 __global__ __launch_bounds__(64) void qkv_epilogue_kernel(
     const float* __restrict__ P, int splits, int Mc, int m0, int n1, int Hq, int Hkv, int D, int Lmax,
-    const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ depth, float theta,
+    const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ depth, const float2* __restrict__ rot,
     uint16_t* __restrict__ qrot, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc) {
     const int head = blockIdx.x, mloc = blockIdx.y, j = threadIdx.x;
     const int half = D / 2;
@@ -300,6 +343,7 @@ __global__ __launch_bounds__(64) void qkv_epilogue_kernel(
     const int N = (Hq + 2 * Hkv) * D;
     const int64_t plane = static_cast<int64_t>(Mc) * N;
     const float* pr = P + static_cast<int64_t>(mloc) * N + head * D + j;
+    const float2 cs = head < Hq + Hkv ? rot[static_cast<int64_t>(t) * half + j] : make_float2(1.f, 0.f);
     float lo = 0.f, hi = 0.f;
     {
         float va[kMaxSplits], vb[kMaxSplits];
@@ -317,9 +361,8 @@ __global__ __launch_bounds__(64) void qkv_epilogue_kernel(
             }
     }
     if (head < Hq + Hkv) {
-        // angle (ctx_len + depth) theta^(-2j/D) formed in fp64
-        const double ang = static_cast<double>(L + d) * pow(static_cast<double>(theta), -2.0 * j / D);
-        const float c = static_cast<float>(cos(ang)), sn = static_cast<float>(sin(ang));
+        // angle (ctx_len + depth) theta^(-2j/D), from the row's table
+        const float c = cs.x, sn = cs.y;
         const float a = lo;
         lo = a * c - hi * sn;
         hi = hi * c + a * sn;
@@ -336,18 +379,44 @@ __global__ __launch_bounds__(64) void qkv_epilogue_kernel(
     }
 }
 
-// y[t] = x[t] + sum of splits (stored bf16), h2[t] = rms(y[t]) g
-__global__ __launch_bounds__(kThreads) void residual_norm_kernel(const float* __restrict__ P, int splits, int Mc,
-                                                                 int m0, int hd, const uint16_t* __restrict__ x,
-                                                                 const uint16_t* __restrict__ g, float eps,
-                                                                 uint16_t* __restrict__ y, uint16_t* __restrict__ h2) {
-    __shared__ float red[kThreads / kWave];
+// y[t] = x[t] + sum of splits (stored bf16), h2[t] = rms(y[t]) g; the rounded y stays in registers
+// for the scaling (columns past the cached ones read it back)
+__global__ __launch_bounds__(kNormThreads) void residual_norm_kernel(const float* __restrict__ P, int splits, int Mc,
+                                                                     int m0, int hd, const uint16_t* __restrict__ x,
+                                                                     const uint16_t* __restrict__ g, float eps,
+                                                                     uint16_t* __restrict__ y, uint16_t* __restrict__ h2) {
+    __shared__ float red[kNormThreads / kWave];
     const int mloc = blockIdx.x;
     const int64_t t = m0 + mloc;
     const int64_t plane = static_cast<int64_t>(Mc) * hd;
     const float* pr = P + static_cast<int64_t>(mloc) * hd;
+    float yv[kNormPasses][4], gv[kNormPasses][4];
+#pragma unroll
+    for (int i = 0; i < kNormPasses; ++i) {
+        const int c = 4 * (threadIdx.x + i * kNormThreads);
+        if (c < hd) {
+            load_bf16x4(x + t * hd + c, yv[i]);
+            load_bf16x4(g + c, gv[i]);
+        }
+    }
     float ss = 0.f;
-    for (int c = 4 * threadIdx.x; c < hd; c += 4 * kThreads) {
+#pragma unroll
+    for (int i = 0; i < kNormPasses; ++i) {
+        const int c = 4 * (threadIdx.x + i * kNormThreads);
+        if (c < hd) {
+            const float4 s = split_sum4(pr, splits, plane, c);
+            yv[i][0] += s.x;
+            yv[i][1] += s.y;
+            yv[i][2] += s.z;
+            yv[i][3] += s.w;
+            store_bf16x4(y + t * hd + c, yv[i]);
+            for (int e = 0; e < 4; ++e) {
+                yv[i][e] = round_bf16(yv[i][e]);          // the stored residual stream
+                ss += yv[i][e] * yv[i][e];
+            }
+        }
+    }
+    for (int c = 4 * (threadIdx.x + kNormPasses * kNormThreads); c < hd; c += 4 * kNormThreads) {
         const float4 s = split_sum4(pr, splits, plane, c);
         float f[4];
         load_bf16x4(x + t * hd + c, f);
@@ -356,11 +425,22 @@ __global__ __launch_bounds__(kThreads) void residual_norm_kernel(const float* __
         f[2] += s.z;
         f[3] += s.w;
         store_bf16x4(y + t * hd + c, f);
-        load_bf16x4(y + t * hd + c, f);              // the stored (rounded) residual stream
-        ss += f[0] * f[0] + f[1] * f[1] + f[2] * f[2] + f[3] * f[3];
+        for (int e = 0; e < 4; ++e) {
+            f[e] = round_bf16(f[e]);
+            ss += f[e] * f[e];
+        }
     }
     const float inv = 1.f / sqrtf(block_sum(ss, red) / hd + eps);
-    for (int c = 4 * threadIdx.x; c < hd; c += 4 * kThreads) {
+#pragma unroll
+    for (int i = 0; i < kNormPasses; ++i) {
+        const int c = 4 * (threadIdx.x + i * kNormThreads);
+        if (c < hd) {
+            float f[4];
+            for (int e = 0; e < 4; ++e) f[e] = yv[i][e] * inv * gv[i][e];
+            store_bf16x4(h2 + t * hd + c, f);
+        }
+    }
+    for (int c = 4 * (threadIdx.x + kNormPasses * kNormThreads); c < hd; c += 4 * kNormThreads) {
         float f[4], gg[4];
         load_bf16x4(y + t * hd + c, f);
         load_bf16x4(g + c, gg);
@@ -448,7 +528,7 @@ struct LayerPlan {
     int T, hd, nqkv, inter;
     int chunk;                       // activation rows per product launch
     int s_qkv, s_o, s_gu, s_down;    // splits per product
-    size_t off_h, off_q, off_a, off_y, off_h2, off_act, off_p, off_attn, total;
+    size_t off_h, off_q, off_a, off_y, off_h2, off_act, off_rot, off_p, off_attn, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -472,6 +552,7 @@ LayerPlan plan_layer(int B, int n1, int Hq, int Hkv, int D, int Lmax, int inter)
     p.off_y = o;   o += align256(T * p.hd * e);
     p.off_h2 = o;  o += align256(T * p.hd * e);
     p.off_act = o; o += align256(T * inter * e);
+    p.off_rot = o; o += align256(T * (D / 2) * sizeof(float2));
     const size_t pmax = max(max(size_t(p.s_qkv) * p.nqkv, size_t(p.s_o) * p.hd),
                             max(size_t(p.s_gu) * 2 * inter, size_t(p.s_down) * p.hd));
     p.off_p = o;   o += align256(pmax * p.chunk * sizeof(float));
@@ -494,11 +575,13 @@ hipError_t launch_verify_layer(const LayerArgs& a, hipStream_t stream) {
     uint16_t *h = bf(p.off_h), *q = bf(p.off_q), *att = bf(p.off_a), *y = bf(p.off_y), *h2 = bf(p.off_h2),
              *act = bf(p.off_act);
     float* P = reinterpret_cast<float*>(ws + p.off_p);
+    float2* rot = reinterpret_cast<float2*>(ws + p.off_rot);
     const uint16_t* x = static_cast<const uint16_t*>(a.x);
     uint16_t* out = static_cast<uint16_t*>(a.out);
     hipError_t e;
 
-    rmsnorm_kernel<<<p.T, kThreads, 0, stream>>>(x, static_cast<const uint16_t*>(a.attn_norm), p.hd, a.eps, h);
+    rmsnorm_kernel<<<p.T, kNormThreads, 0, stream>>>(x, static_cast<const uint16_t*>(a.attn_norm), p.hd, a.eps, h,
+                                                     a.n1, a.D, a.ctx_len, a.depth, a.theta, rot);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int heads = a.Hq + 2 * a.Hkv;
     for (int m0 = 0; m0 < p.T; m0 += p.chunk) {
@@ -507,7 +590,7 @@ hipError_t launch_verify_layer(const LayerArgs& a, hipStream_t stream) {
                              p.nqkv, p.s_qkv, P, nullptr, false, stream)) != hipSuccess)
             return e;
         qkv_epilogue_kernel<<<dim3(heads, mc), 64, 0, stream>>>(P, p.s_qkv, mc, m0, a.n1, a.Hq, a.Hkv, a.D, a.Lmax,
-                                                                a.ctx_len, a.depth, a.theta, q,
+                                                                a.ctx_len, a.depth, rot, q,
                                                                 static_cast<uint16_t*>(a.k_cache),
                                                                 static_cast<uint16_t*>(a.v_cache));
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -521,7 +604,7 @@ hipError_t launch_verify_layer(const LayerArgs& a, hipStream_t stream) {
         if ((e = launch_gemm(att + static_cast<int64_t>(m0) * p.hd, mc, p.hd, static_cast<const uint16_t*>(a.w_o),
                              p.hd, p.s_o, P, nullptr, false, stream)) != hipSuccess)
             return e;
-        residual_norm_kernel<<<mc, kThreads, 0, stream>>>(P, p.s_o, mc, m0, p.hd, x,
+        residual_norm_kernel<<<mc, kNormThreads, 0, stream>>>(P, p.s_o, mc, m0, p.hd, x,
                                                           static_cast<const uint16_t*>(a.mlp_norm), a.eps, y, h2);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
