@@ -62,24 +62,20 @@ __device__ __forceinline__ bool better(float v, int i, float v2, int i2) {
     return v > v2 || (v == v2 && i < i2);
 }
 
+// One DPP step of the wave maximum: v against the lane that the DPP control kCtrl selects.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_max_step(float v) {
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false)));
+}
+
 // Maximum over the wave through DPP: rows of 16 lanes reduce with quad permutations and row
 // rotations (every lane of a row ends with the row's maximum), then the four row maxima are read
 // as scalars.  Unlike a shuffle through the LDS crossbar, no step waits on a memory counter.
 __device__ __forceinline__ float wave_max_dpp(float v) {
-    auto step = [](float x, int ctrl_sel) {
-        int y;
-        switch (ctrl_sel) {       // (the control must be a constant)
-            case 0: y = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false); break;   // quad_perm 1,0,3,2
-            case 1: y = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false); break;   // quad_perm 2,3,0,1
-            case 2: y = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, false); break;  // row_ror 4
-            default: y = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false); break; // row_ror 8
-        }
-        return fmaxf(x, __int_as_float(y));
-    };
-    v = step(v, 0);
-    v = step(v, 1);
-    v = step(v, 2);
-    v = step(v, 3);
+    v = dpp_max_step<0xB1>(v);     // quad_perm 1,0,3,2
+    v = dpp_max_step<0x4E>(v);     // quad_perm 2,3,0,1
+    v = dpp_max_step<0x124>(v);    // row_ror 4
+    v = dpp_max_step<0x128>(v);    // row_ror 8
     const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
     const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
     const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
