@@ -62,12 +62,19 @@ typedef enum {
     SPECV_ERR_INVALID_ARG = 1,   /* NULL pointer, size out of range, bad temperature, ... */
     SPECV_ERR_UNSUPPORTED = 2,   /* a head size, dtype or size the kernels do not cover */
     SPECV_ERR_WORKSPACE = 3,     /* workspace NULL or smaller than the query returns */
-    SPECV_ERR_HIP = 4            /* a kernel launch failed; see specv_last_error() */
+    SPECV_ERR_HIP = 4,           /* a kernel launch failed; see specv_last_error() */
+    /* not statuses: they make every 32-bit value a valid value of the type, so that a value
+       outside the list (passed in from C, say) is an ordinary unknown value in C++ too */
+    SPECV_STATUS_RANGE_LOW_ = -0x7fffffff - 1,
+    SPECV_STATUS_RANGE_HIGH_ = 0x7fffffff
 } specv_status;
 
 typedef enum {
     SPECV_F32 = 0,
-    SPECV_BF16 = 1
+    SPECV_BF16 = 1,
+    /* not dtypes: every 32-bit value is a value of the type (an unknown one is rejected) */
+    SPECV_DTYPE_RANGE_LOW_ = -0x7fffffff - 1,
+    SPECV_DTYPE_RANGE_HIGH_ = 0x7fffffff
 } specv_dtype;
 
 /* Largest supported K + 1 and vocabulary size. */
@@ -226,7 +233,10 @@ typedef enum {
        with probability p'(x); after a rejection p' is p without the rejected
        tokens, renormalised, and the final draw is from it; the draft logits
        are not read (may be NULL) and q_tok is NaN */
-    SPECV_SIBLINGS_DETERMINISTIC = 2
+    SPECV_SIBLINGS_DETERMINISTIC = 2,
+    /* not rules: every 32-bit value is a value of the type (an unknown one is rejected) */
+    SPECV_SIBLINGS_RANGE_LOW_ = -0x7fffffff - 1,
+    SPECV_SIBLINGS_RANGE_HIGH_ = 0x7fffffff
 } specv_sibling_rule;
 
 /*

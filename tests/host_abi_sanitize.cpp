@@ -1,0 +1,129 @@
+// Host-side argument checking of every libspecv entry point, built with AddressSanitizer and
+// UndefinedBehaviorSanitizer on the host code of the library (tests/test_host_sanitizers.py).
+// Every call here is invalid or empty, so each must return its status without launching
+// anything; device pointers are never dereferenced on the host, so stand-in addresses do.
+// Exit status 0 when every call returned what was expected.
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+
+#include "specv.h"
+
+namespace {
+
+int failures = 0;
+
+void expect(const char* what, int got, int want) {
+    if (got != want) {
+        std::printf("FAIL %s: status %d, expected %d (%s)\n", what, got, want, specv_last_error());
+        ++failures;
+    }
+}
+
+// either of two statuses (a check that may meet the missing device first)
+void expect_any(const char* what, int got, int want1, int want2) {
+    if (got != want1 && got != want2) expect(what, got, want1);
+}
+
+void* fake(uintptr_t a) { return reinterpret_cast<void*>(a); }
+
+}  // namespace
+
+int main() {
+    const auto I = SPECV_ERR_INVALID_ARG, U = SPECV_ERR_UNSUPPORTED, W = SPECV_ERR_WORKSPACE;
+    auto* i32 = static_cast<int32_t*>(fake(0x10000));
+    auto* u32 = static_cast<uint32_t*>(fake(0x20000));
+    void* dev = fake(0x30000);
+    void* ws = fake(0x40000);
+    const float nan = std::numeric_limits<float>::quiet_NaN();
+
+    // status strings and the last-error text
+    for (int s = -2; s < 8; ++s)
+        if (specv_status_string(static_cast<specv_status>(s)) == nullptr) expect("status string", 1, 0);
+
+    // mask
+    expect("mask B<0", specv_build_tree_mask(i32, -1, 3, u32, i32, i32, nullptr), I);
+    expect("mask K too large", specv_build_tree_mask(i32, 2, SPECV_MAX_NODES, u32, i32, i32, nullptr), I);
+    expect("mask null parent", specv_build_tree_mask(nullptr, 2, 3, u32, i32, i32, nullptr), I);
+    expect("mask empty", specv_build_tree_mask(i32, 0, 3, u32, i32, i32, nullptr), SPECV_OK);
+
+    // attention
+    const size_t aw = specv_attn_workspace_bytes(2, 5, 8, 2, 128, 64);
+    expect("attn Hq % Hkv", specv_tree_attn_verify(dev, dev, dev, i32, u32, 2, 5, 6, 4, 128, 64, 0.1f, SPECV_BF16,
+                                                    dev, nullptr, ws, aw, nullptr), I);
+    expect("attn D", specv_tree_attn_verify(dev, dev, dev, i32, u32, 2, 5, 8, 2, 96, 64, 0.1f, SPECV_BF16, dev,
+                                            nullptr, ws, aw, nullptr), U);
+    expect("attn Lmax < K + 1", specv_tree_attn_verify(dev, dev, dev, i32, u32, 2, 5, 8, 2, 128, 3, 0.1f, SPECV_BF16,
+                                                        dev, nullptr, ws, aw, nullptr), I);
+    expect("attn scale NaN", specv_tree_attn_verify(dev, dev, dev, i32, u32, 2, 5, 8, 2, 128, 64, nan, SPECV_BF16,
+                                                     dev, nullptr, ws, aw, nullptr), I);
+    // (the workspace plan reads the device's CU count, so without a device this is a HIP error)
+    expect_any("attn workspace", specv_tree_attn_verify(dev, dev, dev, i32, u32, 2, 5, 8, 2, 128, 64, 0.1f,
+                                                         SPECV_BF16, dev, nullptr, ws, aw > 0 ? aw - 1 : 0, nullptr),
+               W, SPECV_ERR_HIP);
+    expect("attn null q", specv_tree_attn_verify(nullptr, dev, dev, i32, u32, 2, 5, 8, 2, 128, 64, 0.1f, SPECV_BF16,
+                                                  dev, nullptr, ws, aw, nullptr), I);
+    expect("attn workspace query", static_cast<int>(specv_attn_workspace_bytes(-1, 5, 8, 2, 128, 64)), 0);
+
+    // accept
+    const size_t cw = specv_accept_workspace_bytes(4, 5, 1000, SPECV_BF16);
+    auto accept = [&](int32_t B, int32_t K, int32_t V, float T, const void* draft, void* w, size_t wb,
+                      int dtype = SPECV_BF16) {
+        return specv_accept_resample(dev, draft, static_cast<specv_dtype>(dtype), i32, i32, B, K, V, T, 1, 0, i32,
+                                     i32, i32, nullptr, nullptr, w, wb, nullptr);
+    };
+    expect("accept B<0", accept(-1, 5, 1000, 1.f, dev, ws, cw), I);
+    expect("accept K", accept(4, SPECV_MAX_NODES, 1000, 1.f, dev, ws, cw), I);
+    expect("accept V 0", accept(4, 5, 0, 1.f, dev, ws, cw), I);
+    expect("accept V too large", accept(4, 5, SPECV_MAX_VOCAB + 1, 1.f, dev, ws, cw), I);
+    expect("accept T<0", accept(4, 5, 1000, -1.f, dev, ws, cw), I);
+    expect("accept T NaN", accept(4, 5, 1000, nan, dev, ws, cw), I);
+    expect("accept T inf", accept(4, 5, 1000, INFINITY, dev, ws, cw), I);
+    expect("accept dtype", accept(4, 5, 1000, 1.f, dev, ws, cw, 7), U);
+    expect("accept no draft", accept(4, 5, 1000, 1.f, nullptr, ws, cw), I);
+    expect("accept workspace", accept(4, 5, 1000, 1.f, dev, ws, cw > 0 ? cw - 1 : 0), W);
+    expect("accept null workspace", accept(4, 5, 1000, 1.f, dev, nullptr, cw), W);
+    expect("accept empty", accept(0, 5, 1000, 1.f, dev, ws, cw), SPECV_OK);
+    expect("accept rule", specv_accept_resample_rule(dev, dev, SPECV_BF16, i32, i32, 4, 5, 1000, 1.f,
+                                                     static_cast<specv_sibling_rule>(9), 1, 0, i32, i32, i32,
+                                                     nullptr, nullptr, ws, cw, nullptr), I);
+    expect("accept workspace query", static_cast<int>(specv_accept_workspace_bytes(4, 5, 0, SPECV_BF16)), 0);
+
+    // KV commit
+    expect("commit Lmax", specv_kv_commit(dev, dev, i32, i32, i32, 2, 5, 2, 128, 3, SPECV_BF16, i32, nullptr), I);
+    expect("commit D", specv_kv_commit(dev, dev, i32, i32, i32, 2, 5, 2, 80, 64, SPECV_BF16, i32, nullptr), U);
+    expect("commit null", specv_kv_commit(nullptr, dev, i32, i32, i32, 2, 5, 2, 128, 64, SPECV_BF16, i32, nullptr), I);
+
+    // tree expansion
+    const size_t xw = specv_tree_expand_workspace_bytes(2, 4);
+    auto expand = [&](int32_t F, int32_t V, int32_t k, float T, int32_t keep, int32_t nmax, size_t wb) {
+        return specv_tree_expand(dev, SPECV_BF16, i32, 2, F, V, k, T, keep, nmax, i32, i32,
+                                 static_cast<double*>(fake(0x50000)), i32, i32, ws, wb, nullptr);
+    };
+    expect("expand k 0", expand(4, 1000, 0, 1.f, 4, 32, xw), I);
+    expect("expand k too large", expand(4, 1000, 17, 1.f, 4, 32, xw), I);
+    expect("expand T 0", expand(4, 1000, 3, 0.f, 4, 32, xw), I);
+    expect("expand nmax", expand(4, 1000, 3, 1.f, 4, SPECV_MAX_NODES + 1, xw), I);
+    expect("expand workspace", expand(4, 1000, 3, 1.f, 4, 32, xw > 0 ? xw - 1 : 0), W);
+
+    // one target layer
+    const size_t lw = specv_verify_layer_workspace_bytes(2, 5, 8, 2, 128, 64, 512);
+    auto layer = [&](int32_t Hq, int32_t Hkv, int32_t D, int32_t Lmax, int32_t inter, float eps, float theta,
+                     void* w, size_t wb) {
+        return specv_verify_layer(dev, dev, dev, dev, dev, dev, dev, eps, theta, dev, dev, i32, u32, i32, 2, 5, Hq,
+                                  Hkv, D, Lmax, inter, dev, w, wb, nullptr);
+    };
+    expect("layer inter % 64", layer(8, 2, 128, 64, 500, 1e-5f, 1e4f, ws, lw), I);
+    expect("layer D", layer(8, 2, 96, 64, 512, 1e-5f, 1e4f, ws, lw), U);
+    expect("layer eps", layer(8, 2, 128, 64, 512, 0.f, 1e4f, ws, lw), I);
+    expect("layer theta", layer(8, 2, 128, 64, 512, 1e-5f, 1.f, ws, lw), I);
+    expect("layer workspace", layer(8, 2, 128, 64, 512, 1e-5f, 1e4f, ws, lw > 0 ? lw - 1 : 0), W);
+    expect("layer unaligned workspace", layer(8, 2, 128, 64, 512, 1e-5f, 1e4f, fake(0x40008), lw), W);
+    expect("layer workspace query", static_cast<int>(specv_verify_layer_workspace_bytes(2, 5, 8, 2, 128, 64, 500)), 0);
+
+    std::printf("%s: %d failing checks\n", failures ? "FAILED" : "ok", failures);
+    return failures ? 1 : 0;
+}
