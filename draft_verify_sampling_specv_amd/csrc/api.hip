@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
 
 #include "../../include/specv.h"
 #include "kernels.h"
@@ -30,6 +31,28 @@ specv_status fail(specv_status s, const char* fmt, ...) {
 specv_status ok() {
     g_last_error[0] = '\0';
     return SPECV_OK;
+}
+
+// The kernels index rows, heads and grids with 32-bit integers: a product of sizes must fit.
+// (Each factor is at most 2^31 and the running product is checked before the next factor, so
+// the 64-bit arithmetic itself cannot overflow.)
+bool fits_i32(std::initializer_list<int64_t> factors) {
+    int64_t p = 1;
+    for (int64_t f : factors) {
+        if (f < 0) return false;
+        p *= f;
+        if (p > INT32_MAX) return false;
+    }
+    return true;
+}
+
+bool attn_sizes_ok(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D) {
+    return fits_i32({B, int64_t(K) + 1, Hq, D}) && fits_i32({B, Hkv, D});
+}
+
+bool layer_sizes_ok(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D, int32_t inter) {
+    return attn_sizes_ok(B, K, Hq, Hkv, D) && fits_i32({B, int64_t(K) + 1, int64_t(Hq) + 2 * int64_t(Hkv), D}) &&
+           fits_i32({B, int64_t(K) + 1, 2, inter});
 }
 
 specv_status hip_status(hipError_t e, const char* what) {
@@ -57,8 +80,9 @@ const char* specv_last_error(void) { return g_last_error; }
 specv_status specv_build_tree_mask(const int32_t* parent, int32_t B, int32_t K, uint32_t* mask,
                                    int32_t* depth, int32_t* tree_status, hipStream_t stream) {
     if (B < 0) return fail(SPECV_ERR_INVALID_ARG, "B = %d < 0", B);
-    if (K < 0 || K + 1 > SPECV_MAX_NODES)
+    if (K < 0 || K > SPECV_MAX_NODES - 1)
         return fail(SPECV_ERR_INVALID_ARG, "K = %d outside [0, %d]", K, SPECV_MAX_NODES - 1);
+    if (!fits_i32({B, int64_t(K) + 1})) return fail(SPECV_ERR_INVALID_ARG, "B * (K + 1) exceeds 2^31 - 1");
     if (B == 0) return ok();
     if (!parent || !mask || !depth || !tree_status)
         return fail(SPECV_ERR_INVALID_ARG, "NULL pointer argument");
@@ -68,7 +92,8 @@ specv_status specv_build_tree_mask(const int32_t* parent, int32_t B, int32_t K, 
 
 size_t specv_attn_workspace_bytes(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
                                   int32_t Lmax) {
-    if (B <= 0 || K < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || (D != 64 && D != 128) || Lmax <= 0)
+    if (B <= 0 || K < 0 || K > SPECV_MAX_NODES - 1 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 ||
+        (D != 64 && D != 128) || Lmax <= 0 || !attn_sizes_ok(B, K, Hq, Hkv, D))
         return 0;
     return specv::attn_workspace_bytes(B, K + 1, Hq, Hkv, D, Lmax);
 }
@@ -79,7 +104,7 @@ specv_status specv_tree_attn_verify(const void* q, const void* k_cache, const vo
                                     float scale, specv_dtype dtype, void* out, float* lse,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (B < 0) return fail(SPECV_ERR_INVALID_ARG, "B = %d < 0", B);
-    if (K < 0 || K + 1 > SPECV_MAX_NODES)
+    if (K < 0 || K > SPECV_MAX_NODES - 1)
         return fail(SPECV_ERR_INVALID_ARG, "K = %d outside [0, %d]", K, SPECV_MAX_NODES - 1);
     if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
         return fail(SPECV_ERR_INVALID_ARG, "Hq = %d, Hkv = %d: need Hq a positive multiple of Hkv", Hq, Hkv);
@@ -89,6 +114,8 @@ specv_status specv_tree_attn_verify(const void* q, const void* k_cache, const vo
     if (dtype != SPECV_F32 && dtype != SPECV_BF16)
         return fail(SPECV_ERR_UNSUPPORTED, "dtype %d not supported", static_cast<int>(dtype));
     if (D != 64 && D != 128) return fail(SPECV_ERR_UNSUPPORTED, "head size D = %d not in {64, 128}", D);
+    if (!attn_sizes_ok(B, K, Hq, Hkv, D))
+        return fail(SPECV_ERR_INVALID_ARG, "B * (K + 1) * Hq * D exceeds 2^31 - 1");
     if (B == 0) return ok();
     if (!q || !k_cache || !v_cache || !ctx_len || !mask || !out)
         return fail(SPECV_ERR_INVALID_ARG, "NULL pointer argument");
@@ -101,7 +128,8 @@ specv_status specv_tree_attn_verify(const void* q, const void* k_cache, const vo
 }
 
 size_t specv_accept_workspace_bytes(int32_t B, int32_t K, int32_t V, specv_dtype logits_dtype) {
-    if (B <= 0 || K < 0 || K + 1 > SPECV_MAX_NODES || V < 1 || V > SPECV_MAX_VOCAB) return 0;
+    if (B <= 0 || K < 0 || K > SPECV_MAX_NODES - 1 || V < 1 || V > SPECV_MAX_VOCAB || !fits_i32({B, int64_t(K) + 1}))
+        return 0;
     return specv::accept_workspace_bytes(B, K + 1, V, logits_dtype == SPECV_BF16);
 }
 
@@ -113,7 +141,7 @@ specv_status specv_accept_resample_rule(const void* target_logits, const void* d
                                         int32_t* out_nodes, float* p_tok, float* q_tok, void* workspace,
                                         size_t workspace_bytes, hipStream_t stream) {
     if (B < 0) return fail(SPECV_ERR_INVALID_ARG, "B = %d < 0", B);
-    if (K < 0 || K + 1 > SPECV_MAX_NODES)
+    if (K < 0 || K > SPECV_MAX_NODES - 1)
         return fail(SPECV_ERR_INVALID_ARG, "K = %d outside [0, %d]", K, SPECV_MAX_NODES - 1);
     if (V < 1 || V > SPECV_MAX_VOCAB)
         return fail(SPECV_ERR_INVALID_ARG, "V = %d outside [1, %d]", V, SPECV_MAX_VOCAB);
@@ -124,6 +152,7 @@ specv_status specv_accept_resample_rule(const void* target_logits, const void* d
         return fail(SPECV_ERR_INVALID_ARG, "sibling rule %d not in {0, 1, 2}", static_cast<int>(rule));
     if (logits_dtype != SPECV_F32 && logits_dtype != SPECV_BF16)
         return fail(SPECV_ERR_UNSUPPORTED, "dtype %d not supported", static_cast<int>(logits_dtype));
+    if (!fits_i32({B, int64_t(K) + 1})) return fail(SPECV_ERR_INVALID_ARG, "B * (K + 1) exceeds 2^31 - 1");
     if (B == 0) return ok();
     if (!target_logits || !tokens || !parent || !accept_len || !out_tokens || !out_nodes)
         return fail(SPECV_ERR_INVALID_ARG, "NULL pointer argument");
@@ -155,7 +184,7 @@ specv_status specv_accept_resample(const void* target_logits, const void* draft_
 }
 
 size_t specv_tree_expand_workspace_bytes(int32_t B, int32_t F) {
-    if (B <= 0 || F <= 0) return 0;
+    if (B <= 0 || F <= 0 || !fits_i32({B, F})) return 0;
     return specv::tree_expand_workspace_bytes(B, F);
 }
 
@@ -181,6 +210,7 @@ specv_status specv_tree_expand(const void* draft_logits, specv_dtype dtype, cons
         return fail(SPECV_ERR_INVALID_ARG, "nmax = %d outside [1, %d]", nmax, SPECV_MAX_NODES);
     if (dtype != SPECV_F32 && dtype != SPECV_BF16)
         return fail(SPECV_ERR_UNSUPPORTED, "dtype %d not supported", static_cast<int>(dtype));
+    if (!fits_i32({B, F})) return fail(SPECV_ERR_INVALID_ARG, "B * F exceeds 2^31 - 1");
     if (B == 0) return ok();
     if (!draft_logits || !frontier || !parent || !tokens || !score || !n_nodes || !new_frontier)
         return fail(SPECV_ERR_INVALID_ARG, "NULL pointer argument");
@@ -197,13 +227,14 @@ specv_status specv_kv_commit(void* k_cache, void* v_cache, const int32_t* ctx_le
                              int32_t K, int32_t Hkv, int32_t D, int32_t Lmax, specv_dtype dtype,
                              int32_t* new_ctx_len, hipStream_t stream) {
     if (B < 0) return fail(SPECV_ERR_INVALID_ARG, "B = %d < 0", B);
-    if (K < 0 || K + 1 > SPECV_MAX_NODES)
+    if (K < 0 || K > SPECV_MAX_NODES - 1)
         return fail(SPECV_ERR_INVALID_ARG, "K = %d outside [0, %d]", K, SPECV_MAX_NODES - 1);
     if (Hkv <= 0) return fail(SPECV_ERR_INVALID_ARG, "Hkv = %d <= 0", Hkv);
     if (Lmax < K + 1) return fail(SPECV_ERR_INVALID_ARG, "Lmax = %d < K + 1 = %d", Lmax, K + 1);
     if (dtype != SPECV_F32 && dtype != SPECV_BF16)
         return fail(SPECV_ERR_UNSUPPORTED, "dtype %d not supported", static_cast<int>(dtype));
     if (D != 64 && D != 128) return fail(SPECV_ERR_UNSUPPORTED, "head size D = %d not in {64, 128}", D);
+    if (!fits_i32({B, int64_t(K) + 1, 2, Hkv})) return fail(SPECV_ERR_INVALID_ARG, "B * (K + 1) * 2 * Hkv exceeds 2^31 - 1");
     if (B == 0) return ok();
     if (!k_cache || !v_cache || !ctx_len || !accept_len || !out_nodes || !new_ctx_len)
         return fail(SPECV_ERR_INVALID_ARG, "NULL pointer argument");
@@ -216,8 +247,9 @@ specv_status specv_kv_commit(void* k_cache, void* v_cache, const int32_t* ctx_le
 
 size_t specv_verify_layer_workspace_bytes(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
                                           int32_t Lmax, int32_t inter) {
-    if (B <= 0 || K < 0 || K + 1 > SPECV_MAX_NODES || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 ||
-        (D != 64 && D != 128) || Lmax < K + 1 || inter <= 0 || inter % 64 != 0)
+    if (B <= 0 || K < 0 || K > SPECV_MAX_NODES - 1 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 ||
+        (D != 64 && D != 128) || Lmax < K + 1 || inter <= 0 || inter % 64 != 0 ||
+        !layer_sizes_ok(B, K, Hq, Hkv, D, inter))
         return 0;
     return specv::layer_workspace_bytes(B, K + 1, Hq, Hkv, D, Lmax, inter);
 }
@@ -230,7 +262,7 @@ specv_status specv_verify_layer(const void* x, const void* w_qkv, const void* w_
                                 int32_t inter, void* out, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream) {
     if (B < 0) return fail(SPECV_ERR_INVALID_ARG, "B = %d < 0", B);
-    if (K < 0 || K + 1 > SPECV_MAX_NODES)
+    if (K < 0 || K > SPECV_MAX_NODES - 1)
         return fail(SPECV_ERR_INVALID_ARG, "K = %d outside [0, %d]", K, SPECV_MAX_NODES - 1);
     if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
         return fail(SPECV_ERR_INVALID_ARG, "Hq = %d, Hkv = %d: need Hq a positive multiple of Hkv", Hq, Hkv);
@@ -241,6 +273,8 @@ specv_status specv_verify_layer(const void* x, const void* w_qkv, const void* w_
     if (!(std::isfinite(rope_theta) && rope_theta > 1.f))
         return fail(SPECV_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
     if (D != 64 && D != 128) return fail(SPECV_ERR_UNSUPPORTED, "head size D = %d not in {64, 128}", D);
+    if (!layer_sizes_ok(B, K, Hq, Hkv, D, inter))
+        return fail(SPECV_ERR_INVALID_ARG, "row, head or MLP sizes exceed 2^31 - 1 elements");
     if (B == 0) return ok();
     const void* ptrs[] = {x, w_qkv, w_o, w_gate_up, w_down, attn_norm, mlp_norm, k_cache, v_cache, out};
     for (const void* p : ptrs) {

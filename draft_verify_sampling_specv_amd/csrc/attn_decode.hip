@@ -119,8 +119,8 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     asm volatile("" ::: "memory");
     load_k(w, Lmax - 1);
     const int L = __builtin_amdgcn_readfirstlane(L0);
-    const bool seq_ok = L >= 0 && L + n1 <= Lmax;
-    const int Ltot = L + n1;
+    const bool seq_ok = L >= 0 && L <= Lmax - n1;
+    const int Ltot = seq_ok ? L + n1 : 0;
     const int ntiles = seq_ok ? (Ltot + kTileKeys - 1) / kTileKeys : 0;
     const int kmax = seq_ok ? Ltot - 1 : 0;
 #pragma unroll

@@ -22,7 +22,7 @@ attn_f32_kernel(const float* __restrict__ q, const float* __restrict__ kc,
     const int words = (n1 + 31) >> 5;
     const int L = ctx_len[b];
     const int64_t orow = (static_cast<int64_t>(b) * n1 + node) * Hq + hh;
-    if (!(L >= 0 && L + n1 <= Lmax)) {
+    if (!(L >= 0 && L <= Lmax - n1)) {
         for (int d = lane; d < D; d += kWave) out[orow * D + d] = NAN;
         if (lse && lane == 0) lse[orow] = NAN;
         return;

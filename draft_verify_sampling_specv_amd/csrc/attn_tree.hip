@@ -351,8 +351,8 @@ attn_tree_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc
     const int words = (n1 + 31) >> 5;
 
     const int L = ctx_len[b];
-    const bool seq_ok = L >= 0 && L + n1 <= Lmax;
-    const int Ltot = L + n1;
+    const bool seq_ok = L >= 0 && L <= Lmax - n1;
+    const int Ltot = seq_ok ? L + n1 : 0;
     const int ntiles = seq_ok ? (Ltot + kTreeTile - 1) / kTreeTile : 0;
     const int tps = (ntiles + nsplit - 1) / nsplit;
     const int t0 = min(ntiles, split * tps), t1 = min(ntiles, t0 + tps);
@@ -428,7 +428,7 @@ attn_tree_combine_kernel(const uint16_t* __restrict__ opart, const float2* __res
     const int kv = hh / G, g = hh % G;
     const int row = node * G + g;
     const int L = ctx_len[b];
-    const bool ok = L >= 0 && L + n1 <= Lmax;
+    const bool ok = L >= 0 && L <= Lmax - n1;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float den = 0.f, M = -INFINITY;
     const int64_t ubase = (static_cast<int64_t>(b) * Hkv + kv) * nsplit;
@@ -472,17 +472,13 @@ attn_tree_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc
 
 // Workgroups of the tree kernel one compute unit holds at once (LDS ring and registers).
 int tree_blocks_per_cu(int D) {
-    static int cache[64][2] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
-    int& c = cache[dev][D == 64 ? 0 : 1];
-    if (!c) {
+    static std::atomic<int> cache64[64], cache128[64];
+    const void* f = (D == 64) ? reinterpret_cast<const void*>(&attn_tree_kernel<64>)
+                              : reinterpret_cast<const void*>(&attn_tree_kernel<128>);
+    return cached_per_device(D == 64 ? cache64 : cache128, [f](int) {
         int n = 0;
-        const void* f = (D == 64) ? reinterpret_cast<const void*>(&attn_tree_kernel<64>)
-                                  : reinterpret_cast<const void*>(&attn_tree_kernel<128>);
-        c = (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, kTreeThreads, 0) == hipSuccess && n > 0) ? n : 1;
-    }
-    return c;
+        return (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, kTreeThreads, 0) == hipSuccess && n > 0) ? n : 1;
+    });
 }
 
 // Row groups of at most kTreeWaves blocks (one per wave), balanced.  Key splits: the time goes as

@@ -6,20 +6,36 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace specv {
 
 constexpr int kMaxNodes = 1024;
 
-// Compute units of the current device (cached per device; 256 if the query fails).
-inline int device_cu_count() {
-    static int cus[64] = {0};
+// A per-device value computed once by `query` and cached in an atomic slot, so that concurrent
+// callers may race to fill it without undefined behaviour (each computes the same value).
+// Devices past the slot table are queried every time.
+template <typename Query>
+inline int cached_per_device(std::atomic<int> (&slots)[64], Query query) {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cus[dev]) {
-        hipDeviceProp_t prop;
-        cus[dev] = (hipGetDeviceProperties(&prop, dev) == hipSuccess) ? prop.multiProcessorCount : 256;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return query(0);
+    if (dev >= 64) return query(dev);
+    int v = slots[dev].load(std::memory_order_relaxed);
+    if (!v) {
+        v = query(dev);
+        slots[dev].store(v, std::memory_order_relaxed);
     }
-    return cus[dev];
+    return v;
+}
+
+// Compute units of the current device (256 if the query fails).
+inline int device_cu_count() {
+    static std::atomic<int> cus[64];
+    return cached_per_device(cus, [](int dev) {
+        int n = 0;
+        return (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n
+                                                                                                            : 256;
+    });
 }
 
 hipError_t launch_build_tree_mask(const int32_t* parent, int B, int n1, uint32_t* mask,

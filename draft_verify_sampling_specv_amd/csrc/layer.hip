@@ -319,7 +319,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const uint16_t* _
     const int j = threadIdx.x;
     if (j < D / 2) {
         const int b = static_cast<int>(row) / n1;
-        const double ang = static_cast<double>(ctx_len[b] + depth[row]) * pow(static_cast<double>(theta), -2.0 * j / D);
+        const double ang = (static_cast<double>(ctx_len[b]) + static_cast<double>(depth[row])) * pow(static_cast<double>(theta), -2.0 * j / D);
         rot[row * (D / 2) + j] = make_float2(static_cast<float>(cos(ang)), static_cast<float>(sin(ang)));
     }
 }
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(64) void qkv_epilogue_kernel(
     const int t = m0 + mloc;
     const int b = t / n1, i = t - b * n1;
     const int L = ctx_len[b], d = depth[t];
-    const bool ok = d >= 0 && L >= 0 && L + n1 <= Lmax;
+    const bool ok = d >= 0 && L >= 0 && L <= Lmax - n1;
     const int N = (Hq + 2 * Hkv) * D;
     const int64_t plane = static_cast<int64_t>(Mc) * N;
     const float* pr = P + static_cast<int64_t>(mloc) * N + head * D + j;

@@ -16,6 +16,15 @@ ATTN_BF16_ABS = 2e-2     # attention output, bf16 path
 ATTN_F32_ABS = 1e-5      # attention output, fp32 path
 
 
+# What each parity check measured (name -> dict), printed in pytest's terminal summary so that a
+# captured run still shows the error magnitudes and near-tie counts against the tolerances.
+RESULTS = {}
+
+
+def record(name, **values):
+    RESULTS.setdefault(name, {}).update(values)
+
+
 def log(*a):
     print(*a, flush=True)
     sys.stdout.flush()
@@ -77,6 +86,7 @@ def compare_accept(gpu, ora, seqs=None, check_probs=True, name=""):
                         gpu["out_tokens"][b][:6].tolist(), ora["out_tokens"][j][:6].tolist(),
                         float(ora["margin"][j])))
     log(f"[{name}] sequences {len(seqs)}, near ties {near}, mismatches {len(bad)}")
+    record(name, kind="accept", sequences=len(seqs), near_ties=near, mismatches=len(bad))
     assert not bad, f"[{name}] mismatches (b, gpu_len, oracle_len, gpu_tok, oracle_tok, margin): {bad[:5]}"
     if check_probs:
         for key in ("p_tok", "q_tok"):
@@ -87,5 +97,6 @@ def compare_accept(gpu, ora, seqs=None, check_probs=True, name=""):
             if fin.any():
                 rel = np.abs(g[fin] - o[fin]) / np.maximum(np.abs(o[fin]), 1e-300)
                 log(f"[{name}] {key} max rel err {rel.max():.3e}")
+                record(name, **{f"{key}_max_rel": float(rel.max())})
                 assert rel.max() <= P_REL, f"[{name}] {key} rel err {rel.max()}"
     return near

@@ -49,6 +49,9 @@ int main() {
     expect("mask K too large", specv_build_tree_mask(i32, 2, SPECV_MAX_NODES, u32, i32, i32, nullptr), I);
     expect("mask null parent", specv_build_tree_mask(nullptr, 2, 3, u32, i32, i32, nullptr), I);
     expect("mask empty", specv_build_tree_mask(i32, 0, 3, u32, i32, i32, nullptr), SPECV_OK);
+    const int32_t IMAX = std::numeric_limits<int32_t>::max();
+    expect("mask K INT_MAX", specv_build_tree_mask(i32, 2, IMAX, u32, i32, i32, nullptr), I);
+    expect("mask B INT_MAX", specv_build_tree_mask(i32, IMAX, 3, u32, i32, i32, nullptr), I);
 
     // attention
     const size_t aw = specv_attn_workspace_bytes(2, 5, 8, 2, 128, 64);
@@ -67,6 +70,16 @@ int main() {
     expect("attn null q", specv_tree_attn_verify(nullptr, dev, dev, i32, u32, 2, 5, 8, 2, 128, 64, 0.1f, SPECV_BF16,
                                                   dev, nullptr, ws, aw, nullptr), I);
     expect("attn workspace query", static_cast<int>(specv_attn_workspace_bytes(-1, 5, 8, 2, 128, 64)), 0);
+    expect("attn K INT_MAX", specv_tree_attn_verify(dev, dev, dev, i32, u32, 2, IMAX, 8, 2, 128, IMAX, 0.1f,
+                                                     SPECV_BF16, dev, nullptr, ws, aw, nullptr), I);
+    expect("attn B INT_MAX", specv_tree_attn_verify(dev, dev, dev, i32, u32, IMAX, 5, 8, 2, 128, 64, 0.1f,
+                                                     SPECV_BF16, dev, nullptr, ws, aw, nullptr), I);
+    expect("attn Hq INT_MAX", specv_tree_attn_verify(dev, dev, dev, i32, u32, 2, 5, IMAX, 1, 128, 64, 0.1f,
+                                                      SPECV_BF16, dev, nullptr, ws, aw, nullptr), I);
+    expect("attn workspace query K INT_MAX", static_cast<int>(specv_attn_workspace_bytes(2, IMAX, 8, 2, 128, 64)), 0);
+    expect("attn workspace query B INT_MAX", static_cast<int>(specv_attn_workspace_bytes(IMAX, 5, 8, 2, 128, 64)), 0);
+    expect("attn workspace query Hq INT_MAX",
+           static_cast<int>(specv_attn_workspace_bytes(2, 5, IMAX, 1, 128, 64)), 0);
 
     // accept
     const size_t cw = specv_accept_workspace_bytes(4, 5, 1000, SPECV_BF16);
@@ -91,11 +104,26 @@ int main() {
                                                      static_cast<specv_sibling_rule>(9), 1, 0, i32, i32, i32,
                                                      nullptr, nullptr, ws, cw, nullptr), I);
     expect("accept workspace query", static_cast<int>(specv_accept_workspace_bytes(4, 5, 0, SPECV_BF16)), 0);
+    expect("accept K INT_MAX", accept(4, IMAX, 1000, 1.f, dev, ws, cw), I);
+    expect("accept B INT_MAX", accept(IMAX, 5, 1000, 1.f, dev, ws, cw), I);
+    expect("accept V INT_MAX", accept(4, 5, IMAX, 1.f, dev, ws, cw), I);
+    expect("accept workspace query K INT_MAX",
+           static_cast<int>(specv_accept_workspace_bytes(4, IMAX, 1000, SPECV_BF16)), 0);
+    expect("accept workspace query B INT_MAX",
+           static_cast<int>(specv_accept_workspace_bytes(IMAX, 5, 1000, SPECV_BF16)), 0);
+    expect("accept workspace query V INT_MAX",
+           static_cast<int>(specv_accept_workspace_bytes(4, 5, IMAX, SPECV_BF16)), 0);
 
     // KV commit
     expect("commit Lmax", specv_kv_commit(dev, dev, i32, i32, i32, 2, 5, 2, 128, 3, SPECV_BF16, i32, nullptr), I);
     expect("commit D", specv_kv_commit(dev, dev, i32, i32, i32, 2, 5, 2, 80, 64, SPECV_BF16, i32, nullptr), U);
     expect("commit null", specv_kv_commit(nullptr, dev, i32, i32, i32, 2, 5, 2, 128, 64, SPECV_BF16, i32, nullptr), I);
+    expect("commit K INT_MAX", specv_kv_commit(dev, dev, i32, i32, i32, 2, IMAX, 2, 128, IMAX, SPECV_BF16, i32,
+                                               nullptr), I);
+    expect("commit B INT_MAX", specv_kv_commit(dev, dev, i32, i32, i32, IMAX, 5, 2, 128, 64, SPECV_BF16, i32,
+                                               nullptr), I);
+    expect("commit Hkv INT_MAX", specv_kv_commit(dev, dev, i32, i32, i32, 2, 5, IMAX, 128, 64, SPECV_BF16, i32,
+                                                 nullptr), I);
 
     // tree expansion
     const size_t xw = specv_tree_expand_workspace_bytes(2, 4);
@@ -108,6 +136,12 @@ int main() {
     expect("expand T 0", expand(4, 1000, 3, 0.f, 4, 32, xw), I);
     expect("expand nmax", expand(4, 1000, 3, 1.f, 4, SPECV_MAX_NODES + 1, xw), I);
     expect("expand workspace", expand(4, 1000, 3, 1.f, 4, 32, xw > 0 ? xw - 1 : 0), W);
+    expect("expand F INT_MAX", expand(IMAX, 1000, 3, 1.f, 4, 32, xw), I);
+    expect("expand V INT_MAX", expand(4, IMAX, 3, 1.f, 4, 32, xw), I);
+    expect("expand k INT_MAX", expand(4, 1000, IMAX, 1.f, 4, 32, xw), I);
+    expect("expand B INT_MAX", specv_tree_expand(dev, SPECV_BF16, i32, IMAX, 4, 1000, 3, 1.f, 4, 32, i32, i32,
+                                                 static_cast<double*>(fake(0x50000)), i32, i32, ws, xw, nullptr), I);
+    expect("expand workspace query", static_cast<int>(specv_tree_expand_workspace_bytes(IMAX, IMAX)), 0);
 
     // one target layer
     const size_t lw = specv_verify_layer_workspace_bytes(2, 5, 8, 2, 128, 64, 512);
@@ -123,6 +157,18 @@ int main() {
     expect("layer workspace", layer(8, 2, 128, 64, 512, 1e-5f, 1e4f, ws, lw > 0 ? lw - 1 : 0), W);
     expect("layer unaligned workspace", layer(8, 2, 128, 64, 512, 1e-5f, 1e4f, fake(0x40008), lw), W);
     expect("layer workspace query", static_cast<int>(specv_verify_layer_workspace_bytes(2, 5, 8, 2, 128, 64, 500)), 0);
+    expect("layer inter INT_MAX", layer(8, 2, 128, 64, IMAX - 63, 1e-5f, 1e4f, ws, lw), I);
+    expect("layer Hq INT_MAX", layer(IMAX, 1, 128, 64, 512, 1e-5f, 1e4f, ws, lw), I);
+    expect("layer K INT_MAX", specv_verify_layer(dev, dev, dev, dev, dev, dev, dev, 1e-5f, 1e4f, dev, dev, i32, u32,
+                                                 i32, 2, IMAX, 8, 2, 128, IMAX, 512, dev, ws, lw, nullptr), I);
+    expect("layer B INT_MAX", specv_verify_layer(dev, dev, dev, dev, dev, dev, dev, 1e-5f, 1e4f, dev, dev, i32, u32,
+                                                 i32, IMAX, 5, 8, 2, 128, 64, 512, dev, ws, lw, nullptr), I);
+    expect("layer workspace query inter INT_MAX",
+           static_cast<int>(specv_verify_layer_workspace_bytes(2, 5, 8, 2, 128, 64, IMAX - 63)), 0);
+    expect("layer workspace query K INT_MAX",
+           static_cast<int>(specv_verify_layer_workspace_bytes(2, IMAX, 8, 2, 128, IMAX, 512)), 0);
+    expect("layer workspace query B INT_MAX",
+           static_cast<int>(specv_verify_layer_workspace_bytes(IMAX, 5, 8, 2, 128, 64, 512)), 0);
 
     std::printf("%s: %d failing checks\n", failures ? "FAILED" : "ok", failures);
     return failures ? 1 : 0;

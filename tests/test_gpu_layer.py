@@ -112,14 +112,15 @@ def test_layer_random_trees(shape):
 
 def test_layer_invalid_sequences():
     rng = np.random.default_rng(9)
-    B, n1 = 4, 6
+    B, n1 = 5, 6
     parent = np.tile(np.arange(-1, n1 - 1), (B, 1)).astype(np.int32)
     parent[2, 4] = 4                                     # not a tree
-    li = workloads.make_layer("layer-invalid", parent, [30, 40, 35, 20], 4, 2, 64, 128, seed_base=77)
+    li = workloads.make_layer("layer-invalid", parent, [30, 40, 35, 20, 25], 4, 2, 64, 128, seed_base=77)
     lmax = li.k_cache.shape[2]
     li.ctx_len[1] = lmax - n1 + 1                        # no room for the nodes
     li.ctx_len[3] = -1
-    log("verify_layer: invalid sequences 1 (no room), 2 (bad tree), 3 (ctx -1)")
+    li.ctx_len[4] = 2**31 - 2                            # ctx_len + K + 1 past the 32-bit range
+    log("verify_layer: invalid sequences 1 (no room), 2 (bad tree), 3 (ctx -1), 4 (ctx 2^31 - 2)")
     _compare(li, _run_gpu(li), _oracle(li), "invalid")
 
 

@@ -98,3 +98,27 @@ def test_selected_rows_match_full_output():
     for b, i in rows:
         np.testing.assert_array_equal(o2[b, i], out[b, i])
         np.testing.assert_array_equal(l2[b, i], lse[b, i])
+
+
+def test_short_context_parity_inputs_see_every_mask_bit():
+    """The GPU parity cases with contexts of 0, 1 and 63 keys (the configurations' head layouts and
+    trees) are built so that a wrong mask bit cannot hide under the 2e-2 bf16 tolerance: flipping
+    any one bit (i, j), j < i, of a row moves that row of the oracle's output by more than twice
+    the tolerance.  Checked on a seeded sample of 24 flips per sequence."""
+    import workloads
+    rng = np.random.default_rng(0)
+    for shape in sorted(workloads.MASK_SENSITIVE_SHAPES):
+        a = workloads.mask_sensitive_attention(shape)
+        om, _, _ = tree.build_tree_mask_batch(a.parent)
+        k64, v64 = a.k_cache.astype(np.float64), a.v_cache.astype(np.float64)
+        B, n1 = a.parent.shape
+        for b in range(B):
+            for _ in range(24):
+                i = int(rng.integers(1, n1))
+                j = int(rng.integers(0, i))
+                m = om.copy()
+                m[b, i, j // 32] ^= np.uint32(1 << (j % 32))
+                ref, _ = attention.tree_attention(a.q, k64, v64, a.ctx_len, om, a.scale, rows=[(b, i)])
+                mut, _ = attention.tree_attention(a.q, k64, v64, a.ctx_len, m, a.scale, rows=[(b, i)])
+                moved = np.abs(mut[b, i] - ref[b, i]).max()
+                assert moved > 4e-2, (shape, int(a.ctx_len[b]), i, j, moved)

@@ -429,6 +429,51 @@ def ptd_attention(parent, seed_base=5001):
     return make_attention("ptd-attn", parent, [32768] * B, 64, 8, 128, "bf16", seed_base)
 
 
+def eagle_shaped_parents(B, seed_base=3200, V=512, T=0.7):
+    """Trees of the EAGLE-style configuration's shape (top-3 children drawn without replacement,
+    depth 6, the 60 nodes of highest cumulative draft probability kept) grown from cheap random
+    draft rows (V = 512, N(0, 3)): for attention cases that need the shape, not the logits."""
+    rng = np.random.default_rng(seed_base)
+    out = []
+    for _ in range(B):
+        rows = {}
+
+        def row(v):
+            if v not in rows:
+                rows[v] = 3.0 * rng.standard_normal(V)
+            return rows[v]
+
+        parent, _, _ = eagle_tree(rng, row, T)
+        out.append(parent)
+    return np.stack(out)
+
+
+# Head layouts and trees of the four full-size configurations, for attention with very short
+# contexts (0, 1 and 63 keys): there the tree's own keys carry much of the softmax weight.
+MASK_SENSITIVE_SHAPES = {
+    "chain": (32, 8),       # chain K=5
+    "eagle": (64, 8),       # EAGLE-style tree, 61 nodes
+    "stress": (40, 8),      # chain K=8
+    "ptd": (64, 8),         # PTD-style random tree, 65 nodes
+}
+MASK_SENSITIVE_CONTEXTS = (0, 1, 63)
+
+
+def mask_sensitive_attention(shape, seed_base=6000):
+    hq, hkv = MASK_SENSITIVE_SHAPES[shape]
+    B = len(MASK_SENSITIVE_CONTEXTS)
+    if shape == "chain":
+        parent = chain_parent(B, 5)
+    elif shape == "stress":
+        parent = chain_parent(B, 8)
+    elif shape == "eagle":
+        parent = eagle_shaped_parents(B)
+    else:
+        parent = ptd_parent(B=B)
+    return make_attention(f"{shape}-short-ctx", parent, list(MASK_SENSITIVE_CONTEXTS), hq, hkv, 128, "bf16",
+                          seed_base + sorted(MASK_SENSITIVE_SHAPES).index(shape))
+
+
 def random_case(seed, B, n1, V, T, dtype="f32", max_children=3, max_depth=None,
                 target_std=2.0, draft_sigma=0.7, siblings="without_replacement"):
     """Small random tree case for parity sweeps."""
