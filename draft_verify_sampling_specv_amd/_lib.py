@@ -199,7 +199,8 @@ class AcceptBuffers:
         res = AcceptResult(torch.empty((B,), **i32), torch.empty((B, n1), **i32), torch.empty((B, n1), **i32),
                            torch.empty((B, n1), **f32), torch.empty((B, n1), **f32))
         ws = accept_workspace_bytes(B, n1 - 1, V, dtype)
-        return AcceptBuffers(res, torch.empty((max(ws, 1),), dtype=torch.uint8, device=device))
+        # zero-filled once; the library keeps it valid from call to call
+        return AcceptBuffers(res, torch.zeros((max(ws, 1),), dtype=torch.uint8, device=device))
 
 
 def accept_resample(target_logits, draft_logits, tokens, parent, temperature, seed=0, offset=0,

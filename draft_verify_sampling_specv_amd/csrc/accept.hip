@@ -12,10 +12,8 @@
 // from p' when rejected, and the final draw excludes the rejected candidates.
 //
 // One launch whose grid never exceeds the number of workgroups the device holds at once (one per
-// CU here: the LDS tables need about 100 KB), so on a device running this kernel alone every
-// workgroup is resident together.  (A cooperative launch would guarantee that, but costs about
-// 20 us per call on this machine.)  Workgroups form teams of P; a team owns
-// one sequence at a time (sequences are dealt to teams round-robin) and every phase that streams
+// CU here: the LDS tables need about 100 KB).  Workgroups form teams of P; a team owns one
+// sequence at a time (sequences are dealt to teams round-robin) and every phase that streams
 // the vocabulary is split over the P workgroups of the team:
 //   1. statistics: items (row, chunk of 64 * kVec * kWaveLoads elements), one wave per item, over
 //      every target row and the draft rows of internal nodes, coalesced 16-byte loads, one exp per
@@ -29,20 +27,35 @@
 //      final draw pass are split into P contiguous ranges; partial sums are exchanged and added in
 //      rank order (fp64), so every workgroup sees the same totals.  The workgroup whose range holds
 //      the CDF crossing searches it (per-segment sums in LDS, then one wave) and writes the token.
-// Workgroups exchange values through 64-bit words (32-bit value, 32-bit tag of the launch) written
-// and read with device-scope atomic stores / loads: a word carries its own validity, so no fence
-// is needed.  Every wait is bounded by a wall-clock timeout, sticky per workgroup, so a launch ends
-// within about one timeout even if a teammate were never scheduled (e.g. CUs held by another
-// process); the sequences of a workgroup that timed out report accept_len = -2.
+// Workgroups exchange values through 64-bit words (32-bit value, 32-bit epoch of the launch)
+// written and read with device-scope atomic stores / loads: a word carries its own validity, so
+// no fence is needed.  The epoch lives in the workspace and advances by one per launch -- a replay
+// of a captured launch included.
+//
+// No workgroup depends on another being scheduled.  A wait for a teammate's words (its chunk
+// statistics, or its share of a vocabulary pass) lasts at most a budget (wait_ticks); after that
+// the waiting workgroup computes the missing values itself, with the same arithmetic in the same
+// order (a variant of the code that loads one vector at a time), so they are the same bits
+// whoever computes them, and publishes them.  The outputs are therefore exact whatever the
+// device does: a teammate that runs late (CUs held by another stream or process) costs time
+// only.  Outputs are written by fixed workgroups (rank 0; the owner of the draw's CDF crossing),
+// which all run eventually.
 //
 // Precision: per-element exponentials in fp32 (v_exp_f32), chunk and segment sums in fp32,
-// everything above (row normalisers, ratios, c, Q, R, the CDF threshold and prefixes) in fp64.
+// everything above (row normalisers, ratios, c, Q, R, the CDF threshold and prefixes) in fp64;
+// team partial sums cross workgroups as fp64 (two words).
 
 #include <algorithm>
 #include <atomic>
+#include <cstdlib>
 
 #include "common.h"
 #include "kernels.h"
+
+// No contraction of multiplies and adds into fma in this file: a value that one workgroup
+// computes on behalf of another must be the same bits as the owner's, and with contraction the
+// choice could differ between two inlined copies of the same code.
+#pragma clang fp contract(off)
 
 namespace specv {
 
@@ -62,20 +75,25 @@ constexpr int kRuleIid = 1;                 // drawn independently from q_v
 constexpr int kRuleDeterministic = 2;       // fixed candidates (a point mass each)
 constexpr int kMaskNodes = 128;             // trees up to this size keep children bit masks
 constexpr int kMaskWords = kMaskNodes / 64;
-constexpr uint64_t kTimeoutTicks = 50000000ull;   // 0.5 s of the 100 MHz wall clock
+constexpr int kLine = 8;                    // 64-bit words per control line (64 bytes)
 
 template <typename T>
 constexpr int item_elems() { return kWave * Elem<T>::kVec * kWaveLoads; }   // bf16 8192, fp32 4096
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// ctl: the epoch (word 0), counts of batches of statistics (word 1) and of range partials (word 2)
+// computed on a teammate's behalf since the workspace was cleared (diagnostics); seen: the epoch
+// each workgroup last held [B * P] (32 bits); stat: tagged chunk statistics [B][n1][nchunk][4];
+// part: tagged fp64 partial sums of the team exchanges [B][n1 + 1][P][2].
 struct AcceptLayout {
-    size_t stat, part, err, total;
+    size_t ctl, seen, stat, part, total;
     AcceptLayout(int B, int n1, int nchunk, int P) {
-        stat = 0;
+        ctl = 0;
+        seen = align256(ctl + sizeof(uint64_t) * kLine);
+        stat = align256(seen + sizeof(uint32_t) * size_t(B) * P);
         part = align256(stat + sizeof(uint64_t) * size_t(B) * n1 * nchunk * 4);
-        err = align256(part + sizeof(uint64_t) * size_t(B) * (n1 + 1) * P);
-        total = align256(err + sizeof(uint32_t));
+        total = align256(part + sizeof(uint64_t) * size_t(B) * (n1 + 1) * P * 2);
     }
 };
 
@@ -130,61 +148,41 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Publish / read a tagged 64-bit word (value in the low half, launch tag in the high half).
+// Publish a tagged 64-bit word (value in the low half, the launch's epoch in the high half).
 __device__ __forceinline__ void put_word(uint64_t* p, uint32_t bits, uint32_t tag) {
     __hip_atomic_store(p, (static_cast<uint64_t>(tag) << 32) | bits, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Once a wait of this workgroup has timed out (*timed_out, sticky for the launch), later waits
-// return at once, so a launch ends within about one timeout whatever happens.
-__device__ uint32_t get_word(uint64_t* p, uint32_t tag, int* timed_out) {
-    uint64_t w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (static_cast<uint32_t>(w >> 32) != tag && !*timed_out) {
-        const uint64_t t0 = wall_clock64();
-        do {
-            __builtin_amdgcn_s_sleep(1);
-            w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (wall_clock64() - t0 > kTimeoutTicks) {
-                *timed_out = 1;
-                break;
-            }
-        } while (static_cast<uint32_t>(w >> 32) != tag);
-    }
-    return static_cast<uint32_t>(w);
+__device__ __forceinline__ uint64_t load_word(uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Read n tagged words at p (n <= N): all loads are issued before any tag is checked, and the
-// words not yet published are polled together (bounded as in get_word).
-template <int N>
-__device__ __forceinline__ void get_words(uint64_t* p, int n, uint32_t tag, int* timed_out, uint32_t (&v)[N]) {
-    uint64_t raw[N];
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-        raw[i] = (i < n) ? __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-    auto missing = [&]() {
-        bool any = false;
-#pragma unroll
-        for (int i = 0; i < N; ++i) any |= (i < n) && static_cast<uint32_t>(raw[i] >> 32) != tag;
-        return any;
+// An fp64 value as two tagged words (high half first).
+__device__ __forceinline__ void put_double(uint64_t* p, double x, uint32_t tag) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(x));
+    put_word(p, static_cast<uint32_t>(b >> 32), tag);
+    put_word(p + 1, static_cast<uint32_t>(b), tag);
+}
+
+// Wait at most `budget` ticks of the 100 MHz wall clock for both words of an fp64 value (both
+// requested together, then whichever is missing polled); true if they came, with the value.
+__device__ bool get_double(uint64_t* p, uint32_t tag, uint64_t budget, double* out) {
+    uint64_t w0 = load_word(p), w1 = load_word(p + 1);
+    auto absent = [&]() {
+        return static_cast<uint32_t>(w0 >> 32) != tag || static_cast<uint32_t>(w1 >> 32) != tag;
     };
-    if (missing() && !*timed_out) {
-        // poll the missing words together, one round trip per round
+    if (absent()) {
         const uint64_t t0 = wall_clock64();
         do {
+            if (wall_clock64() - t0 > budget) return false;
             __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-            for (int i = 0; i < N; ++i)
-                if (i < n && static_cast<uint32_t>(raw[i] >> 32) != tag)
-                    raw[i] = __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (wall_clock64() - t0 > kTimeoutTicks) {
-                *timed_out = 1;
-                break;
-            }
-        } while (missing());
+            if (static_cast<uint32_t>(w0 >> 32) != tag) w0 = load_word(p);
+            if (static_cast<uint32_t>(w1 >> 32) != tag) w1 = load_word(p + 1);
+        } while (absent());
     }
-#pragma unroll
-    for (int i = 0; i < N; ++i) v[i] = static_cast<uint32_t>(raw[i]);
+    *out = __longlong_as_double(static_cast<long long>((w0 << 32) | (w1 & 0xFFFFFFFFull)));
+    return true;
 }
 
 // Bit e set iff token base + e is in the exclusion list (tokens whose weight is 0 in a draw:
@@ -198,25 +196,122 @@ __device__ __forceinline__ uint32_t excluded_in(const int32_t* excl, int nexcl, 
     return m;
 }
 
+// The statistics of one item (one wave): (max, sum of exp2((z - max) k)) over elements [lo, hi)
+// of `src`, or (max, argmax) at T = 0, as two words (w0, w1; in every lane).  The wave's lanes
+// take the item's 16-byte vectors u = 0 .. kWaveLoads - 1 in order; `r` holds their raw words if
+// `loaded`, else they are loaded here, all at once -- or, with kLean, one at a time (few
+// registers, same arithmetic in the same order, so the same bits).
+template <typename T, bool kGreedy, bool kVecOK, bool kLean>
+__device__ __forceinline__ void item_stats(const T* src, int lo, int hi, int lane, float k, uint4 (&r)[kWaveLoads],
+                                           bool loaded, uint32_t& w0, uint32_t& w1) {
+    constexpr int kVec = Elem<T>::kVec;
+    if (kVecOK && !kLean && !loaded) load_item<T>(src, lo, hi, lane, r);
+    // values of vector u, converted from the raw words when used (two passes: max, then sum of
+    // exp), so only the raw 16-byte words stay in registers
+    auto values = [&](int u, float* z) {
+        const int base = lo + (u * kWave + lane) * kVec;
+        if (kVecOK) {
+            uint4 rv;
+            if constexpr (kLean) {
+                const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<T*>(src + lo), 0, (hi - lo) * static_cast<int>(sizeof(T)), kBufferWord3);
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, u * kWave * 16, 0);
+                rv = make_uint4(v[0], v[1], v[2], v[3]);
+            } else {
+                rv = r[u];
+            }
+            // (a vector lies wholly inside or outside the row; selects, no branches)
+            cvt_vec<T>(rv, z);
+            const bool in = base < hi;
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) z[e] = in ? z[e] : -INFINITY;
+        } else {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) z[e] = (base + e < hi) ? Elem<T>::load(src, base + e) : -INFINITY;
+        }
+    };
+    if (kGreedy) {
+        // this lane's elements come in increasing index order, so a strict > keeps the lowest
+        // index among equal values; branch-free selects; kVec independent running maxima (one
+        // per vector position), merged at the end
+        float bv = -INFINITY;
+        int bi = INT_MAX;
+        float bvs[kVec];
+        int bis[kVec];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) { bvs[e] = -INFINITY; bis[e] = INT_MAX; }
+        auto scan = [&](int u) {
+            float z[kVec];
+            values(u, z);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) {
+                const int x = lo + (u * kWave + lane) * kVec + e;
+                const bool take = (z[e] > bvs[e]) & (x < hi);
+                bvs[e] = take ? z[e] : bvs[e];
+                bis[e] = take ? x : bis[e];
+            }
+        };
+        if constexpr (kVecOK && !kLean) {
+#pragma unroll
+            for (int u = 0; u < kWaveLoads; ++u) scan(u);
+        } else {
+#pragma nounroll
+            for (int u = 0; u < kWaveLoads; ++u) scan(u);
+        }
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) argmax_merge(bv, bi, bvs[e], bis[e]);
+        wave_argmax(bv, bi);
+        w0 = __float_as_uint(bv);
+        w1 = static_cast<uint32_t>(bi);
+    } else {
+        // online over the 16-byte vectors: the running sum is rescaled once per vector
+        // (branch-free: a reference of 0 while everything is -inf makes every term 0)
+        float m = -INFINITY, sum = 0.f;
+        auto fold = [&](int u) {
+            float z[kVec];
+            values(u, z);
+            float mu = m;
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) mu = fmaxf(mu, z[e]);
+            const float mref = (mu == -INFINITY) ? 0.f : mu;
+            float add = 0.f;
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) add += __builtin_amdgcn_exp2f((z[e] - mref) * k);
+            sum = sum * __builtin_amdgcn_exp2f((m - mref) * k) + add;
+            m = mu;
+        };
+        if constexpr (kVecOK && !kLean) {
+#pragma unroll
+            for (int u = 0; u < kWaveLoads; ++u) fold(u);
+        } else {
+#pragma nounroll
+            for (int u = 0; u < kWaveLoads; ++u) fold(u);
+        }
+        wave_max_sum(m, sum, k);
+        w0 = __float_as_uint(m);
+        w1 = __float_as_uint(sum);
+    }
+}
+
 // Streaming pass over tiles [t0, t1) of one row pair with the draw weights.  Tile i covers
 // kThreads * kVec consecutive elements; within a tile wave ww owns the contiguous segment of
 // 64 * kVec elements at (ww * 64) * kVec.  Segment sums go to seg[(i - t0) * kWaves + ww] if seg is
-// given.  Up to kPassBatch tiles are loaded together; the raw words of the last batch stay in rt /
+// given.  Up to kBatch tiles are loaded together; the raw words of the last batch stay in rt /
 // rd.  Returns the block's total (fp64, identical in all threads).
-template <typename T, bool kVecOK>
-__device__ double range_pass(const T* __restrict__ trow, const T* __restrict__ drow, int V, int t0,
+template <typename T, bool kVecOK, int kBatch = kPassBatch>
+__device__ __forceinline__ double range_pass(const T* __restrict__ trow, const T* __restrict__ drow, int V, int t0,
                              int t1, float mt, float md, float k, float p_scale, float q_scale,
                              const int32_t* excl, int nexcl,
-                             float* seg, double* red, uint4 (&rt)[kPassBatch], uint4 (&rd)[kPassBatch]) {
+                             float* seg, double* red, uint4 (&rt)[kBatch], uint4 (&rd)[kBatch]) {
     constexpr int kVec = Elem<T>::kVec;
     constexpr int kTile = kThreads * kVec;
     const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const bool use_q = q_scale != 0.f;
     double acc = 0.0;
-    for (int i0 = t0; i0 < t1; i0 += kPassBatch) {
+    for (int i0 = t0; i0 < t1; i0 += kBatch) {
         if (kVecOK) {
 #pragma unroll
-            for (int j = 0; j < kPassBatch; ++j) {
+            for (int j = 0; j < kBatch; ++j) {
                 const int base = (i0 + j) * kTile + threadIdx.x * kVec;
                 rt[j] = make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
                 rd[j] = rt[j];
@@ -227,7 +322,7 @@ __device__ double range_pass(const T* __restrict__ trow, const T* __restrict__ d
             }
         }
 #pragma unroll
-        for (int j = 0; j < kPassBatch; ++j) {
+        for (int j = 0; j < kBatch; ++j) {
             if (i0 + j >= t1) break;
             const int base = (i0 + j) * kTile + threadIdx.x * kVec;
             float zt[kVec], zd[kVec];
@@ -267,19 +362,53 @@ __device__ double range_pass(const T* __restrict__ trow, const T* __restrict__ d
     return tot;
 }
 
-// Team exchange: publish this workgroup's partial, return the P partials' exclusive prefix before
-// `rank` and the total (fp64, rank order; identical in every workgroup of the team).  The partials
-// stay in s_vals for the caller.
-__device__ void team_exchange(uint64_t* slots, int P, int rank, float mine, uint32_t tag, double* s_vals,
-                              int* s_to, double& before, double& total) {
-    if (threadIdx.x == 0) put_word(slots + rank, __float_as_uint(mine), tag);
-    if (static_cast<int>(threadIdx.x) < P) {
-        const uint32_t bits = (static_cast<int>(threadIdx.x) == rank)
-                                  ? __float_as_uint(mine)
-                                  : get_word(slots + threadIdx.x, tag, s_to);
-        s_vals[threadIdx.x] = static_cast<double>(__uint_as_float(bits));
+// The same pass, one tile at a time (few registers; the same sums in the same order, so the same
+// bits): computes a teammate's share when it runs late.
+template <typename T, bool kVecOK>
+__device__ __forceinline__ double range_pass_lean(const T* trow, const T* drow, int V, int t0, int t1, float mt,
+                                                  float md, float k, float p_scale, float q_scale,
+                                                  const int32_t* excl, int nexcl, double* red) {
+    uint4 xt[1], xd[1];
+    return range_pass<T, kVecOK, 1>(trow, drow, V, t0, t1, mt, md, k, p_scale, q_scale, excl, nexcl, nullptr, red,
+                                    xt, xd);
+}
+
+// Team exchange of fp64 partial sums (two tagged words each).  exchange_post publishes this
+// workgroup's partial, reads the team's P partials into s_vals, waiting at most `budget` for
+// each, and returns the mask of those still missing then (the same in every thread; P <= 64, so
+// wave 0 does the reads).  The caller computes each missing partial itself and hands it to
+// exchange_fill; exchange_sum adds them in rank order, so every workgroup of the team gets the
+// same prefix and total.
+__device__ __forceinline__ uint64_t exchange_post(uint64_t* slots, int P, int rank, double mine, uint32_t tag,
+                                                  uint64_t budget, double* s_vals, uint64_t* s_mask) {
+    const int t = threadIdx.x;
+    if (t == 0) put_double(slots + 2 * rank, mine, tag);
+    if (t < kWave) {
+        bool miss = false;
+        if (t < P) {
+            double v = mine;
+            if (t != rank && !get_double(slots + 2 * t, tag, budget, &v)) miss = true;
+            s_vals[t] = v;
+        }
+        const uint64_t m = __ballot(miss);
+        if (t == 0) *s_mask = m;
     }
     __syncthreads();
+    return *s_mask;
+}
+
+// Every thread stores the value (the same in all; each reads its own store afterwards); thread 0
+// publishes it for the other workgroups and counts it at *counter.
+__device__ __forceinline__ void exchange_fill(uint64_t* slots, int r, double v, uint32_t tag, double* s_vals,
+                                              uint64_t* counter) {
+    s_vals[r] = v;
+    if (threadIdx.x == 0) {
+        put_double(slots + 2 * r, v, tag);
+        __hip_atomic_fetch_add(counter, uint64_t{1}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+__device__ __forceinline__ void exchange_sum(const double* s_vals, int P, int rank, double& before, double& total) {
     before = 0.0;
     total = 0.0;
     for (int r = 0; r < P; ++r) {
@@ -295,8 +424,8 @@ __global__ void __launch_bounds__(kThreads)
 accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
               const int32_t* __restrict__ tokens, const int32_t* __restrict__ parent, int B, int n1,
               int V, int nchunk, int P, int rule, float k, double invT, uint64_t seed, uint64_t offset,
-              uint32_t tag, uint64_t* __restrict__ statw, uint64_t* __restrict__ partw,
-              uint32_t* __restrict__ err, int32_t* __restrict__ accept_len,
+              uint64_t* __restrict__ ctl, uint32_t* __restrict__ seen, uint64_t wait_ticks,
+              uint64_t* __restrict__ statw, uint64_t* __restrict__ partw, int32_t* __restrict__ accept_len,
               int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_nodes,
               float* __restrict__ p_tok, float* __restrict__ q_tok) {
     constexpr int kVec = Elem<T>::kVec;
@@ -328,7 +457,8 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
     __shared__ int wcount[kWaves];
     __shared__ float pv[kWaves];
     __shared__ int pi[kWaves];
-    __shared__ int s_bad, s_ni, s_cmd, s_row, s_n, s_sel, s_found, s_to, s_next, s_nexcl;
+    __shared__ int s_bad, s_ni, s_cmd, s_row, s_n, s_sel, s_found, s_late, s_next, s_nexcl;
+    __shared__ uint64_t s_mask;
     __shared__ float s_ps, s_qs;
     __shared__ double s_R, s_base;
 
@@ -340,11 +470,18 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
     const int tpb = (ntile + P - 1) / P;
     const int my_t0 = min(ntile, rank * tpb), my_t1 = min(ntile, my_t0 + tpb);
 
-    if (t == 0) s_to = 0;
+    // This launch's epoch: ctl[0] + 1 (0 is the tag of a zero-filled word), loaded in A of the
+    // workgroup's first sequence beside the parent array (so nothing waits for it alone).  Once
+    // a workgroup holds it, it stores it in its slot of `seen` (after the load has returned, so
+    // that no later read can see a newer epoch); workgroup 0 advances the epoch when it leaves,
+    // after it has seen every slot hold it.  (Plain stores, no contended counter; workgroup 0 is
+    // rarely the last to finish.)
+    uint32_t tag = 0, epoch_raw = 0;
+    if (t == 0) s_late = 0;     // (ordered by the barriers of A)
     for (int b = team; b < B; b += nteams) {
         const int64_t seq = static_cast<int64_t>(b) * n1;
         uint64_t* sw = statw + seq * nchunk * 4;
-        uint64_t* pw = partw + static_cast<int64_t>(b) * (n1 + 1) * P;
+        uint64_t* pw = partw + static_cast<int64_t>(b) * (n1 + 1) * P * 2;
 
         // -- A. stage and validate the parent array and the draft tokens.  The barriers of A and
         //    B order LDS only, so the loads of this wave's first statistics item, issued here when
@@ -363,6 +500,9 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
         for (int i = t; i < kMaskNodes * kMaskWords; i += kThreads) cmask[i / kMaskWords][i % kMaskWords] = 0;
         // (relaxed atomic loads: unlike loads of read-only arguments the compiler does not sink
         // them below the barrier, so they are issued ahead of the item's loads)
+        const bool first_seq = b == team;
+        if (first_seq)
+            epoch_raw = static_cast<uint32_t>(__hip_atomic_load(ctl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         const int pa0 = __hip_atomic_load(parent + seq + min(t, n1 - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         const int xa0 = __hip_atomic_load(tokens + seq + min(t, n1 - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         asm volatile("" ::: "memory");
@@ -384,6 +524,11 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
             tok[i] = x;
             const bool ok = (i == 0) ? (p == -1) : (p >= 0 && p < i && x >= 0 && x < V);
             if (!ok) s_bad = 1;
+        }
+        if (first_seq) {
+            tag = static_cast<uint32_t>(
+                __builtin_amdgcn_readfirstlane(static_cast<int>(epoch_raw == 0xFFFFFFFFu ? 1u : epoch_raw + 1u)));
+            if (t == 0) __hip_atomic_store(seen + blockIdx.x, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         lds_barrier();
         if (s_bad) {
@@ -519,85 +664,12 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
             const T* src = (isd ? draft : target) + (seq + row) * V;
             const int lo = c * kItem, hi = min(V, lo + kItem);
             uint64_t* slot = sw + (static_cast<int64_t>(row) * nchunk + c) * 4 + (isd ? 2 : 0);
-            // values of load u are converted from the raw words when used (two passes: max, then
-            // sum of exp), so only the raw 16-byte words stay in registers.  (The wave's first
-            // item, kk == w, was loaded in A when `pre`.)
-            if (kVecOK && !(pre && kk == wu)) load_item<T>(src, lo, hi, lane, r);
-            auto values = [&](int u, float* z) {
-                const int base = lo + (u * kWave + lane) * kVec;
-                if (kVecOK) {
-                    // (a vector lies wholly inside or outside the row; selects, no branches)
-                    cvt_vec<T>(r[u], z);
-                    const bool in = base < hi;
-#pragma unroll
-                    for (int e = 0; e < kVec; ++e) z[e] = in ? z[e] : -INFINITY;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < kVec; ++e) z[e] = (base + e < hi) ? Elem<T>::load(src, base + e) : -INFINITY;
-                }
-            };
-            if (kGreedy) {
-                float bv = -INFINITY;
-                int bi = INT_MAX;
-                // this lane's elements come in increasing index order, so a strict > keeps the
-                // lowest index among equal values; branch-free selects
-                // kVec independent running maxima (one per vector position), merged at the end
-                float bvs[kVec];
-                int bis[kVec];
-#pragma unroll
-                for (int e = 0; e < kVec; ++e) { bvs[e] = -INFINITY; bis[e] = INT_MAX; }
-                auto scan = [&](int u) {
-                    float z[kVec];
-                    values(u, z);
-#pragma unroll
-                    for (int e = 0; e < kVec; ++e) {
-                        const int x = lo + (u * kWave + lane) * kVec + e;
-                        const bool take = (z[e] > bvs[e]) & (x < hi);
-                        bvs[e] = take ? z[e] : bvs[e];
-                        bis[e] = take ? x : bis[e];
-                    }
-                };
-                if constexpr (kVecOK) {
-#pragma unroll
-                    for (int u = 0; u < kWaveLoads; ++u) scan(u);
-                } else {
-                    for (int u = 0; u < kWaveLoads; ++u) scan(u);
-                }
-#pragma unroll
-                for (int e = 0; e < kVec; ++e) argmax_merge(bv, bi, bvs[e], bis[e]);
-                wave_argmax(bv, bi);
-                if (lane == 0) {
-                    put_word(slot, __float_as_uint(bv), tag);
-                    put_word(slot + 1, static_cast<uint32_t>(bi), tag);
-                }
-            } else {
-                // online over the 16-byte vectors: the running sum is rescaled once per vector
-                // (branch-free: a reference of 0 while everything is -inf makes every term 0)
-                float m = -INFINITY, s = 0.f;
-                auto fold = [&](int u) {
-                    float z[kVec];
-                    values(u, z);
-                    float mu = m;
-#pragma unroll
-                    for (int e = 0; e < kVec; ++e) mu = fmaxf(mu, z[e]);
-                    const float mref = (mu == -INFINITY) ? 0.f : mu;
-                    float add = 0.f;
-#pragma unroll
-                    for (int e = 0; e < kVec; ++e) add += __builtin_amdgcn_exp2f((z[e] - mref) * k);
-                    s = s * __builtin_amdgcn_exp2f((m - mref) * k) + add;
-                    m = mu;
-                };
-                if constexpr (kVecOK) {
-#pragma unroll
-                    for (int u = 0; u < kWaveLoads; ++u) fold(u);
-                } else {
-                    for (int u = 0; u < kWaveLoads; ++u) fold(u);
-                }
-                wave_max_sum(m, s, k);
-                if (lane == 0) {
-                    put_word(slot, __float_as_uint(m), tag);
-                    put_word(slot + 1, __float_as_uint(s), tag);
-                }
+            // (the wave's first item, kk == w, was loaded in A when `pre`)
+            uint32_t w0, w1;
+            item_stats<T, kGreedy, kVecOK, false>(src, lo, hi, lane, k, r, pre && kk == wu, w0, w1);
+            if (lane == 0) {
+                put_word(slot, w0, tag);
+                put_word(slot + 1, w1, tag);
             }
             kk = nk;
         }
@@ -635,7 +707,7 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                     for (int j = 0; j < kStage; ++j) any |= need[j] && static_cast<uint32_t>(raw[j] >> 32) != tag;
                     return any;
                 };
-                if (missing() && !s_to) {
+                if (missing()) {
                     const uint64_t t0 = wall_clock64();
                     do {
                         __builtin_amdgcn_s_sleep(1);
@@ -644,8 +716,8 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                             if (need[j] && static_cast<uint32_t>(raw[j] >> 32) != tag)
                                 raw[j] = __hip_atomic_load(src + t + j * kThreads, __ATOMIC_RELAXED,
                                                            __HIP_MEMORY_SCOPE_AGENT);
-                        if (wall_clock64() - t0 > kTimeoutTicks) {
-                            s_to = 1;
+                        if (wall_clock64() - t0 > wait_ticks) {
+                            s_late = 1;
                             break;
                         }
                     } while (missing());
@@ -654,6 +726,42 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                 for (int j = 0; j < kStage; ++j)
                     if (need[j]) seg[t + j * kThreads] = __uint_as_float(static_cast<uint32_t>(raw[j]));
                 __syncthreads();
+                if (s_late) {
+                    // rare: words of the batch still missing after the wait.  Each wave checks 64
+                    // of the batch's items at a time (item q: words 2q, 2q + 1) and computes the
+                    // missing ones itself -- the bits their owner publishes -- then the batch is
+                    // read again.
+                    const int nq = nw / 2;
+                    for (int q0 = wu * kWave; q0 < nq; q0 += kThreads) {
+                        const int q = q0 + lane, i = 2 * q;
+                        bool m = false;
+                        if (q < nq && (i % 4 < 2 || (!kGreedy && rule != kRuleDeterministic && info[r0 + i / rw] != 0)))
+                            m = static_cast<uint32_t>(load_word(src + i) >> 32) != tag ||
+                                static_cast<uint32_t>(load_word(src + i + 1) >> 32) != tag;
+                        for (uint64_t mask = __ballot(m); mask; mask &= mask - 1) {
+                            const int iw = 2 * (q0 + __builtin_ctzll(mask));
+                            const int row = r0 + iw / rw, c = (iw % rw) / 4, side = (iw % 4) / 2;
+                            const int lo = c * kItem;
+                            uint32_t w0, w1;
+                            uint4 unused[kWaveLoads];
+                            item_stats<T, kGreedy, kVecOK, true>((side ? draft : target) + (seq + row) * V, lo,
+                                                                 min(V, lo + kItem), lane, k, unused, false, w0, w1);
+                            if (lane == 0) {
+                                put_word(src + iw, w0, tag);
+                                put_word(src + iw + 1, w1, tag);
+                            }
+                        }
+                    }
+                    __threadfence();       // (this workgroup's stores have reached the device cache)
+                    __syncthreads();
+                    if (t == 0) {
+                        s_late = 0;
+                        __hip_atomic_fetch_add(ctl + 1, uint64_t{1}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                    __syncthreads();
+                    r0 -= rb;
+                    continue;
+                }
                 // wave-uniform loop over groups of rpw rows; lane group `sub` owns one row
                 for (int k0 = w * rpw; k0 < nr; k0 += kWaves * rpw) {
                     const int rl = k0 + sub;
@@ -826,13 +934,25 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                 __syncthreads();
                 if (s_cmd != 0) break;
                 const int64_t rr = (seq + s_row) * V;
-                const double mine = range_pass<T, kVecOK>(target + rr, draft + rr, V, my_t0, my_t1, Mt[s_row],
-                                                          Md[s_row], k, s_ps, s_qs, ilist, 0, nullptr, red, rt, rd);
+                const int row = s_row;
+                const float ps = s_ps, qs = s_qs;
+                const double mine = range_pass<T, kVecOK>(target + rr, draft + rr, V, my_t0, my_t1, Mt[row], Md[row],
+                                                          k, ps, qs, ilist, 0, nullptr, red, rt, rd);
                 double Rn = mine;
                 if (P > 1) {
+                    uint64_t* slots = pw + static_cast<int64_t>(npass) * P * 2;
+                    // teammates whose share did not come in time: computed here
+                    for (uint64_t miss = exchange_post(slots, P, rank, mine, tag, wait_ticks, s_vals, &s_mask); miss;
+                         miss &= miss - 1) {
+                        const int r = __builtin_ctzll(miss);
+                        const int a0 = min(ntile, r * tpb), a1 = min(ntile, a0 + tpb);
+                        exchange_fill(slots, r,
+                                      range_pass_lean<T, kVecOK>(target + rr, draft + rr, V, a0, a1, Mt[row], Md[row], k,
+                                                                 ps, qs, ilist, 0, red),
+                                      tag, s_vals, ctl + 2);
+                    }
                     double before_unused;
-                    team_exchange(pw + static_cast<int64_t>(npass) * P, P, rank, static_cast<float>(mine), tag,
-                                  s_vals, &s_to, before_unused, Rn);
+                    exchange_sum(s_vals, P, rank, before_unused, Rn);
                 }
                 ++npass;
                 __syncthreads();
@@ -854,10 +974,6 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
         if (cmd == 2) {
             if (rank == 0 && t == 0) out_tokens[seq + na] = info[e];
             __syncthreads();
-            if (s_to && t == 0) {
-                atomicOr(err, 1u);
-                if (rank == 0) accept_len[b] = -2;
-            }
             continue;
         }
 
@@ -869,9 +985,19 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
         const double mine = range_pass<T, kVecOK>(target + rr, draft + rr, V, my_t0, my_t1, mt, md, k, ps, qs,
                                                   ilist, nexcl, seg, red, rt, rd);
         double before = 0.0, W = mine;
-        if (P > 1)
-            team_exchange(pw + static_cast<int64_t>(npass) * P, P, rank, static_cast<float>(mine), tag, s_vals,
-                          &s_to, before, W);
+        if (P > 1) {
+            uint64_t* slots = pw + static_cast<int64_t>(npass) * P * 2;
+            for (uint64_t miss = exchange_post(slots, P, rank, mine, tag, wait_ticks, s_vals, &s_mask); miss;
+                 miss &= miss - 1) {
+                const int r = __builtin_ctzll(miss);
+                const int a0 = min(ntile, r * tpb), a1 = min(ntile, a0 + tpb);
+                exchange_fill(slots, r,
+                              range_pass_lean<T, kVecOK>(target + rr, draft + rr, V, a0, a1, mt, md, k, ps, qs, ilist,
+                                                         nexcl, red),
+                              tag, s_vals, ctl + 2);
+            }
+            exchange_sum(s_vals, P, rank, before, W);
+        }
         const double thr = ures[e] * W;
         // the owner: the first rank whose running sum passes thr (or, if rounding left thr at or
         // above the total, the last rank with mass); every workgroup finds the same one
@@ -1017,10 +1143,13 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
             }
         }
         __syncthreads();
-        if (s_to && t == 0) {
-            atomicOr(err, 1u);
-            if (rank == 0) accept_len[b] = -2;
-        }
+    }
+    if (blockIdx.x == 0) {      // (every workgroup reaches A of its first sequence: these waits end)
+        for (int i = t; i < static_cast<int>(gridDim.x); i += kThreads)
+            while (__hip_atomic_load(seen + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag)
+                __builtin_amdgcn_s_sleep(1);
+        __syncthreads();
+        if (t == 0) __hip_atomic_store(ctl, static_cast<uint64_t>(tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -1035,11 +1164,18 @@ int team_size(int B) {
 template <typename T>
 int chunks_of(int V) { return (V + item_elems<T>() - 1) / item_elems<T>(); }
 
-uint32_t next_tag() {
-    // distinct for 2^31 consecutive launches, never 0, away from small integers
-    static std::atomic<uint32_t> counter{0x2545F491u};
-    const uint32_t c = counter.fetch_add(1u, std::memory_order_relaxed);
-    return (c * 0x9E3779B1u) | 0x80000000u;
+// How long a workgroup waits for a teammate's values before computing them itself: 100 us, or
+// SPECV_ACCEPT_WAIT_US (microseconds; 0 makes every wait that is not already over compute the
+// values here, which the tests use to run that path).
+uint64_t wait_ticks() {
+    const char* e = std::getenv("SPECV_ACCEPT_WAIT_US");
+    long us = 100;
+    if (e && *e) {
+        char* end = nullptr;
+        const long v = std::strtol(e, &end, 10);
+        if (end && *end == '\0' && v >= 0 && v <= 10000000) us = v;
+    }
+    return static_cast<uint64_t>(us) * 100u;      // the wall clock runs at 100 MHz
 }
 
 template <typename T, bool kGreedy, bool kVecOK>
@@ -1048,16 +1184,16 @@ hipError_t launch_kernel(const AcceptArgs& a, hipStream_t stream) {
     int P = team_size(a.B);
     const AcceptLayout lay(a.B, a.n1, nchunk, P);
     char* ws = static_cast<char*>(a.workspace);
+    uint64_t* ctl = reinterpret_cast<uint64_t*>(ws + lay.ctl);
+    uint32_t* seen = reinterpret_cast<uint32_t*>(ws + lay.seen);
     uint64_t* statw = reinterpret_cast<uint64_t*>(ws + lay.stat);
     uint64_t* partw = reinterpret_cast<uint64_t*>(ws + lay.part);
-    uint32_t* err = reinterpret_cast<uint32_t*>(ws + lay.err);
     const void* fn = reinterpret_cast<const void*>(&accept_kernel<T, kGreedy, kVecOK>);
-    static int per_cu = -1;
-    if (per_cu < 0) {
+    static std::atomic<int> occupancy[64];
+    const int per_cu = cached_per_device(occupancy, [fn](int) {
         int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kThreads, 0) != hipSuccess || nb < 1) nb = 1;
-        per_cu = nb;
-    }
+        return (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kThreads, 0) == hipSuccess && nb > 0) ? nb : 1;
+    });
     const int capacity = per_cu * device_cu_count();
     const int nteams = std::max(1, std::min(a.B, capacity / P));
     const int grid = nteams * P;
@@ -1068,7 +1204,7 @@ hipError_t launch_kernel(const AcceptArgs& a, hipStream_t stream) {
     double invT = kGreedy ? 0.0 : 1.0 / static_cast<double>(a.temperature);
     float k = kGreedy ? 0.f : static_cast<float>(1.4426950408889634 * invT);   // log2(e) / T
     uint64_t seed = a.seed, offset = a.offset;
-    uint32_t tag = next_tag();
+    uint64_t wt = wait_ticks();
     const int32_t* tokens = a.tokens;
     const int32_t* parent = a.parent;
     int32_t* accept_len = a.accept_len;
@@ -1078,7 +1214,7 @@ hipError_t launch_kernel(const AcceptArgs& a, hipStream_t stream) {
     float* q_tok = a.q_tok;
     int rule = a.rule;
     hipLaunchKernelGGL((accept_kernel<T, kGreedy, kVecOK>), dim3(grid), dim3(kThreads), 0, stream, target, draft,
-                       tokens, parent, B, n1, V, nchunk, P, rule, k, invT, seed, offset, tag, statw, partw, err,
+                       tokens, parent, B, n1, V, nchunk, P, rule, k, invT, seed, offset, ctl, seen, wt, statw, partw,
                        accept_len, out_tokens, out_nodes, p_tok, q_tok);
     return hipGetLastError();
 }

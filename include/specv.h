@@ -178,12 +178,14 @@ size_t specv_attn_workspace_bytes(int32_t B, int32_t K, int32_t Hq, int32_t Hkv,
  *                 uniform if the walk ends there; a word w maps to
  *                 (2 * (w >> 12) + 1) * 2^-53.  Advance offset once per call.
  *   accept_len    [B] int32: number of accepted draft nodes; -1 if the parent
- *                 array is invalid or a draft token is outside [0, V); -2 if
- *                 the sequence was not finished because the workgroups that
- *                 share it could not all run at once (another process holding
- *                 compute units); each wait gives up after about 0.5 s, so the
- *                 call always completes; the other outputs of a -2 sequence
- *                 are then unspecified.
+ *                 array is invalid or a draft token is outside [0, V).  The
+ *                 result does not depend on how the device schedules the
+ *                 call: the workgroups that share a sequence never wait on one
+ *                 another for longer than a budget (100 us; environment
+ *                 variable SPECV_ACCEPT_WAIT_US, read at each call, sets it
+ *                 in microseconds), after which a workgroup computes the
+ *                 values it waits for itself, bit for bit what their owner
+ *                 computes.
  *   out_nodes     [B][K+1] int32: accepted node ids from the first level down,
  *                 then -1
  *   out_tokens    [B][K+1] int32: the accepted tokens, then the resampled /
@@ -191,7 +193,11 @@ size_t specv_attn_workspace_bytes(int32_t B, int32_t K, int32_t Hq, int32_t Hkv,
  *   p_tok, q_tok  [B][K+1] float32 or NULL: p_parent(v)(tokens[v]) and
  *                 q_parent(v)(tokens[v]) for every v >= 1; NaN at v == 0, at
  *                 T == 0 and for invalid sequences
- *   workspace / workspace_bytes: at least specv_accept_workspace_bytes(...)
+ *   workspace / workspace_bytes: at least specv_accept_workspace_bytes(...),
+ *                 zero-filled by the caller before its first use; the calls
+ *                 keep it valid afterwards (its first 128 bytes carry a launch
+ *                 counter from call to call, so it is not cleared again, and a
+ *                 call captured in a graph stays correct on every replay).
  *
  * Ownership: every pointer is device memory owned by the caller; the call only
  * enqueues work on `stream` and returns.  Calls that share a workspace must be
