@@ -8,6 +8,7 @@ library has not been built this import fails.
   build_tree_mask(parent)                                  -> mask, depth, status
   tree_attn_verify(q, k_cache, v_cache, ctx_len, mask)     -> out, lse
   accept_resample(target, draft, tokens, parent, T, seed, offset) -> AcceptResult
+  accept_resample_noalloc(...)   the same through the entry point that allocates nothing
   kv_commit(k_cache, v_cache, ctx_len, accept_len, out_nodes)     -> new_ctx_len
   tree_expand(draft_logits, frontier, tree, k, T, keep)           -> new_frontier (tree updated)
   verify_layer(x, weights, k_cache, v_cache, ctx_len, mask, depth, Hq) -> out (caches written)
@@ -23,6 +24,7 @@ from ._lib import (  # noqa: F401
     build_tree_mask,
     tree_attn_verify,
     accept_resample,
+    accept_resample_noalloc,
     kv_commit,
     DraftTree,
     tree_expand,

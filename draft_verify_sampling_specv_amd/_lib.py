@@ -51,6 +51,12 @@ lib.specv_accept_resample_rule.argtypes = [
     ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int,
     ctypes.c_uint64, ctypes.c_uint64,
     _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+lib.specv_accept_resample_rule_noalloc.restype = ctypes.c_int
+lib.specv_accept_resample_rule_noalloc.argtypes = [
+    _vp, _vp, ctypes.c_int, _vp, _vp,
+    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int,
+    ctypes.c_uint64, ctypes.c_uint64,
+    _vp, _vp, _vp, _vp, _vp, _vp]
 SIBLING_RULES = {"without_replacement": 0, "iid": 1, "deterministic": 2}
 
 lib.specv_tree_expand_workspace_bytes.restype = ctypes.c_size_t
@@ -227,6 +233,35 @@ def accept_resample(target_logits, draft_logits, tokens, parent, temperature, se
         _ptr(r.accept_len), _ptr(r.out_tokens), _ptr(r.out_nodes),
         _ptr(r.p_tok) if with_probs else None, _ptr(r.q_tok) if with_probs else None,
         _ptr(bufs.workspace), bufs.workspace.numel(), _stream()))
+    return r
+
+
+def accept_resample_noalloc(target_logits, draft_logits, tokens, parent, temperature, seed=0, offset=0,
+                            result=None, with_probs=True, siblings="without_replacement"):
+    """accept_resample through the entry point that allocates nothing (its workspace is built
+    into the library, 8 MiB per device); `result` (an AcceptResult) may be preallocated."""
+    target_logits = _dev(target_logits)
+    if draft_logits is not None:
+        draft_logits = _dev(draft_logits)
+        if draft_logits.dtype != target_logits.dtype or draft_logits.shape != target_logits.shape:
+            raise TypeError("draft_logits must match target_logits in dtype and shape")
+    tokens, parent = _dev(tokens, torch.int32), _dev(parent, torch.int32)
+    B, n1, V = target_logits.shape
+    if tokens.shape != (B, n1) or parent.shape != (B, n1):
+        raise ValueError("tokens and parent must be [B][K+1]")
+    if siblings not in SIBLING_RULES:
+        raise ValueError(f"siblings must be one of {sorted(SIBLING_RULES)}")
+    if result is None:
+        i32 = dict(dtype=torch.int32, device=target_logits.device)
+        f32 = dict(dtype=torch.float32, device=target_logits.device)
+        result = AcceptResult(torch.empty((B,), **i32), torch.empty((B, n1), **i32), torch.empty((B, n1), **i32),
+                              torch.empty((B, n1), **f32), torch.empty((B, n1), **f32))
+    r = result
+    _check("specv_accept_resample_rule_noalloc", lib.specv_accept_resample_rule_noalloc(
+        _ptr(target_logits), _ptr(draft_logits), _dtype_code(target_logits), _ptr(tokens), _ptr(parent),
+        B, n1 - 1, V, float(temperature), SIBLING_RULES[siblings], int(seed), int(offset),
+        _ptr(r.accept_len), _ptr(r.out_tokens), _ptr(r.out_nodes),
+        _ptr(r.p_tok) if with_probs else None, _ptr(r.q_tok) if with_probs else None, _stream()))
     return r
 
 

@@ -1234,6 +1234,32 @@ size_t accept_workspace_bytes(int B, int n1, int V, bool bf16) {
     return AcceptLayout(B, n1, nchunk, team_size(B)).total;
 }
 
+// The built-in workspace of the allocation-free entry point: zero when the library is loaded (the
+// epoch words then hold 0), kept valid by the calls that use it.  One copy per device, held until
+// the process ends; calls that overlap on one device race on it.
+namespace {
+static __device__ __align__(256) unsigned char scratch[kAcceptScratchBytes];
+}  // namespace
+
+hipError_t accept_scratch(void** ptr) {
+    // the array's device address on the current device (the host-side name of the array is not
+    // a device address), looked up once per device
+    static std::atomic<void*> addr[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
+}
+
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream) {
     const bool vec = aligned16(a.target) && (a.draft == nullptr || aligned16(a.draft));
     if (a.bf16) {

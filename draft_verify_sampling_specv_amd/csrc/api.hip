@@ -133,13 +133,15 @@ size_t specv_accept_workspace_bytes(int32_t B, int32_t K, int32_t V, specv_dtype
     return specv::accept_workspace_bytes(B, K + 1, V, logits_dtype == SPECV_BF16);
 }
 
-specv_status specv_accept_resample_rule(const void* target_logits, const void* draft_logits,
-                                        specv_dtype logits_dtype, const int32_t* tokens,
-                                        const int32_t* parent, int32_t B, int32_t K, int32_t V,
-                                        float temperature, specv_sibling_rule rule, uint64_t seed,
-                                        uint64_t offset, int32_t* accept_len, int32_t* out_tokens,
-                                        int32_t* out_nodes, float* p_tok, float* q_tok, void* workspace,
-                                        size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// Arguments of the accept entry points, checked; on success `a` is filled (workspace unset) and
+// `need` is the workspace size.  B == 0 returns SPECV_OK with a.B == 0 (nothing to launch).
+specv_status accept_args(const void* target_logits, const void* draft_logits, specv_dtype logits_dtype,
+                         const int32_t* tokens, const int32_t* parent, int32_t B, int32_t K, int32_t V,
+                         float temperature, specv_sibling_rule rule, uint64_t seed, uint64_t offset,
+                         int32_t* accept_len, int32_t* out_tokens, int32_t* out_nodes, float* p_tok, float* q_tok,
+                         specv::AcceptArgs& a, size_t& need) {
     if (B < 0) return fail(SPECV_ERR_INVALID_ARG, "B = %d < 0", B);
     if (K < 0 || K > SPECV_MAX_NODES - 1)
         return fail(SPECV_ERR_INVALID_ARG, "K = %d outside [0, %d]", K, SPECV_MAX_NODES - 1);
@@ -153,6 +155,8 @@ specv_status specv_accept_resample_rule(const void* target_logits, const void* d
     if (logits_dtype != SPECV_F32 && logits_dtype != SPECV_BF16)
         return fail(SPECV_ERR_UNSUPPORTED, "dtype %d not supported", static_cast<int>(logits_dtype));
     if (!fits_i32({B, int64_t(K) + 1})) return fail(SPECV_ERR_INVALID_ARG, "B * (K + 1) exceeds 2^31 - 1");
+    a = specv::AcceptArgs{};
+    need = 0;
     if (B == 0) return ok();
     if (!target_logits || !tokens || !parent || !accept_len || !out_tokens || !out_nodes)
         return fail(SPECV_ERR_INVALID_ARG, "NULL pointer argument");
@@ -160,14 +164,56 @@ specv_status specv_accept_resample_rule(const void* target_logits, const void* d
     if (need_draft && !draft_logits)
         return fail(SPECV_ERR_INVALID_ARG,
                     "draft_logits may be NULL only at temperature 0 or for deterministic siblings");
-    const size_t need = specv::accept_workspace_bytes(B, K + 1, V, logits_dtype == SPECV_BF16);
+    need = specv::accept_workspace_bytes(B, K + 1, V, logits_dtype == SPECV_BF16);
+    a = specv::AcceptArgs{target_logits, need_draft ? draft_logits : nullptr,
+                          logits_dtype == SPECV_BF16, tokens, parent, B, K + 1, V, temperature,
+                          static_cast<int>(rule), seed, offset, accept_len, out_tokens, out_nodes, p_tok, q_tok,
+                          nullptr};
+    return SPECV_OK;
+}
+
+}  // namespace
+
+specv_status specv_accept_resample_rule(const void* target_logits, const void* draft_logits,
+                                        specv_dtype logits_dtype, const int32_t* tokens,
+                                        const int32_t* parent, int32_t B, int32_t K, int32_t V,
+                                        float temperature, specv_sibling_rule rule, uint64_t seed,
+                                        uint64_t offset, int32_t* accept_len, int32_t* out_tokens,
+                                        int32_t* out_nodes, float* p_tok, float* q_tok, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+    specv::AcceptArgs a;
+    size_t need = 0;
+    const specv_status st = accept_args(target_logits, draft_logits, logits_dtype, tokens, parent, B, K, V,
+                                        temperature, rule, seed, offset, accept_len, out_tokens, out_nodes, p_tok,
+                                        q_tok, a, need);
+    if (st != SPECV_OK || a.B == 0) return st;
     if (!workspace || workspace_bytes < need)
         return fail(SPECV_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
-    specv::AcceptArgs a{target_logits, need_draft ? draft_logits : nullptr,
-                        logits_dtype == SPECV_BF16, tokens, parent, B, K + 1, V, temperature,
-                        static_cast<int>(rule), seed, offset, accept_len, out_tokens, out_nodes, p_tok, q_tok,
-                        workspace};
+    a.workspace = workspace;
     return hip_status(specv::launch_accept(a, stream), "accept_resample");
+}
+
+specv_status specv_accept_resample_rule_noalloc(const void* target_logits, const void* draft_logits,
+                                                specv_dtype logits_dtype, const int32_t* tokens,
+                                                const int32_t* parent, int32_t B, int32_t K, int32_t V,
+                                                float temperature, specv_sibling_rule rule, uint64_t seed,
+                                                uint64_t offset, int32_t* accept_len, int32_t* out_tokens,
+                                                int32_t* out_nodes, float* p_tok, float* q_tok,
+                                                hipStream_t stream) {
+    specv::AcceptArgs a;
+    size_t need = 0;
+    const specv_status st = accept_args(target_logits, draft_logits, logits_dtype, tokens, parent, B, K, V,
+                                        temperature, rule, seed, offset, accept_len, out_tokens, out_nodes, p_tok,
+                                        q_tok, a, need);
+    if (st != SPECV_OK || a.B == 0) return st;
+    if (need > specv::kAcceptScratchBytes)
+        return fail(SPECV_ERR_WORKSPACE, "this call needs %zu bytes of workspace; the built-in one holds %zu",
+                    need, specv::kAcceptScratchBytes);
+    void* ws = nullptr;
+    const hipError_t e = specv::accept_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, "accept_resample_noalloc (workspace address)");
+    a.workspace = ws;
+    return hip_status(specv::launch_accept(a, stream), "accept_resample_noalloc");
 }
 
 specv_status specv_accept_resample(const void* target_logits, const void* draft_logits,

@@ -62,6 +62,9 @@ struct AcceptArgs {
 
 size_t accept_workspace_bytes(int B, int n1, int V, bool bf16);
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
+// The allocation-free variant's built-in workspace: size, and its address on the current device.
+constexpr size_t kAcceptScratchBytes = size_t(8) << 20;
+hipError_t accept_scratch(void** ptr);
 
 // ------------------------------------------------------------------------------------ tree expansion
 constexpr int kExpandMaxK = 16;        // children per frontier node at most

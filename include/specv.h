@@ -262,6 +262,27 @@ specv_status specv_accept_resample_rule(const void* target_logits, const void* d
                                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * specv_accept_resample_rule without a workspace argument, for callers that
+ * cannot allocate device memory (code under graph capture, tight serving
+ * loops, harnesses that forbid allocation).  It allocates nothing: the
+ * workspace is an 8 MiB array built into the library, one per device, zero
+ * when the library is loaded and kept valid by these calls; it persists until
+ * the process ends.  Arguments, outputs and errors are those of
+ * specv_accept_resample_rule, except SPECV_ERR_WORKSPACE when the call needs
+ * more than 8 MiB of workspace (specv_accept_workspace_bytes; e.g. B = 64,
+ * K = 8, V = 151936 in fp32 needs about 0.8 MiB).  Calls that overlap on one
+ * device (two streams, two threads without ordering) race on the array and
+ * must not be made; calls ordered on one stream are safe.
+ */
+specv_status specv_accept_resample_rule_noalloc(const void* target_logits, const void* draft_logits,
+                                                specv_dtype logits_dtype,
+                                                const int32_t* tokens, const int32_t* parent,
+                                                int32_t B, int32_t K, int32_t V, float temperature,
+                                                specv_sibling_rule rule, uint64_t seed, uint64_t offset,
+                                                int32_t* accept_len, int32_t* out_tokens, int32_t* out_nodes,
+                                                float* p_tok, float* q_tok, hipStream_t stream);
+
+/*
  * KV-cache commit after a verify step: keep the accepted path, drop the rest.
  *
  * [SD-review] §4 (limitations): the cache entries of rejected drafts have to

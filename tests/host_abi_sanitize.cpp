@@ -104,6 +104,17 @@ int main() {
                                                      static_cast<specv_sibling_rule>(9), 1, 0, i32, i32, i32,
                                                      nullptr, nullptr, ws, cw, nullptr), I);
     expect("accept workspace query", static_cast<int>(specv_accept_workspace_bytes(4, 5, 0, SPECV_BF16)), 0);
+    auto noalloc = [&](int B, int K, int V, float T, const void* d) {
+        return specv_accept_resample_rule_noalloc(dev, d, SPECV_BF16, i32, i32, B, K, V, T,
+                                                  SPECV_SIBLINGS_WITHOUT_REPLACEMENT, 1, 0, i32, i32, i32, nullptr,
+                                                  nullptr, nullptr);
+    };
+    expect("noalloc B < 0", noalloc(-1, 5, 1000, 1.f, dev), I);
+    expect("noalloc K INT_MAX", noalloc(4, IMAX, 1000, 1.f, dev), I);
+    expect("noalloc T nan", noalloc(4, 5, 1000, std::nanf(""), dev), I);
+    expect("noalloc draft null", noalloc(4, 5, 1000, 1.f, nullptr), I);
+    expect("noalloc empty", noalloc(0, 5, 1000, 1.f, dev), SPECV_OK);
+    expect("noalloc beyond its workspace", noalloc(256, 128, 262144, 1.f, dev), W);
     expect("accept K INT_MAX", accept(4, IMAX, 1000, 1.f, dev, ws, cw), I);
     expect("accept B INT_MAX", accept(IMAX, 5, 1000, 1.f, dev, ws, cw), I);
     expect("accept V INT_MAX", accept(4, 5, IMAX, 1.f, dev, ws, cw), I);
