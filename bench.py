@@ -13,8 +13,13 @@ Prints ONE JSON line.  Extra legs:
 
   verify_layer  one whole target layer over the same 192 rows (specv_verify_layer): its time,
                 the attention call's share of it, and the weight-streaming rate of the rest.
+  configs       every configuration of the workload list (tiny, chain, chain-greedy, eagle,
+                stress, ptd): us per kernel, HBM fractions of accept and attention, MFMA fraction of
+                attention, positions/s accept-only and verify, alpha and the expected tokens per
+                step against the measured mean.
 
-  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-layer] [--copy-probe]
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-layer] [--no-configs]
+                  [--config NAME] [--copy-probe]
 --copy-probe only runs a device-to-device copy of known size (to calibrate HBM byte counters).
 """
 
@@ -89,6 +94,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline leg")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--no-layer", action="store_true", help="skip the one-layer measurement")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration legs")
     ap.add_argument("--config", default=None, choices=sorted(CONFIGS),
                     help="measure every kernel on one configuration (prints a per-config JSON line "
                          "instead of the headline line)")
@@ -139,7 +145,7 @@ def main():
         copy_probe(torch)
         return
     if args.config:
-        measure_config(args.config, args, torch, specv, workloads)
+        print(json.dumps(measure_config(args.config, args, torch, specv, workloads)))
         return
 
     n1 = K + 1
@@ -250,6 +256,8 @@ def main():
     out = {
         "metric": METRIC,
         "value": positions / (ms_step * 1e-3),
+        "value_reading": "verify: B*K draft positions / time of one whole step (mask build + tree attention, "
+                         "one layer + accept/resample); the accept-only reading is accept_only_positions_per_s",
         "unit": "positions/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -283,6 +291,12 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_layer:
         out["verify_layer"] = measure_layer(torch, specv, max(10, args.steps // 4))
+    if not args.no_configs:
+        # every configuration of the workload list, one after another (inputs resident in HBM)
+        out["configs"] = {}
+        for name in ("tiny", "chain", "chain-greedy", "eagle", "stress", "ptd"):
+            log(f"config {name}")
+            out["configs"][name] = measure_config(name, args, torch, specv, workloads)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(acc_sets0_w, a0)
     print(json.dumps(out))
@@ -459,11 +473,14 @@ def measure_config(name, args, torch, specv, workloads):
     out_nodes = r.out_nodes.cpu().numpy()
     # KV-cache commit of the accepted paths (the step after the verify step, not part of it), on a
     # copy of the cache; every call moves the same rows
-    kcc, vcc = kc.clone(), vc.clone()
-    new_ctx = torch.empty_like(cl)
-    ms_commit = timed(lambda i: specv.kv_commit(kcc, vcc, cl, r.accept_len, r.out_nodes, out=new_ctx), steps)
-    moved = sum(1 for b in range(B) for d in range(1, int(accept_len[b]) + 1) if out_nodes[b, d - 1] != d)
-    del kcc, vcc
+    # (the tiny case's accept trials and its attention tree are different batches: no commit leg)
+    ms_commit, moved = None, 0
+    if (B, n1) == tuple(a.parent.shape):
+        kcc, vcc = kc.clone(), vc.clone()
+        new_ctx = torch.empty_like(cl)
+        ms_commit = timed(lambda i: specv.kv_commit(kcc, vcc, cl, r.accept_len, r.out_nodes, out=new_ctx), steps)
+        moved = sum(1 for b in range(B) for d in range(1, int(accept_len[b]) + 1) if out_nodes[b, d - 1] != d)
+        del kcc, vcc
 
     # algorithmic work
     pa = w.parent
@@ -498,8 +515,56 @@ def measure_config(name, args, torch, specv, workloads):
         "positions_per_s_accept_only": positions / (ms_acc * 1e-3),
         "positions_per_s_verify": positions / ((ms_mask + ms_attn + ms_acc) * 1e-3),
         "mean_tokens_per_step": float(np.mean(accept_len + 1)),
+        "acceptance": acceptance_stats(torch, w, tl, dl, accept_len),
     }
-    print(json.dumps(out))
+    del sets_acc, sets_att, tl, dl, q, kc, vc
+    torch.cuda.empty_cache()
+    return out
+
+
+def acceptance_stats(torch, w, tl, dl, accept_len):
+    """Per-position acceptance rate alpha = sum_x min(p(x), q(x)) (the lesson, "Expected Speedup";
+    the review, section 2 "Efficiency analysis") from the logits of the draft nodes' parent rows,
+    and, for chains, the expected tokens per step (1 - alpha^(K+1)) / (1 - alpha) beside the
+    measured mean of accept_len + 1.  Computed here with torch (a measurement, not the verify
+    path)."""
+    B, n1 = w.tokens.shape
+    out = {"mean_tokens_measured": float(np.mean(accept_len + 1))}
+    if w.T <= 0 or dl is None or n1 < 2:
+        out["note"] = "greedy or no draft positions: alpha not defined by the sampling rule"
+        return out
+    chain = bool(np.all(w.parent[:, 1:] == np.arange(n1 - 1)[None, :]))
+
+    def alpha_rows(t_rows, d_rows):
+        pt = torch.softmax(t_rows.float() / w.T, dim=-1)
+        qt = torch.softmax(d_rows.float() / w.T, dim=-1)
+        return torch.minimum(pt, qt).sum(dim=-1).double().cpu().numpy().ravel()
+
+    if chain:
+        a = np.concatenate([alpha_rows(tl[b0:b0 + 256, :n1 - 1], dl[b0:b0 + 256, :n1 - 1])
+                            for b0 in range(0, B, 256)])
+    else:
+        a = np.concatenate([alpha_rows(tl[b, sorted(set(int(x) for x in w.parent[b, 1:]))],
+                                       dl[b, sorted(set(int(x) for x in w.parent[b, 1:]))]) for b in range(B)])
+    out["alpha_mean"] = float(a.mean())
+    out["alpha_min"] = float(a.min())
+    out["alpha_max"] = float(a.max())
+    if chain:
+        K = n1 - 1
+        al = float(a.mean())
+        out["expected_tokens_closed_form"] = (1.0 - al ** (K + 1)) / (1.0 - al) if al < 1 else float(K + 1)
+        out["closed_form"] = "(1 - alpha^(K+1)) / (1 - alpha), alpha = mean over positions"
+        # the same expectation with each position's own alpha (the draft tokens here are drawn
+        # independently per position, so acceptances are independent Bernoulli(alpha_j)):
+        # E = sum_k prod_{j<k} alpha_j, averaged over the sequences
+        ab = a.reshape(B, K)
+        out["expected_tokens_per_position_alpha"] = float(np.mean(
+            1.0 + np.sum(np.cumprod(ab, axis=1), axis=1)))
+        sd = float(np.std(accept_len + 1))
+        out["measured_std_error"] = sd / math.sqrt(B)
+    else:
+        out["note"] = "tree: alpha over the internal nodes' rows; the chain closed form does not apply"
+    return out
 
 
 def cpu_baseline(w, a):
