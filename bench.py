@@ -57,7 +57,7 @@ MFMA_PEAK_TFLOPS = 2500.0
 
 # HBM traffic of the dominant kernel (attn_decode_kernel<128, 8, 1>) per call on this workload, from
 # two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), each scaled by what the same
-# counter reads for a 256 MiB device-to-device copy (FETCH_SIZE 131084.0 KiB -> x1.99982,
+# counter reads for a 256 MiB device-to-device copy (FETCH_SIZE 131084.6 KiB -> x1.99981,
 # WRITE_SIZE 262144.0 KiB -> x1.0).  Summaries and commands: profiles/chain_step_pmc.md.
 # Valid only for the kernel sources it was measured on (their SHA-256 below); null otherwise.
 ATTN_TRAFFIC = {
@@ -65,8 +65,8 @@ ATTN_TRAFFIC = {
                 "draft_verify_sampling_specv_amd/csrc/attn_common.h",
                 "draft_verify_sampling_specv_amd/csrc/common.h",
                 "draft_verify_sampling_specv_amd/csrc/kernels.h"],
-    "sha256": "96874cbf6e4baf38366ddaa35773e398801dff37bb4f2d359c9b0824e053f94d",
-    "fetch_kib": 132448.5, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131084.0, "write_scale": 1.0,
+    "sha256": "5ef2ac6e742f0c82c2d78172ab991431b472bcba68b4bcca707153d8013a718f",
+    "fetch_kib": 132455.2, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131084.6, "write_scale": 1.0,
 }
 
 
