@@ -17,7 +17,8 @@
 // the vocabulary is split over the P workgroups of the team:
 //   1. statistics: items (row, chunk of 64 * kVec * kWaveLoads elements), one wave per item, over
 //      every target row and the draft rows of internal nodes, coalesced 16-byte loads, one exp per
-//      element: per-chunk (max, sum of exp2((z - max) log2e / T)), or (max, argmax) at T = 0.
+//      element: per-chunk (R, sum of exp2(z k - R)) with k = log2e / T and the reference R the
+//      chunk's largest z k (one fma per term), or (max, argmax) at T = 0.
 //   2. every workgroup of the team combines the chunk statistics (fp64 above chunk level) and
 //      builds per-node tables in LDS (p, q of each draft token under its parent's rows, p/q, both
 //      Philox uniforms, first child / next sibling / repeated-token links);
@@ -41,11 +42,14 @@
 // only.  Outputs are written by fixed workgroups (rank 0; the owner of the draw's CDF crossing),
 // which all run eventually.
 //
-// Precision: per-element exponentials in fp32 (v_exp_f32), chunk and segment sums in fp32,
-// everything above (row normalisers, ratios, c, Q, R, the CDF threshold and prefixes) in fp64;
-// team partial sums cross workgroups as fp64 (two words).
+// Precision: per-element exponentials in fp32 (v_exp_f32) of z k - R rounded once (an fma),
+// chunk and segment sums in fp32, everything above (row normalisers, ratios, c, Q, R, the CDF
+// threshold and prefixes) in fp64; team partial sums cross workgroups as fp64 (two words).  A
+// reference is kept at or above -FLT_MAX, so a row whose logits all lie below -FLT_MAX / k (about
+// -2.4e38 T), like a row of -inf, has no probability mass.
 
 #include <algorithm>
+#include <cfloat>
 #include <atomic>
 #include <cstdlib>
 
@@ -112,11 +116,12 @@ __device__ __forceinline__ void cvt_vec<uint16_t>(const uint4& r, float* out) {
     out[4] = bf16_lo(r.z); out[5] = bf16_hi(r.z); out[6] = bf16_lo(r.w); out[7] = bf16_hi(r.w);
 }
 
-// Draw weight of one element: (p(x) - c q(x))+ with p = exp2((zt - mt) k) / S_t, q likewise.
-__device__ __forceinline__ float draw_weight(float zt, float zd, float mt, float md, float k,
+// Draw weight of one element: (p(x) - c q(x))+ with p = exp2(zt k - rt) / S_t (rt the row's
+// reference), q likewise.
+__device__ __forceinline__ float draw_weight(float zt, float zd, float rt, float rd, float k,
                                              float p_scale, float q_scale) {
-    const float p = __builtin_amdgcn_exp2f((zt - mt) * k) * p_scale;
-    const float q = __builtin_amdgcn_exp2f((zd - md) * k) * q_scale;
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(zt, k, -rt)) * p_scale;
+    const float q = __builtin_amdgcn_exp2f(__builtin_fmaf(zd, k, -rd)) * q_scale;
     return fmaxf(p - q, 0.0f);
 }
 
@@ -196,8 +201,9 @@ __device__ __forceinline__ uint32_t excluded_in(const int32_t* excl, int nexcl, 
     return m;
 }
 
-// The statistics of one item (one wave): (max, sum of exp2((z - max) k)) over elements [lo, hi)
-// of `src`, or (max, argmax) at T = 0, as two words (w0, w1; in every lane).  The wave's lanes
+// The statistics of one item (one wave): (R, sum of exp2(z k - R)) over elements [lo, hi) of
+// `src`, R the largest z k (kept at or above -FLT_MAX), or (max, argmax) at T = 0, as two words
+// (w0, w1; in every lane).  The wave's lanes
 // take the item's 16-byte vectors u = 0 .. kWaveLoads - 1 in order; `r` holds their raw words if
 // `loaded`, else they are loaded here, all at once -- or, with kLean, one at a time (few
 // registers, same arithmetic in the same order, so the same bits).
@@ -220,11 +226,15 @@ __device__ __forceinline__ void item_stats(const T* src, int lo, int hi, int lan
             } else {
                 rv = r[u];
             }
-            // (a vector lies wholly inside or outside the row; selects, no branches)
-            cvt_vec<T>(rv, z);
+            // (a vector lies wholly inside or outside the row: outside, its raw words become
+            // -inf; selects, no branches)
             const bool in = base < hi;
-#pragma unroll
-            for (int e = 0; e < kVec; ++e) z[e] = in ? z[e] : -INFINITY;
+            constexpr uint32_t kNegInf = sizeof(T) == 2 ? 0xff80ff80u : 0xff800000u;
+            rv.x = in ? rv.x : kNegInf;
+            rv.y = in ? rv.y : kNegInf;
+            rv.z = in ? rv.z : kNegInf;
+            rv.w = in ? rv.w : kNegInf;
+            cvt_vec<T>(rv, z);
         } else {
 #pragma unroll
             for (int e = 0; e < kVec; ++e) z[e] = (base + e < hi) ? Elem<T>::load(src, base + e) : -INFINITY;
@@ -264,21 +274,24 @@ __device__ __forceinline__ void item_stats(const T* src, int lo, int hi, int lan
         w0 = __float_as_uint(bv);
         w1 = static_cast<uint32_t>(bi);
     } else {
-        // online over the 16-byte vectors: the running sum is rescaled once per vector
-        // (branch-free: a reference of 0 while everything is -inf makes every term 0)
-        float m = -INFINITY, sum = 0.f;
+        // online over the 16-byte vectors in the scaled domain: the reference R is the largest
+        // z k so far, each term exp2(z k - R) with the argument rounded once (an fma), and the
+        // running sum is rescaled once per vector.  R starts at, and never goes below, -FLT_MAX,
+        // so no term or rescale factor is ever NaN (terms of -inf logits are 0) and no branch or
+        // select guards it.
+        float R = -FLT_MAX, sum = 0.f;
         auto fold = [&](int u) {
             float z[kVec];
             values(u, z);
-            float mu = m;
+            float mu = -INFINITY;
 #pragma unroll
             for (int e = 0; e < kVec; ++e) mu = fmaxf(mu, z[e]);
-            const float mref = (mu == -INFINITY) ? 0.f : mu;
+            const float Ru = fmaxf(R, fmaxf(mu * k, -FLT_MAX));
             float add = 0.f;
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) add += __builtin_amdgcn_exp2f((z[e] - mref) * k);
-            sum = sum * __builtin_amdgcn_exp2f((m - mref) * k) + add;
-            m = mu;
+            for (int e = 0; e < kVec; ++e) add += __builtin_amdgcn_exp2f(__builtin_fmaf(z[e], k, -Ru));
+            sum = __builtin_fmaf(sum, __builtin_amdgcn_exp2f(R - Ru), add);
+            R = Ru;
         };
         if constexpr (kVecOK && !kLean) {
 #pragma unroll
@@ -287,8 +300,8 @@ __device__ __forceinline__ void item_stats(const T* src, int lo, int hi, int lan
 #pragma nounroll
             for (int u = 0; u < kWaveLoads; ++u) fold(u);
         }
-        wave_max_sum(m, sum, k);
-        w0 = __float_as_uint(m);
+        wave_max_sum(R, sum, 1.0f);      // (references already scaled)
+        w0 = __float_as_uint(R);
         w1 = __float_as_uint(sum);
     }
 }
@@ -423,7 +436,7 @@ template <typename T, bool kGreedy, bool kVecOK>
 __global__ void __launch_bounds__(kThreads)
 accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
               const int32_t* __restrict__ tokens, const int32_t* __restrict__ parent, int B, int n1,
-              int V, int nchunk, int P, int rule, float k, double invT, uint64_t seed, uint64_t offset,
+              int V, int nchunk, int P, int rule, float k, uint64_t seed, uint64_t offset,
               uint64_t* __restrict__ ctl, uint32_t* __restrict__ seen, uint64_t wait_ticks,
               uint64_t* __restrict__ statw, uint64_t* __restrict__ partw, int32_t* __restrict__ accept_len,
               int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_nodes,
@@ -796,10 +809,10 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                         if (ok)
                             for (int c = cl; c < nchunk; c += g) {
                                 const float x0 = sv[c * 4], x1 = sv[c * 4 + 1];
-                                if (x0 != -INFINITY) st += static_cast<double>(x1) * __builtin_amdgcn_exp2f((x0 - mt) * k);
+                                st += static_cast<double>(x1) * __builtin_amdgcn_exp2f(x0 - mt);
                                 if (dr) {
                                     const float y0 = sv[c * 4 + 2], y1 = sv[c * 4 + 3];
-                                    if (y0 != -INFINITY) sd += static_cast<double>(y1) * __builtin_amdgcn_exp2f((y0 - md) * k);
+                                    sd += static_cast<double>(y1) * __builtin_amdgcn_exp2f(y0 - md);
                                 }
                             }
                         for (int o = g >> 1; o > 0; o >>= 1) {
@@ -824,8 +837,8 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                 if (v > 0) {
                     const int pa = par[v];
                     const float zt = (v == t) ? widen<T>(gzt) : Elem<T>::load(target + (seq + pa) * V, tok[v]);
-                    const double lp = (static_cast<double>(zt) - Mt[pa]) * invT;
-                    const double pd = exp(lp) / St[pa];
+                    const double lp = static_cast<double>(zt) * k - Mt[pa];     // (log2 units)
+                    const double pd = exp2(lp) / St[pa];
                     pv_ = static_cast<float>(pd);
                     if (rule == kRuleDeterministic) {
                         // a point-mass proposal: the ratio is p(x) itself (over the unrejected mass)
@@ -833,9 +846,9 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                         qx[v] = 1.f;
                     } else {
                         const float zd = (v == t) ? widen<T>(gzd) : Elem<T>::load(draft + (seq + pa) * V, tok[v]);
-                        const double lq = (static_cast<double>(zd) - Md[pa]) * invT;
-                        const double qd = exp(lq) / Sd[pa];
-                        pq[v] = exp(lp - lq) * (Sd[pa] / St[pa]);
+                        const double lq = static_cast<double>(zd) * k - Md[pa];
+                        const double qd = exp2(lq) / Sd[pa];
+                        pq[v] = exp2(lp - lq) * (Sd[pa] / St[pa]);
                         qx[v] = static_cast<float>(qd);
                         qv_ = static_cast<float>(qd);
                     }
@@ -1131,7 +1144,8 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
             for (int x = t; x < V; x += kThreads) {
                 const float zt = Elem<T>::load(target + rr, x);
                 const float zd = (qs != 0.f) ? Elem<T>::load(draft + rr, x) : -INFINITY;
-                const float d = __builtin_amdgcn_exp2f((zt - mt) * k) * ps - __builtin_amdgcn_exp2f((zd - md) * k) * qs;
+                const float d = __builtin_amdgcn_exp2f(__builtin_fmaf(zt, k, -mt)) * ps -
+                                __builtin_amdgcn_exp2f(__builtin_fmaf(zd, k, -md)) * qs;
                 argmax_merge(bv, bi, d, x);
             }
             wave_argmax(bv, bi);
@@ -1214,7 +1228,7 @@ hipError_t launch_kernel(const AcceptArgs& a, hipStream_t stream) {
     float* q_tok = a.q_tok;
     int rule = a.rule;
     hipLaunchKernelGGL((accept_kernel<T, kGreedy, kVecOK>), dim3(grid), dim3(kThreads), 0, stream, target, draft,
-                       tokens, parent, B, n1, V, nchunk, P, rule, k, invT, seed, offset, ctl, seen, wt, statw, partw,
+                       tokens, parent, B, n1, V, nchunk, P, rule, k, seed, offset, ctl, seen, wt, statw, partw,
                        accept_len, out_tokens, out_nodes, p_tok, q_tok);
     return hipGetLastError();
 }
