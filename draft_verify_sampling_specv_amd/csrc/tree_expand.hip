@@ -9,9 +9,10 @@
 // per parent.
 //
 //   expand_topk_kernel   one 16-wave workgroup per frontier row: one coalesced pass over the row
-//                        (batches of four 16-byte loads per thread) keeps a per-thread top-k in
-//                        registers -- a batch is examined only if its max would enter -- and the
-//                        online (max, sum of exp) of z / T, one rescale per vector; k rounds of a
+//                        (batches of four 16-byte loads per thread, the next batch in flight while
+//                        one is processed) keeps a per-thread top-k in registers -- a batch is
+//                        examined only if its max would enter -- and the online log-sum-exp of
+//                        z / T (scaled reference, one fma per term, one rescale per vector); k rounds of a
 //                        wave-wide argmax over the lanes' list heads merge each wave, and one wave
 //                        merges the waves' lists through LDS.  HBM-bound: each row is read once.
 //   expand_select_kernel one workgroup per sequence: the rank of every candidate (score, then
@@ -22,6 +23,7 @@
 // Ties: equal logits go to the lower token id; equal scores to the earlier row, then the better
 // rank.  Scores are fp64 (the row's log-sum-exp is combined in fp64 from fp32 per-thread sums).
 
+#include <cfloat>
 #include <cmath>
 
 #include "common.h"
@@ -34,6 +36,7 @@ constexpr int kTopThreads = 1024;           // 16 waves per row: enough loads in
 constexpr int kTopWaves = kTopThreads / kWave;
 constexpr int kBatch = 4;                   // 16-byte vectors per thread loaded together
 constexpr int kSelThreads = 512;
+constexpr double kLn2d = 0.6931471805599453;
 
 struct RowTop {              // per-row result in the workspace
     int32_t tok[kExpandMaxK];
@@ -143,7 +146,9 @@ expand_topk_kernel(const T* __restrict__ logits, const int32_t* __restrict__ fro
     for (int j = 0; j < K; ++j) { tv[j] = -INFINITY; ti[j] = INT_MAX; }
     float wthr = -INFINITY;              // the wave-wide entry bound (see below)
     int held = 0;
-    float m = -INFINITY, s = 0.f;        // online max and sum of exp2((x - m) kexp2)
+    // online log-sum-exp in the scaled domain: R the largest x kexp2 so far (never below
+    // -FLT_MAX), s the sum of exp2(x kexp2 - R), each argument one fma
+    float R = -FLT_MAX, s = 0.f;
     auto insert = [&](float x, int xi) {
         ++held;
         float cv = x;
@@ -170,13 +175,12 @@ expand_topk_kernel(const T* __restrict__ logits, const int32_t* __restrict__ fro
 #pragma unroll
             for (int e = 1; e < kVec; ++e) vm[q] = fmaxf(vm[q], x[q][e]);
             // online log-sum-exp, one rescale per vector
-            const float mn = fmaxf(m, vm[q]);
-            const float ref = (mn == -INFINITY) ? 0.f : mn;
+            const float Rn = fmaxf(R, vm[q] * kexp2);
             float add = 0.f;
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) add += __builtin_amdgcn_exp2f((x[q][e] - ref) * kexp2);
-            s = s * __builtin_amdgcn_exp2f((m - ref) * kexp2) + add;
-            m = mn;
+            for (int e = 0; e < kVec; ++e) add += __builtin_amdgcn_exp2f(__builtin_fmaf(x[q][e], kexp2, -Rn));
+            s = __builtin_fmaf(s, __builtin_amdgcn_exp2f(R - Rn), add);
+            R = Rn;
             bmax = fmaxf(bmax, vm[q]);
         }
         // wave-wide entry bound: the kk-th largest of the lanes' batch maxima -- kk elements at
@@ -197,10 +201,11 @@ expand_topk_kernel(const T* __restrict__ logits, const int32_t* __restrict__ fro
         }
     };
     for (int bi = 0; bi < nfull; ++bi) {
-        if (bi > 0) load_full(bi * kBatchElems);
         float x[kBatch][kVec];
 #pragma unroll
         for (int q = 0; q < kBatch; ++q) unpack16<T>(r[q], x[q]);
+        // the next batch is in flight while this one is processed
+        if (bi + 1 < nfull) load_full((bi + 1) * kBatchElems);
         process(bi * kBatchElems, x, false);
     }
     // the rest of the row (and every batch of a row without 16-byte vectors): bounds-checked
@@ -235,8 +240,8 @@ expand_topk_kernel(const T* __restrict__ logits, const int32_t* __restrict__ fro
 
     // per wave: kk rounds, each taking the best head of the lanes' sorted lists (the winning lane
     // shifts its list up by one)
-    wave_max_sum(m, s, kexp2);
-    if (lane == 0) { wm[w] = m; ws[w] = s; }
+    wave_max_sum(R, s, 1.0f);            // (references already scaled)
+    if (lane == 0) { wm[w] = R; ws[w] = s; }
     for (int r = 0; r < kk; ++r) {
         float bv = tv[0];
         int bi = ti[0], bl = (ti[0] == INT_MAX) ? -1 : lane;
@@ -297,9 +302,8 @@ expand_topk_kernel(const T* __restrict__ logits, const int32_t* __restrict__ fro
             float M = -INFINITY;
             for (int q = 0; q < kTopWaves; ++q) M = fmaxf(M, wm[q]);
             double S = 0.0;
-            for (int q = 0; q < kTopWaves; ++q)
-                if (wm[q] != -INFINITY) S += static_cast<double>(ws[q]) * exp2(static_cast<double>(wm[q] - M) * kexp2);
-            out->lse = static_cast<double>(M) * invT + log(S);
+            for (int q = 0; q < kTopWaves; ++q) S += static_cast<double>(ws[q]) * exp2(static_cast<double>(wm[q]) - M);
+            out->lse = static_cast<double>(M) * kLn2d + log(S);
             out->count = kk;
         }
     }
