@@ -57,7 +57,7 @@ MFMA_PEAK_TFLOPS = 2500.0
 
 # HBM traffic of the dominant kernel (attn_decode_kernel<128, 8, 1>) per call on this workload, from
 # two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), each scaled by what the same
-# counter reads for a 256 MiB device-to-device copy (FETCH_SIZE 131084.6 KiB -> x1.99981,
+# counter reads for a 256 MiB device-to-device copy (FETCH_SIZE 131085.2 KiB -> x1.99980,
 # WRITE_SIZE 262144.0 KiB -> x1.0).  Summaries and commands: profiles/chain_step_pmc.md.
 # Valid only for the kernel sources it was measured on (their SHA-256 below); null otherwise.
 ATTN_TRAFFIC = {
@@ -66,7 +66,7 @@ ATTN_TRAFFIC = {
                 "draft_verify_sampling_specv_amd/csrc/common.h",
                 "draft_verify_sampling_specv_amd/csrc/kernels.h"],
     "sha256": "5ef2ac6e742f0c82c2d78172ab991431b472bcba68b4bcca707153d8013a718f",
-    "fetch_kib": 132455.2, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131084.6, "write_scale": 1.0,
+    "fetch_kib": 132448.6, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131085.2, "write_scale": 1.0,
 }
 
 
@@ -415,7 +415,8 @@ def measure_config(name, args, torch, specv, workloads):
 
     B, n1 = w.tokens.shape
     V = w.V
-    mask, _, _ = specv.build_tree_mask(apar)
+    mask_out = specv.build_tree_mask(apar)          # (outputs reused: nothing allocated when timed)
+    mask = mask_out[0]
     abuf = specv.AttnBuffers.allocate(q, kc)
     cbuf = specv.AcceptBuffers.allocate(B, n1, V, ldt, "cuda")
 
@@ -432,7 +433,7 @@ def measure_config(name, args, torch, specv, workloads):
         return ev0.elapsed_time(ev1) / n
 
     steps = max(20, min(args.steps, 200))
-    ms_mask = timed(lambda i: specv.build_tree_mask(apar), steps)
+    ms_mask = timed(lambda i: specv.build_tree_mask(apar, out=mask_out), steps)
     ms_attn = timed(lambda i: specv.tree_attn_verify(*sets_att[i % len(sets_att)], cl, mask, a.scale, buffers=abuf),
                     steps)
     ms_acc = timed(lambda i: specv.accept_resample(*sets_acc[i % len(sets_acc)], w.T, seed=1, offset=i,
