@@ -69,17 +69,31 @@ ATTN_TRAFFIC = {
     "fetch_kib": 132448.6, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131085.2, "write_scale": 1.0,
 }
 
+# The same for the sampled accept kernel (accept_kernel<bf16, sampled>) on this workload: the
+# statistics pass reads the 22.5 MB of rows once, the draw re-reads the end node's rows (about
+# 4 MB), and the writes are mostly register spill stores.
+ACCEPT_TRAFFIC = {
+    "sources": ["draft_verify_sampling_specv_amd/csrc/accept.hip",
+                "draft_verify_sampling_specv_amd/csrc/common.h",
+                "draft_verify_sampling_specv_amd/csrc/kernels.h"],
+    "sha256": "73b241502e0c2afdbd3a31be847c67dcfb59678225ef276421785d0885114797",
+    "fetch_kib": 13218.8, "write_kib": 2164.0, "fetch_scale": 262144.0 / 131085.2, "write_scale": 1.0,
+}
 
-def attn_traffic_bytes():
+
+def traffic_bytes(t):
     import hashlib
     h = hashlib.sha256()
-    for f in ATTN_TRAFFIC["sources"]:
+    for f in t["sources"]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
-    if h.hexdigest() != ATTN_TRAFFIC["sha256"]:
+    if h.hexdigest() != t["sha256"]:
         return None
-    t = ATTN_TRAFFIC
     return (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024.0
+
+
+def attn_traffic_bytes():
+    return traffic_bytes(ATTN_TRAFFIC)
 
 
 def log(*a):
@@ -277,7 +291,8 @@ def main():
                      "kernel": "attn_decode_kernel<128,8,1> (specv_tree_attn_verify, one launch)",
                      "bytes_per_call": ab, "ms_per_call": ms_attn},
         "roofline_accept": {"bound": "hbm", "achieved": acc_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": acc_gbs / HBM_PEAK_GBS, "bytes_per_call": cb, "ms_per_call": ms_accept,
+                            "frac": acc_gbs / HBM_PEAK_GBS, "traffic": traffic_bytes(ACCEPT_TRAFFIC),
+                            "bytes_per_call": cb, "ms_per_call": ms_accept,
                             "kernel": "accept_kernel<bf16> (specv_accept_resample, one launch)"},
         "accept_only_positions_per_s": positions / (ms_accept * 1e-3),
         "ms_mask": ms_mask,
