@@ -76,7 +76,7 @@ ACCEPT_TRAFFIC = {
     "sources": ["draft_verify_sampling_specv_amd/csrc/accept.hip",
                 "draft_verify_sampling_specv_amd/csrc/common.h",
                 "draft_verify_sampling_specv_amd/csrc/kernels.h"],
-    "sha256": "73b241502e0c2afdbd3a31be847c67dcfb59678225ef276421785d0885114797",
+    "sha256": "ff7cb199ce8002f53a70db321040275fe2a88433540a6fab431eede00aa2d317",
     "fetch_kib": 13218.8, "write_kib": 2164.0, "fetch_scale": 262144.0 / 131085.2, "write_scale": 1.0,
 }
 

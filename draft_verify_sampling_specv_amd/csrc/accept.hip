@@ -58,7 +58,8 @@
 
 // No contraction of multiplies and adds into fma in this file: a value that one workgroup
 // computes on behalf of another must be the same bits as the owner's, and with contraction the
-// choice could differ between two inlined copies of the same code.
+// choice could differ between two inlined copies of the same code.  (The fmas that the code
+// writes out, __builtin_fmaf, are the same operation in every copy.)
 #pragma clang fp contract(off)
 
 namespace specv {
@@ -457,7 +458,7 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
     __shared__ int32_t dup[kMaxNodes];      // token repeats an earlier sibling's
     __shared__ uint64_t cmask[kMaskNodes][kMaskWords];   // children of each node as a bit mask
     __shared__ int32_t ilist[kMaxNodes];    // internal rows in index order
-    __shared__ float Mt[kMaxNodes], Md[kMaxNodes];
+    __shared__ float Mt[kMaxNodes], Md[kMaxNodes];   // row references (largest z k; scaled domain)
     __shared__ double St[kMaxNodes], Sd[kMaxNodes];
     __shared__ double pq[kMaxNodes];        // p(x)/q(x) of node x under its parent's rows
     __shared__ float qx[kMaxNodes];         // q(x)
