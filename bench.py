@@ -66,7 +66,7 @@ ATTN_TRAFFIC = {
                 "draft_verify_sampling_specv_amd/csrc/common.h",
                 "draft_verify_sampling_specv_amd/csrc/kernels.h"],
     "sha256": "5ef2ac6e742f0c82c2d78172ab991431b472bcba68b4bcca707153d8013a718f",
-    "fetch_kib": 132448.6, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131085.2, "write_scale": 1.0,
+    "fetch_kib": 132458.6, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131085.2, "write_scale": 1.0,
 }
 
 # The same for the sampled accept kernel (accept_kernel<bf16, sampled>) on this workload: the
@@ -77,7 +77,7 @@ ACCEPT_TRAFFIC = {
                 "draft_verify_sampling_specv_amd/csrc/common.h",
                 "draft_verify_sampling_specv_amd/csrc/kernels.h"],
     "sha256": "ff7cb199ce8002f53a70db321040275fe2a88433540a6fab431eede00aa2d317",
-    "fetch_kib": 13218.8, "write_kib": 2164.0, "fetch_scale": 262144.0 / 131085.2, "write_scale": 1.0,
+    "fetch_kib": 13209.6, "write_kib": 2164.0, "fetch_scale": 262144.0 / 131085.2, "write_scale": 1.0,
 }
 
 
