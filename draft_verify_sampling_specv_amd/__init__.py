@@ -12,6 +12,8 @@ library has not been built this import fails.
   kv_commit(k_cache, v_cache, ctx_len, accept_len, out_nodes)     -> new_ctx_len
   tree_expand(draft_logits, frontier, tree, k, T, keep)           -> new_frontier (tree updated)
   verify_layer(x, weights, k_cache, v_cache, ctx_len, mask, depth, Hq) -> out (caches written)
+  pack_layer_weights(weights) / pack_weights(w)    the layer's matrices in the tile order its
+                                                   products read (verify_layer takes either)
 """
 
 from ._lib import (  # noqa: F401
@@ -32,6 +34,8 @@ from ._lib import (  # noqa: F401
     accept_workspace_bytes,
     attn_workspace_bytes,
     LayerWeights,
+    pack_weights,
+    pack_layer_weights,
     verify_layer,
     verify_layer_workspace_bytes,
 )

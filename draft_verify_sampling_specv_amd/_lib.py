@@ -77,6 +77,10 @@ lib.specv_verify_layer_workspace_bytes.argtypes = [ctypes.c_int32] * 7
 lib.specv_verify_layer.restype = ctypes.c_int
 lib.specv_verify_layer.argtypes = (
     [_vp] * 7 + [ctypes.c_float, ctypes.c_float] + [_vp] * 5 + [ctypes.c_int32] * 7 + [_vp, _vp, ctypes.c_size_t, _vp])
+lib.specv_verify_layer_packed.restype = ctypes.c_int
+lib.specv_verify_layer_packed.argtypes = lib.specv_verify_layer.argtypes
+lib.specv_pack_weights.restype = ctypes.c_int
+lib.specv_pack_weights.argtypes = [_vp, ctypes.c_int32, ctypes.c_int32, _vp, _vp]
 
 
 class SpecvError(RuntimeError):
@@ -341,13 +345,35 @@ def tree_expand(draft_logits, frontier, tree, k, temperature, keep, new_frontier
 
 @dataclass
 class LayerWeights:
-    """bf16 GPU tensors in the [out][in] layout of a linear map."""
+    """bf16 GPU tensors in the [out][in] layout of a linear map (packed: the four matrices in the
+    tile order of specv_pack_weights, their shapes unchanged; see pack_layer_weights)."""
     w_qkv: torch.Tensor          # [(Hq + 2 Hkv) D][Hq D]: query, key, value rows
     w_o: torch.Tensor            # [Hq D][Hq D]
     w_gate_up: torch.Tensor      # [2 inter][Hq D]: gate rows, then up rows
     w_down: torch.Tensor         # [Hq D][inter]
     attn_norm: torch.Tensor      # [Hq D]
     mlp_norm: torch.Tensor       # [Hq D]
+    packed: bool = False
+
+
+def pack_weights(w, out=None):
+    """w [N][K] bf16 (GPU, contiguous; N a multiple of 32, K of 64) -> a tensor of the same shape
+    holding it in the tile order the layer's products read (specv_pack_weights)."""
+    if not w.is_cuda or not w.is_contiguous() or w.dtype != torch.bfloat16 or w.dim() != 2:
+        raise ValueError("w must be a contiguous 2-D bf16 GPU tensor")
+    if out is None:
+        out = torch.empty_like(w)
+    N, K = w.shape
+    _check("specv_pack_weights", lib.specv_pack_weights(_ptr(w), N, K, _ptr(out), _stream()))
+    return out
+
+
+def pack_layer_weights(weights):
+    """LayerWeights with its four matrices packed (the norm gains are shared, not copied)."""
+    if weights.packed:
+        return weights
+    return LayerWeights(pack_weights(weights.w_qkv), pack_weights(weights.w_o), pack_weights(weights.w_gate_up),
+                        pack_weights(weights.w_down), weights.attn_norm, weights.mlp_norm, packed=True)
 
 
 def verify_layer_workspace_bytes(B, K, Hq, Hkv, D, Lmax, inter):
@@ -385,7 +411,8 @@ def verify_layer(x, weights, k_cache, v_cache, ctx_len, mask, depth, Hq, eps=1e-
     if workspace is None:
         workspace = torch.empty((max(verify_layer_workspace_bytes(B, n1 - 1, Hq, Hkv, D, Lmax, inter), 1),),
                                 dtype=torch.uint8, device=x.device)
-    _check("specv_verify_layer", lib.specv_verify_layer(
+    fn = "specv_verify_layer_packed" if w.packed else "specv_verify_layer"
+    _check(fn, getattr(lib, fn)(
         _ptr(x), _ptr(w.w_qkv), _ptr(w.w_o), _ptr(w.w_gate_up), _ptr(w.w_down), _ptr(w.attn_norm),
         _ptr(w.mlp_norm), float(eps), float(theta), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), _ptr(mask),
         _ptr(depth), B, n1 - 1, Hq, Hkv, D, Lmax, inter, _ptr(out), _ptr(workspace), workspace.numel(),

@@ -300,13 +300,17 @@ size_t specv_verify_layer_workspace_bytes(int32_t B, int32_t K, int32_t Hq, int3
     return specv::layer_workspace_bytes(B, K + 1, Hq, Hkv, D, Lmax, inter);
 }
 
-specv_status specv_verify_layer(const void* x, const void* w_qkv, const void* w_o, const void* w_gate_up,
-                                const void* w_down, const void* attn_norm, const void* mlp_norm,
-                                float rms_eps, float rope_theta, void* k_cache, void* v_cache,
-                                const int32_t* ctx_len, const uint32_t* mask, const int32_t* depth,
-                                int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D, int32_t Lmax,
-                                int32_t inter, void* out, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+specv_status verify_layer_call(const void* x, const void* w_qkv, const void* w_o, const void* w_gate_up,
+                               const void* w_down, const void* attn_norm, const void* mlp_norm,
+                               float rms_eps, float rope_theta, void* k_cache, void* v_cache,
+                               const int32_t* ctx_len, const uint32_t* mask, const int32_t* depth,
+                               int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D, int32_t Lmax,
+                               int32_t inter, void* out, void* workspace, size_t workspace_bytes,
+                               bool packed, hipStream_t stream) {
     if (B < 0) return fail(SPECV_ERR_INVALID_ARG, "B = %d < 0", B);
     if (K < 0 || K > SPECV_MAX_NODES - 1)
         return fail(SPECV_ERR_INVALID_ARG, "K = %d outside [0, %d]", K, SPECV_MAX_NODES - 1);
@@ -335,8 +339,48 @@ specv_status specv_verify_layer(const void* x, const void* w_qkv, const void* w_
                     workspace_bytes);
     specv::LayerArgs a{x, w_qkv, w_o, w_gate_up, w_down, attn_norm, mlp_norm, rms_eps, rope_theta,
                        k_cache, v_cache, ctx_len, mask, depth, B, K + 1, Hq, Hkv, D, Lmax, inter, out,
-                       workspace};
+                       workspace, packed};
     return hip_status(specv::launch_verify_layer(a, stream), "verify_layer");
+}
+
+}  // namespace
+
+extern "C" {
+
+specv_status specv_verify_layer(const void* x, const void* w_qkv, const void* w_o, const void* w_gate_up,
+                                const void* w_down, const void* attn_norm, const void* mlp_norm,
+                                float rms_eps, float rope_theta, void* k_cache, void* v_cache,
+                                const int32_t* ctx_len, const uint32_t* mask, const int32_t* depth,
+                                int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D, int32_t Lmax,
+                                int32_t inter, void* out, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+    return verify_layer_call(x, w_qkv, w_o, w_gate_up, w_down, attn_norm, mlp_norm, rms_eps, rope_theta, k_cache,
+                             v_cache, ctx_len, mask, depth, B, K, Hq, Hkv, D, Lmax, inter, out, workspace,
+                             workspace_bytes, false, stream);
+}
+
+specv_status specv_verify_layer_packed(const void* x, const void* w_qkv, const void* w_o, const void* w_gate_up,
+                                       const void* w_down, const void* attn_norm, const void* mlp_norm,
+                                       float rms_eps, float rope_theta, void* k_cache, void* v_cache,
+                                       const int32_t* ctx_len, const uint32_t* mask, const int32_t* depth,
+                                       int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D, int32_t Lmax,
+                                       int32_t inter, void* out, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+    return verify_layer_call(x, w_qkv, w_o, w_gate_up, w_down, attn_norm, mlp_norm, rms_eps, rope_theta, k_cache,
+                             v_cache, ctx_len, mask, depth, B, K, Hq, Hkv, D, Lmax, inter, out, workspace,
+                             workspace_bytes, true, stream);
+}
+
+specv_status specv_pack_weights(const void* w, int32_t N, int32_t K, void* packed, hipStream_t stream) {
+    if (N <= 0 || N % 32 != 0) return fail(SPECV_ERR_INVALID_ARG, "N = %d is not a positive multiple of 32", N);
+    if (K <= 0 || K % 64 != 0) return fail(SPECV_ERR_INVALID_ARG, "K = %d is not a positive multiple of 64", K);
+    if (!w || !packed) return fail(SPECV_ERR_INVALID_ARG, "NULL pointer argument");
+    if ((reinterpret_cast<uintptr_t>(w) & 15) || (reinterpret_cast<uintptr_t>(packed) & 15))
+        return fail(SPECV_ERR_INVALID_ARG, "w and packed must be 16-byte aligned");
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(w), b0 = reinterpret_cast<uintptr_t>(packed);
+    const uintptr_t bytes = static_cast<uintptr_t>(N) * static_cast<uintptr_t>(K) * 2u;
+    if (a0 < b0 + bytes && b0 < a0 + bytes) return fail(SPECV_ERR_INVALID_ARG, "w and packed overlap");
+    return hip_status(specv::launch_pack_weights(w, N, K, packed, stream), "pack_weights");
 }
 
 }  // extern "C"

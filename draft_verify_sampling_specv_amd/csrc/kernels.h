@@ -138,10 +138,13 @@ struct LayerArgs {
     int B, n1, Hq, Hkv, D, Lmax, inter;
     void* out;
     void* workspace;
+    bool packed;               // the four weight matrices in the tile order of launch_pack_weights
 };
 
 size_t layer_workspace_bytes(int B, int n1, int Hq, int Hkv, int D, int Lmax, int inter);
 hipError_t launch_verify_layer(const LayerArgs& a, hipStream_t stream);
+// W [N][K] bf16 (N a multiple of 32, K of 64) -> the tile order the layer's products read
+hipError_t launch_pack_weights(const void* w, int N, int K, void* packed, hipStream_t stream);
 
 // the three paths behind launch_attention
 size_t attn_tree_workspace_bytes(int B, int n1, int Hq, int Hkv, int D, int Lmax);

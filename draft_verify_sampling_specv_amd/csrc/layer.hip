@@ -74,7 +74,11 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // kGateUp: W is the [2 N][K] gate/up matrix and the workgroup's 128 rows are gate rows
 // 64 t .. 64 t + 63 (waves 0, 1) and the matching up rows N + 64 t .. (waves 2, 3); with one split
 // the kernel finishes the MLP activation itself, act[m][n] = silu(gate) up in bf16 (no partials).
-template <int MB, bool kGateUp>
+//
+// kPacked: W is in the tile order of pack_weights_kernel (rows a multiple of 32), so each weight
+// load instruction of a wave reads 1 KB contiguous -- 8 whole 128-byte lines -- instead of 32 bytes
+// of 32 different rows' lines; the vector L1 then tracks a quarter of the line requests per byte.
+template <int MB, bool kGateUp, bool kPacked>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(const uint16_t* __restrict__ X, int M, int K,
                                                                const uint16_t* __restrict__ W, int N,
                                                                int steps_per_split, float* __restrict__ P,
@@ -93,14 +97,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(const uint16_t* _
         constexpr int kHalf = kMW / 2;                 // gate waves (the rest hold the matching up rows)
         const int nw = kGateUp ? (blockIdx.x * kHalf + wv % kHalf) * kRowsPerWave : blockIdx.x * kTileRows + wv * kRowsPerWave;
         const int64_t wrow = kGateUp ? min(nw + r, N - 1) + (wv >= kHalf ? N : 0) : min(nw + r, N - 1);
-        // the 32 columns 32 h .. 32 h + 31 of each step
-        const uint4* wp = reinterpret_cast<const uint4*>(W + wrow * K + k0 + 32 * h);
+        // row-major: the 32 columns 32 h .. 32 h + 31 of each step, slice j at 8 j; packed: the
+        // wave's 32-row block (clamped past N like the rows), 1 KB per (step, slice) from its
+        // first step, lane l at 16 l
+        const int rb = kGateUp ? min(nw, N - 1) / kRowsPerWave + (wv >= kHalf ? N / kRowsPerWave : 0)
+                               : min(nw, N - 1) / kRowsPerWave;
+        const uint4* wp = kPacked
+            ? reinterpret_cast<const uint4*>(W) + ((static_cast<int64_t>(rb) * (K / kStep) + st0) * 4) * kWave + lane
+            : reinterpret_cast<const uint4*>(W + wrow * K + k0 + 32 * h);
+        auto wload = [&](int s, int j) { return kPacked ? wp[(s * 4 + j) * kWave] : wp[s * (kStep / 8) + j]; };
         uint4 wr[kInFlight][4];
 #pragma unroll
         for (int u = 0; u < kInFlight; ++u) {
             const int s = min(u, nsteps - 1);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) wr[u][j] = wp[s * (kStep / 8) + j];
+            for (int j = 0; j < 4; ++j) wr[u][j] = wload(s, j);
         }
         f32x16_t acc[MB];
 #pragma unroll
@@ -128,7 +139,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(const uint16_t* _
                 // refill this ring slot with the step kInFlight ahead
                 const int sw = min(s + kInFlight, nsteps - 1);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) wr[u][j] = wp[sw * (kStep / 8) + j];
+                for (int j = 0; j < 4; ++j) wr[u][j] = wload(sw, j);
                 __syncthreads();                       // chunk s read by all; chunk s + 1 staged
             }
         }
@@ -221,6 +232,23 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(const uint16_t* _
         }
         if constexpr (kGateUp) __syncthreads();        // matches the up-value exchange
     }
+}
+
+// The tile order of a weight matrix W [N][K] bf16 (N a multiple of 32, K of 64) for gemm_kernel:
+// 16-byte unit ((rb * (K / 64) + s) * 4 + j) * 64 + l holds W[32 rb + l % 32][64 s + 32 (l / 32)
+// + 8 j .. + 8]: the A operand of MFMA slice j of step s for lane l of the wave that owns rows
+// 32 rb .. 32 rb + 31.  One thread per output unit (coalesced stores).
+__global__ __launch_bounds__(kThreads) void pack_weights_kernel(const uint4* __restrict__ W, int N, int K,
+                                                                uint4* __restrict__ Pk) {
+    const int64_t u = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    const int ks = K / kStep;
+    if (u >= static_cast<int64_t>(N) * K / 8) return;
+    const int l = static_cast<int>(u % kWave), j = static_cast<int>((u / kWave) % 4);
+    const int64_t t = u / (4 * kWave);
+    const int s = static_cast<int>(t % ks);
+    const int64_t rb = t / ks;
+    const int64_t row = rb * kRowsPerWave + l % 32;
+    Pk[u] = W[(row * K + static_cast<int64_t>(s) * kStep + 32 * (l / 32) + 8 * j) / 8];
 }
 
 constexpr int kMaxSplits = 16;
@@ -500,7 +528,7 @@ int gemm_tiles(int N, bool gate_up) {
 
 // gate_up: W is [2 N][K] and act receives silu(gate) up (splits must be 1)
 hipError_t launch_gemm(const uint16_t* X, int M, int K, const uint16_t* W, int N, int splits, float* P,
-                       uint16_t* act, bool gate_up, hipStream_t stream) {
+                       uint16_t* act, bool gate_up, bool packed, hipStream_t stream) {
     const int steps = K / kStep;
     const int per = (steps + splits - 1) / splits;
     const dim3 grid(gemm_tiles(N, gate_up), splits);
@@ -509,8 +537,13 @@ hipError_t launch_gemm(const uint16_t* X, int M, int K, const uint16_t* W, int N
     switch (mb) {
 #define SPECV_GEMM_CASE(n)                                                                              \
         case n:                                                                                         \
-            if (gate_up) gemm_kernel<n, true><<<grid, kGemmThreads, 0, stream>>>(X, M, K, W, N, per, P, act); \
-            else gemm_kernel<n, false><<<grid, kGemmThreads, 0, stream>>>(X, M, K, W, N, per, P, act);  \
+            if (packed) {                                                                               \
+                if (gate_up) gemm_kernel<n, true, true><<<grid, kGemmThreads, 0, stream>>>(X, M, K, W, N, per, P, act); \
+                else gemm_kernel<n, false, true><<<grid, kGemmThreads, 0, stream>>>(X, M, K, W, N, per, P, act); \
+            } else {                                                                                    \
+                if (gate_up) gemm_kernel<n, true, false><<<grid, kGemmThreads, 0, stream>>>(X, M, K, W, N, per, P, act); \
+                else gemm_kernel<n, false, false><<<grid, kGemmThreads, 0, stream>>>(X, M, K, W, N, per, P, act); \
+            }                                                                                           \
             break;
         SPECV_GEMM_CASE(1) SPECV_GEMM_CASE(2) SPECV_GEMM_CASE(3) SPECV_GEMM_CASE(4)
         SPECV_GEMM_CASE(5) SPECV_GEMM_CASE(6) SPECV_GEMM_CASE(7) SPECV_GEMM_CASE(8)
@@ -583,7 +616,7 @@ hipError_t launch_verify_layer(const LayerArgs& a, hipStream_t stream) {
     for (int m0 = 0; m0 < p.T; m0 += p.chunk) {
         const int mc = min(p.chunk, p.T - m0);
         if ((e = launch_gemm(h + static_cast<int64_t>(m0) * p.hd, mc, p.hd, static_cast<const uint16_t*>(a.w_qkv),
-                             p.nqkv, p.s_qkv, P, nullptr, false, stream)) != hipSuccess)
+                             p.nqkv, p.s_qkv, P, nullptr, false, a.packed, stream)) != hipSuccess)
             return e;
         qkv_epilogue_kernel<<<dim3(heads, mc), 64, 0, stream>>>(P, p.s_qkv, mc, m0, a.n1, a.Hq, a.Hkv, a.D, a.Lmax,
                                                                 a.ctx_len, a.depth, rot, q,
@@ -598,7 +631,7 @@ hipError_t launch_verify_layer(const LayerArgs& a, hipStream_t stream) {
     for (int m0 = 0; m0 < p.T; m0 += p.chunk) {
         const int mc = min(p.chunk, p.T - m0);
         if ((e = launch_gemm(att + static_cast<int64_t>(m0) * p.hd, mc, p.hd, static_cast<const uint16_t*>(a.w_o),
-                             p.hd, p.s_o, P, nullptr, false, stream)) != hipSuccess)
+                             p.hd, p.s_o, P, nullptr, false, a.packed, stream)) != hipSuccess)
             return e;
         residual_norm_kernel<<<mc, kNormThreads, 0, stream>>>(P, p.s_o, mc, m0, p.hd, x,
                                                           static_cast<const uint16_t*>(a.mlp_norm), a.eps, y, h2);
@@ -609,7 +642,7 @@ hipError_t launch_verify_layer(const LayerArgs& a, hipStream_t stream) {
         const bool fused = p.s_gu == 1;
         if ((e = launch_gemm(h2 + static_cast<int64_t>(m0) * p.hd, mc, p.hd,
                              static_cast<const uint16_t*>(a.w_gate_up), fused ? a.inter : 2 * a.inter, p.s_gu, P,
-                             act + static_cast<int64_t>(m0) * a.inter, fused, stream)) != hipSuccess)
+                             act + static_cast<int64_t>(m0) * a.inter, fused, a.packed, stream)) != hipSuccess)
             return e;
         if (!fused) {
             silu_mul_kernel<<<dim3((a.inter / 4 + kThreads - 1) / kThreads, mc), kThreads, 0, stream>>>(
@@ -620,13 +653,22 @@ hipError_t launch_verify_layer(const LayerArgs& a, hipStream_t stream) {
     for (int m0 = 0; m0 < p.T; m0 += p.chunk) {
         const int mc = min(p.chunk, p.T - m0);
         if ((e = launch_gemm(act + static_cast<int64_t>(m0) * a.inter, mc, a.inter,
-                             static_cast<const uint16_t*>(a.w_down), p.hd, p.s_down, P, nullptr, false, stream)) !=
+                             static_cast<const uint16_t*>(a.w_down), p.hd, p.s_down, P, nullptr, false, a.packed,
+                             stream)) !=
             hipSuccess)
             return e;
         residual_kernel<<<dim3(row_grid_hd.x, mc), kThreads, 0, stream>>>(P, p.s_down, mc, m0, p.hd, y, out);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_pack_weights(const void* w, int N, int K, void* packed, hipStream_t stream) {
+    const int64_t units = static_cast<int64_t>(N) * K / 8;
+    const int64_t blocks = (units + kThreads - 1) / kThreads;
+    pack_weights_kernel<<<static_cast<unsigned>(blocks), kThreads, 0, stream>>>(
+        static_cast<const uint4*>(w), N, K, static_cast<uint4*>(packed));
+    return hipGetLastError();
 }
 
 }  // namespace specv

@@ -19,7 +19,9 @@
  *                           rejected branches';
  *   specv_verify_layer      one whole target-model layer over the draft nodes
  *                           (projections, rotary encoding at the tree
- *                           positions, the tree attention above, gated MLP).
+ *                           positions, the tree attention above, gated MLP);
+ *   specv_pack_weights, specv_verify_layer_packed   the same layer on weights
+ *                           stored in the tile order its products read.
  *
  * Sources (web pages on speculative decoding):
  *   [SD-review] paper review of Leviathan, Kalman, Matias, "Fast Inference
@@ -427,6 +429,41 @@ specv_status specv_verify_layer(const void* x, const void* w_qkv, const void* w_
 /* Workspace bytes of specv_verify_layer (0 for invalid sizes). */
 size_t specv_verify_layer_workspace_bytes(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
                                           int32_t Lmax, int32_t inter);
+
+/*
+ * A weight matrix of the layer in the tile order its products read (the same
+ * layer as specv_verify_layer, [SD-EAGLE] "Two-Model Setup" step 2; the order
+ * is a storage format only, the arithmetic is unchanged).
+ *
+ *   w       [N][K] bf16, row-major ([out][in] of the linear map)
+ *   N, K    N a positive multiple of 32, K a positive multiple of 64 (true of
+ *           every matrix of the layer: (Hq + 2 Hkv) D, Hq D, 2 inter rows)
+ *   packed  N K bf16 elements: 16-byte unit ((rb (K/64) + s) 4 + j) 64 + l
+ *           holds w[32 rb + l % 32][64 s + 32 (l / 32) + 8 j .. + 8], so that
+ *           each weight load of the product reads 1 KB contiguous
+ *
+ * Pack once per matrix (weights are static); the gate/up matrix packs as one
+ * [2 inter][Hq D] matrix.  Ownership: device memory of the caller, both
+ * 16-byte aligned and not overlapping; asynchronous on `stream`.
+ * Errors: SPECV_ERR_INVALID_ARG (sizes, NULL, alignment, overlap), SPECV_ERR_HIP.
+ */
+specv_status specv_pack_weights(const void* w, int32_t N, int32_t K, void* packed, hipStream_t stream);
+
+/*
+ * specv_verify_layer with w_qkv, w_o, w_gate_up and w_down each in the order of
+ * specv_pack_weights.  Arguments, outputs, workspace and errors are those of
+ * specv_verify_layer; the outputs are bit-identical to it (the same products
+ * in the same order, only the weights' storage order differs).
+ */
+specv_status specv_verify_layer_packed(const void* x, const void* w_qkv, const void* w_o,
+                                       const void* w_gate_up, const void* w_down,
+                                       const void* attn_norm, const void* mlp_norm,
+                                       float rms_eps, float rope_theta,
+                                       void* k_cache, void* v_cache, const int32_t* ctx_len,
+                                       const uint32_t* mask, const int32_t* depth,
+                                       int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
+                                       int32_t Lmax, int32_t inter, void* out,
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* specv_status_string(specv_status s);

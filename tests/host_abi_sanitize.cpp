@@ -181,6 +181,18 @@ int main() {
     expect("layer workspace query B INT_MAX",
            static_cast<int>(specv_verify_layer_workspace_bytes(IMAX, 5, 8, 2, 128, 64, 512)), 0);
 
+    // the same layer on packed weights, and packing
+    expect("packed layer K INT_MAX", specv_verify_layer_packed(dev, dev, dev, dev, dev, dev, dev, 1e-5f, 1e4f, dev,
+                                                               dev, i32, u32, i32, 2, IMAX, 8, 2, 128, IMAX, 512,
+                                                               dev, ws, lw, nullptr), I);
+    expect("packed layer inter % 64", specv_verify_layer_packed(dev, dev, dev, dev, dev, dev, dev, 1e-5f, 1e4f, dev,
+                                                                dev, i32, u32, i32, 2, 5, 8, 2, 128, 64, 500, dev, ws,
+                                                                lw, nullptr), I);
+    expect("pack N INT_MAX", specv_pack_weights(dev, IMAX, 64, fake(0x90000), nullptr), I);
+    expect("pack K INT_MAX", specv_pack_weights(dev, 64, IMAX, fake(0x90000), nullptr), I);
+    expect("pack N negative", specv_pack_weights(dev, -32, 64, fake(0x90000), nullptr), I);
+    expect("pack NULL", specv_pack_weights(nullptr, 64, 64, fake(0x90000), nullptr), I);
+
     std::printf("%s: %d failing checks\n", failures ? "FAILED" : "ok", failures);
     return failures ? 1 : 0;
 }

@@ -157,3 +157,83 @@ def test_layer_output_may_overwrite_its_input():
         outs.append(out.float().cpu().numpy())
     assert np.array_equal(outs[0], outs[1])
     log("verify_layer: in-place output matches")
+
+
+def _pack_reference(w):
+    """The tile order of specv_pack_weights written out in numpy: 16-byte unit
+    ((rb (K/64) + s) 4 + j) 64 + l holds w[32 rb + l % 32][64 s + 32 (l / 32) + 8 j .. + 8]."""
+    N, K = w.shape
+    out = np.empty((N * K // 8, 8), dtype=w.dtype)
+    u = 0
+    for rb in range(N // 32):
+        for s in range(K // 64):
+            for j in range(4):
+                for lane in range(64):
+                    row, col = 32 * rb + lane % 32, 64 * s + 32 * (lane // 32) + 8 * j
+                    out[u] = w[row, col:col + 8]
+                    u += 1
+    return out.reshape(N, K)
+
+
+@pytest.mark.parametrize("N,K", [(32, 64), (64, 192), (320, 128)])
+def test_pack_weights_tile_order(N, K):
+    specv = _specv()
+    rng = np.random.default_rng(N * 1000 + K)
+    bits = rng.integers(0, 1 << 16, size=(N, K), dtype=np.uint16)       # every bf16 pattern, NaNs included
+    w = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    packed = specv.pack_weights(w)
+    torch.cuda.synchronize()
+    got = packed.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, _pack_reference(bits)), f"N={N} K={K}"
+    log(f"pack_weights: N={N} K={K} matches the tile order")
+
+
+@pytest.mark.parametrize("shape", [
+    (3, 7, 4, 2, 64, 384, 100),
+    (3, 7, 3, 1, 64, 320, 90),           # ragged weight tiles: rows past N clamped in both orders
+    (2, 40, 4, 2, 128, 192, 150),
+    (40, 7, 4, 2, 64, 128, 40),          # several activation launches
+])
+def test_packed_layer_is_bit_identical(shape):
+    """The same products in the same order: outputs and cache rows equal to the row-major layer's."""
+    specv = _specv()
+    B, n1, Hq, Hkv, D, inter, ctx = shape
+    rng = np.random.default_rng(sum(shape))
+    parent = np.stack([workloads.random_tree(rng, n1 - 1, 3, 6) for _ in range(B)]).reshape(B, n1)
+    li = workloads.make_layer("layer-packed", parent, rng.integers(ctx // 2, ctx + 1, size=B), Hq, Hkv, D, inter,
+                              seed_base=int(rng.integers(1 << 30)), extra_slack=3)
+    w = specv.LayerWeights(_bf(li.w_qkv), _bf(li.w_o), _bf(li.w_gate_up), _bf(li.w_down), _bf(li.attn_norm),
+                           _bf(li.mlp_norm))
+    wp = specv.pack_layer_weights(w)
+    assert wp.packed and wp.attn_norm is w.attn_norm
+    mask, depth, _ = specv.build_tree_mask(torch.from_numpy(parent).cuda())
+    ctxt = torch.from_numpy(li.ctx_len).cuda()
+    res = []
+    for weights in (w, wp):
+        kc, vc = _bf(li.k_cache), _bf(li.v_cache)
+        out = specv.verify_layer(_bf(li.x), weights, kc, vc, ctxt, mask, depth, Hq)
+        torch.cuda.synchronize()
+        res.append([t.view(torch.int16).cpu().numpy() for t in (out, kc, vc)])
+    for a, b, what in zip(res[0], res[1], ("out", "k_cache", "v_cache")):
+        assert np.array_equal(a, b), f"{shape}: {what} differs between packed and row-major weights"
+    log(f"verify_layer packed: B={B} N1={n1} Hq={Hq} Hkv={Hkv} D={D} inter={inter} bit-identical")
+
+
+def test_packed_layer_chain_workload_bit_identical():
+    specv = _specv()
+    li = workloads.chain_layer()
+    w = specv.LayerWeights(_bf(li.w_qkv), _bf(li.w_o), _bf(li.w_gate_up), _bf(li.w_down), _bf(li.attn_norm),
+                           _bf(li.mlp_norm))
+    wp = specv.pack_layer_weights(w)
+    mask, depth, _ = specv.build_tree_mask(torch.from_numpy(li.parent).cuda())
+    ctxt = torch.from_numpy(li.ctx_len).cuda()
+    res = []
+    for weights in (w, wp):
+        kc, vc = _bf(li.k_cache), _bf(li.v_cache)
+        out = specv.verify_layer(_bf(li.x), weights, kc, vc, ctxt, mask, depth, li.Hq)
+        torch.cuda.synchronize()
+        res.append([t.view(torch.int16).cpu().numpy() for t in (out, kc, vc)])
+        del kc, vc
+    for a, b, what in zip(res[0], res[1], ("out", "k_cache", "v_cache")):
+        assert np.array_equal(a, b), f"chain workload: {what} differs between packed and row-major weights"
+    log("verify_layer packed: chain workload bit-identical")

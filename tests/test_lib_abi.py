@@ -216,3 +216,37 @@ def test_verify_layer_host_validation(specv):
     assert specv.verify_layer_workspace_bytes(32, 5, 32, 8, 128, 2054, 14336) > 0
     assert specv.verify_layer_workspace_bytes(32, 5, 32, 8, 128, 2054, 100) == 0
     assert "specv_verify_layer" in declared_functions()
+
+
+def test_packed_layer_host_validation(specv):
+    """The packed layer shares every check of specv_verify_layer; packing checks its sizes,
+    pointers, alignment and overlap on the host."""
+    lib = specv.lib
+    v = ctypes.c_void_p(256)
+
+    def layer(**kw):
+        a = dict(B=2, K=5, inter=128, ws=v)
+        a.update(kw)
+        return lib.specv_verify_layer_packed(v, v, v, v, v, v, v, 1e-5, 10000.0, v, v, v, v, v, a["B"], a["K"], 4, 2,
+                                             64, 64, a["inter"], v, a["ws"], 1 << 40, None)
+
+    assert layer(B=-1) == 1
+    assert layer(inter=100) == 1
+    assert layer(ws=None) == 3
+    assert layer(B=0) == 0
+
+    def pack(w=256, N=64, K=128, out=1 << 20):
+        return lib.specv_pack_weights(ctypes.c_void_p(w) if w else None, N, K,
+                                      ctypes.c_void_p(out) if out else None, None)
+
+    assert pack(N=0) == 1
+    assert pack(N=48) == 1                  # not a multiple of 32
+    assert pack(K=96) == 1                  # not a multiple of 64
+    assert pack(N=-32) == 1
+    assert pack(w=0) == 1
+    assert pack(out=0) == 1
+    assert pack(w=264) == 1                 # misaligned
+    assert pack(out=256 + 64 * 128) == 1    # overlaps w (64 x 128 bf16 = 16 KiB)
+    assert b"overlap" in lib.specv_last_error()
+    for n in ("specv_pack_weights", "specv_verify_layer_packed"):
+        assert n in declared_functions()
