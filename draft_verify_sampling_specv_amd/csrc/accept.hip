@@ -28,6 +28,10 @@
 //      final draw pass are split into P contiguous ranges; partial sums are exchanged and added in
 //      rank order (fp64), so every workgroup sees the same totals.  The workgroup whose range holds
 //      the CDF crossing searches it (per-segment sums in LDS, then one wave) and writes the token.
+// Phase 1 can also run as a launch of its own just before (accept_stats_kernel: one wave per
+// item over the whole device, the same item code, the same tagged words), after which the team
+// kernel skips it.  That is the default where the team kernel would deal many items to each
+// workgroup: dispatch then balances the stream across the device, which a static deal cannot.
 // Workgroups exchange values through 64-bit words (32-bit value, 32-bit epoch of the launch)
 // written and read with device-scope atomic stores / loads: a word carries its own validity, so
 // no fence is needed.  The epoch lives in the workspace and advances by one per launch -- a replay
@@ -431,13 +435,69 @@ __device__ __forceinline__ void exchange_sum(const double* s_vals, int P, int ra
     }
 }
 
+// ---------------------------------------------------------------------------------- statistics launch
+
+constexpr int kStatThreads = 256;               // 4 waves, one item each
+constexpr int kStatWaves = kStatThreads / kWave;
+
+// The launch's tag: the workspace epoch + 1 (0 is the tag of a zero-filled word; the epoch
+// 0xFFFFFFFF wraps to tag 1).
+__device__ __forceinline__ uint32_t tag_of(uint32_t epoch) { return epoch == 0xFFFFFFFFu ? 1u : epoch + 1u; }
+
+// Phase 1 as a launch of its own: one wave per item (row, chunk) of every sequence -- all target
+// rows, then the draft rows of internal nodes -- writing the tagged chunk statistics the team
+// kernel reads, with the same arithmetic (item_stats, same template), so the same bits.  The
+// workgroups are independent and short, so the device's dispatcher spreads the vocabulary stream
+// over every compute unit as they free up: no static deal, no teammate to wait for.  A draft
+// item first checks that its row has a child (any parent[b][c] == row); a leaf's draft row is not
+// read.  The tag is the one the team kernel that follows on the stream will use: it reads the
+// same epoch, which only that kernel advances.
+template <typename T, bool kGreedy, bool kVecOK>
+__global__ void __launch_bounds__(kStatThreads)
+accept_stats_kernel(const T* __restrict__ target, const T* __restrict__ draft, const int32_t* __restrict__ parent,
+                    int B, int n1, int V, int nchunk, int with_draft, float k, const uint64_t* __restrict__ ctl,
+                    uint64_t* __restrict__ statw) {
+    constexpr int kItem = item_elems<T>();
+    const int lane = threadIdx.x % kWave;
+    const int wu = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
+    const int64_t tgt_items = static_cast<int64_t>(n1) * nchunk;
+    const int64_t per_seq = tgt_items * (with_draft ? 2 : 1);
+    const int64_t total = per_seq * B;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kStatWaves;
+    const uint32_t tag = tag_of(static_cast<uint32_t>(
+        __builtin_amdgcn_readfirstlane(static_cast<int>(load_word(const_cast<uint64_t*>(ctl))))));
+    for (int64_t it = static_cast<int64_t>(blockIdx.x) * kStatWaves + wu; it < total; it += stride) {
+        const int64_t b = it / per_seq, j0 = it - b * per_seq;
+        const bool isd = j0 >= tgt_items;
+        const int64_t j = isd ? j0 - tgt_items : j0;
+        const int row = static_cast<int>(j / nchunk), c = static_cast<int>(j - static_cast<int64_t>(row) * nchunk);
+        const int64_t seq = b * n1;
+        if (isd) {
+            // only rows with a child are read (values of parent are compared, never used as indices)
+            bool f = false;
+            for (int i = 1 + lane; i < n1; i += kWave) f |= parent[seq + i] == row;
+            if (__ballot(f) == 0) continue;      // (wave-uniform)
+        }
+        const T* src = (isd ? draft : target) + (seq + row) * V;
+        const int lo = c * kItem, hi = min(V, lo + kItem);
+        uint4 r[kWaveLoads];
+        uint32_t w0, w1;
+        item_stats<T, kGreedy, kVecOK, false>(src, lo, hi, lane, k, r, false, w0, w1);
+        if (lane == 0) {
+            uint64_t* slot = statw + ((seq + row) * nchunk + c) * 4 + (isd ? 2 : 0);
+            put_word(slot, w0, tag);
+            put_word(slot + 1, w1, tag);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------------- the kernel
 
 template <typename T, bool kGreedy, bool kVecOK>
 __global__ void __launch_bounds__(kThreads)
 accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
               const int32_t* __restrict__ tokens, const int32_t* __restrict__ parent, int B, int n1,
-              int V, int nchunk, int P, int rule, float k, uint64_t seed, uint64_t offset,
+              int V, int nchunk, int P, int rule, float k, uint64_t seed, uint64_t offset, int stats_ready,
               uint64_t* __restrict__ ctl, uint32_t* __restrict__ seen, uint64_t wait_ticks,
               uint64_t* __restrict__ statw, uint64_t* __restrict__ partw, int32_t* __restrict__ accept_len,
               int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_nodes,
@@ -522,7 +582,7 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
         asm volatile("" ::: "memory");
         uint4 r[kWaveLoads];
         const int it0 = rank + wu * P;
-        const bool pre = kPre && it0 < n1 * nchunk;       // wave-uniform
+        const bool pre = kPre && !stats_ready && it0 < n1 * nchunk;       // wave-uniform
         if constexpr (kPre) {
             // issued by every wave (branch-free, so the compiler's count of outstanding loads
             // stays exact); a wave without a target-row first item gets an empty range, whose
@@ -540,8 +600,7 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
             if (!ok) s_bad = 1;
         }
         if (first_seq) {
-            tag = static_cast<uint32_t>(
-                __builtin_amdgcn_readfirstlane(static_cast<int>(epoch_raw == 0xFFFFFFFFu ? 1u : epoch_raw + 1u)));
+            tag = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(tag_of(epoch_raw))));
             if (t == 0) __hip_atomic_store(seen + blockIdx.x, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         lds_barrier();
@@ -664,7 +723,8 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
         //    since the two waves sharing a SIMD do not progress at the same rate (the older one is
         //    favoured at issue), which a fixed split would turn into idle waves at the end of the
         //    phase
-        const int nitems = (n1 + ni) * nchunk;
+        //    (nothing to do here when the statistics launch has written them)
+        const int nitems = stats_ready ? 0 : (n1 + ni) * nchunk;
         for (int kk = wu;;) {     // (wave-uniform)
             const int it = rank + kk * P;
             if (it >= nitems) break;
@@ -1193,6 +1253,20 @@ uint64_t wait_ticks() {
     return static_cast<uint64_t>(us) * 100u;      // the wall clock runs at 100 MHz
 }
 
+// Whether phase 1 runs as a launch of its own before the team kernel: SPECV_ACCEPT_SPLIT = 0
+// (never) or 1 (always); by default when the team kernel would deal at least kSplitItems items
+// to each of its workgroups.  There the static deal's uneven finish costs more than the second
+// launch (many sequences per team, or long rows over small teams); with a few items per
+// workgroup the statistics hide under the team kernel's own start-up and the second launch is
+// pure latency.
+constexpr int64_t kSplitItems = 128;
+bool split_stats(int64_t items, int grid) {
+    const char* e = std::getenv("SPECV_ACCEPT_SPLIT");
+    if (e && e[0] == '0' && e[1] == '\0') return false;
+    if (e && e[0] == '1' && e[1] == '\0') return true;
+    return items >= kSplitItems * grid;
+}
+
 template <typename T, bool kGreedy, bool kVecOK>
 hipError_t launch_kernel(const AcceptArgs& a, hipStream_t stream) {
     int nchunk = chunks_of<T>(a.V);
@@ -1228,9 +1302,21 @@ hipError_t launch_kernel(const AcceptArgs& a, hipStream_t stream) {
     float* p_tok = a.p_tok;
     float* q_tok = a.q_tok;
     int rule = a.rule;
+    const int with_draft = (!kGreedy && rule != kRuleDeterministic) ? 1 : 0;
+    const int64_t items = static_cast<int64_t>(B) * n1 * nchunk * (1 + with_draft);
+    int stats_ready = 0;
+    if (split_stats(items, grid)) {
+        const int64_t wgs = std::min<int64_t>((items + kStatWaves - 1) / kStatWaves, int64_t{1} << 22);
+        hipLaunchKernelGGL((accept_stats_kernel<T, kGreedy, kVecOK>), dim3(static_cast<unsigned>(wgs)),
+                           dim3(kStatThreads), 0, stream, target, draft, parent, B, n1, V, nchunk, with_draft, k,
+                           ctl, statw);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        stats_ready = 1;
+    }
     hipLaunchKernelGGL((accept_kernel<T, kGreedy, kVecOK>), dim3(grid), dim3(kThreads), 0, stream, target, draft,
-                       tokens, parent, B, n1, V, nchunk, P, rule, k, seed, offset, ctl, seen, wt, statw, partw,
-                       accept_len, out_tokens, out_nodes, p_tok, q_tok);
+                       tokens, parent, B, n1, V, nchunk, P, rule, k, seed, offset, stats_ready, ctl, seen, wt,
+                       statw, partw, accept_len, out_tokens, out_nodes, p_tok, q_tok);
     return hipGetLastError();
 }
 

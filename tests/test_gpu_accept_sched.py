@@ -6,6 +6,11 @@ computes them itself.  With a budget of 0 almost every value not yet published w
 is computed on the owner's behalf; the outputs must stay bit-identical to the default run and
 to the oracle.  The same holds with another stream holding compute units, and for a call
 captured in a graph and replayed (each launch takes a new epoch from the workspace).
+
+The chunk statistics run either inside the team kernel or as a launch of their own before it
+(SPECV_ACCEPT_SPLIT; by default the split where each workgroup would get many items): the wait
+tests pin the team kernel's own statistics phase (SPECV_ACCEPT_SPLIT=0), and the two forms must
+give the same bits on every configuration.
 """
 
 import numpy as np
@@ -78,6 +83,7 @@ def test_accept_exact_when_every_wait_gives_up(name, monkeypatch):
     b0 = specv.AcceptBuffers.allocate(w.B, w.N1, w.V, logits_dtype(w), "cuda")
     ref = _run(w, inputs, b0)
     monkeypatch.setenv("SPECV_ACCEPT_WAIT_US", "0")
+    monkeypatch.setenv("SPECV_ACCEPT_SPLIT", "0")
     b1 = specv.AcceptBuffers.allocate(w.B, w.N1, w.V, logits_dtype(w), "cuda")
     outs = [_run(w, inputs, b1) for _ in range(3)]
     items, parts = _counters(b1)
@@ -89,12 +95,33 @@ def test_accept_exact_when_every_wait_gives_up(name, monkeypatch):
         compare_accept(outs[0], run_accept_oracle(w), name=f"wait0-{name}")
 
 
+SPLIT_CASES = dict(CASES, tiny=lambda: workloads.tiny_chain_trials(10_000))
+
+
+@pytest.mark.parametrize("name", list(SPLIT_CASES))
+def test_accept_split_statistics_launch_gives_the_same_bits(name, monkeypatch):
+    """Phase 1 as its own launch (one wave per item over the whole device) or inside the team
+    kernel: the same arithmetic on the same items, so identical outputs, call after call."""
+    specv = _specv()
+    w = SPLIT_CASES[name]()
+    inputs = _inputs(w)
+    bufs = specv.AcceptBuffers.allocate(w.B, w.N1, w.V, logits_dtype(w), "cuda")
+    for i in range(2):
+        monkeypatch.setenv("SPECV_ACCEPT_SPLIT", "0")
+        fused = _run(w, inputs, bufs, offset=w.offset + i)
+        monkeypatch.setenv("SPECV_ACCEPT_SPLIT", "1")
+        split = _run(w, inputs, bufs, offset=w.offset + i)
+        _same(fused, split, f"split-{name}-{i}")
+    log(f"[{name}] statistics launched apart and inside the team kernel: identical outputs")
+
+
 def test_accept_wait_zero_takes_the_recompute_paths(monkeypatch):
     """On a team of several workgroups, a budget of 0 must actually exercise both paths."""
     specv = _specv()
     w = workloads.eagle_config()          # B = 16: teams of 16 workgroups
     inputs = _inputs(w)
     monkeypatch.setenv("SPECV_ACCEPT_WAIT_US", "0")
+    monkeypatch.setenv("SPECV_ACCEPT_SPLIT", "0")
     bufs = specv.AcceptBuffers.allocate(w.B, w.N1, w.V, logits_dtype(w), "cuda")
     for i in range(5):
         _run(w, inputs, bufs, offset=w.offset + i)
