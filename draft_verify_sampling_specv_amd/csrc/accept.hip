@@ -141,7 +141,7 @@ __device__ __forceinline__ void load_item(const T* row, int lo, int hi, int lane
         const_cast<T*>(row + lo), 0, (hi - lo) * static_cast<int>(sizeof(T)), kBufferWord3);
 #pragma unroll
     for (int u = 0; u < kWaveLoads; ++u) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, u * kWave * 16, 0);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, u * kWave * 16, kCachePolicyNT);
         r[u] = make_uint4(v[0], v[1], v[2], v[3]);
     }
 }
@@ -226,7 +226,7 @@ __device__ __forceinline__ void item_stats(const T* src, int lo, int hi, int lan
             if constexpr (kLean) {
                 const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                     const_cast<T*>(src + lo), 0, (hi - lo) * static_cast<int>(sizeof(T)), kBufferWord3);
-                const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, u * kWave * 16, 0);
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, u * kWave * 16, kCachePolicyNT);
                 rv = make_uint4(v[0], v[1], v[2], v[3]);
             } else {
                 rv = r[u];
@@ -334,8 +334,8 @@ __device__ __forceinline__ double range_pass(const T* __restrict__ trow, const T
                 rt[j] = make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
                 rd[j] = rt[j];
                 if (i0 + j < t1 && base < V) {
-                    rt[j] = *reinterpret_cast<const uint4*>(trow + base);
-                    if (use_q) rd[j] = *reinterpret_cast<const uint4*>(drow + base);
+                    rt[j] = load_nt(trow + base);
+                    if (use_q) rd[j] = load_nt(drow + base);
                 }
             }
         }

@@ -161,7 +161,7 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                 const int key = min(kb + 16 * ks + 8 * (e / 4) + 4 * h + (e % 4), kmax);
 #pragma unroll
                 for (int dh = 0; dh < kDH; ++dh)
-                    vr[ks][dh][e] = *reinterpret_cast<const uint32_t*>(vbase + static_cast<int64_t>(key) * D + 64 * dh + 2 * col);
+                    vr[ks][dh][e] = load_nt32(vbase + static_cast<int64_t>(key) * D + 64 * dh + 2 * col);
             }
         load_k(min(t + KS, ntiles - 1), kmax);
 

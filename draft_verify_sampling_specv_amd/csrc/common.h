@@ -9,6 +9,21 @@ namespace specv {
 constexpr int kWave = 64;
 
 // ---------------------------------------------------------------------------------------------
+// Streaming loads with the non-temporal cache policy, for data read once (the KV cache, logit
+// rows, packed weights).  Plain streaming reads of HBM measured about 15% faster with it on this
+// device (16-byte loads over 1 GiB: 6.9-7.1 TB/s against 6.0-6.2 TB/s with the default policy).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kCachePolicyNT = 2;      // buffer-load cache-policy operand: non-temporal
+
+__device__ __forceinline__ uint4 load_nt(const void* p) {
+    const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t load_nt32(const void* p) {
+    return __builtin_nontemporal_load(static_cast<const uint32_t*>(p));
+}
+
+// ---------------------------------------------------------------------------------------------
 // Element loads.  Logits and attention operands arrive as fp32 or bf16; bf16 is widened to fp32
 // by placing its 16 bits in the high half of an fp32 word (exact).
 
