@@ -1259,7 +1259,7 @@ uint64_t wait_ticks() {
 // launch (many sequences per team, or long rows over small teams); with a few items per
 // workgroup the statistics hide under the team kernel's own start-up and the second launch is
 // pure latency.
-constexpr int64_t kSplitItems = 128;
+constexpr int64_t kSplitItems = 64;
 bool split_stats(int64_t items, int grid) {
     const char* e = std::getenv("SPECV_ACCEPT_SPLIT");
     if (e && e[0] == '0' && e[1] == '\0') return false;
