@@ -57,7 +57,7 @@ MFMA_PEAK_TFLOPS = 2500.0
 
 # HBM traffic of the dominant kernel (attn_decode_kernel<128, 8, 1>) per call on this workload, from
 # two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), each scaled by what the same
-# counter reads for a 256 MiB device-to-device copy (FETCH_SIZE 131085.0 KiB -> x1.99981,
+# counter reads for a 256 MiB device-to-device copy (FETCH_SIZE 131084.5 KiB -> x1.99981,
 # WRITE_SIZE 262144.0 KiB -> x1.0).  Summaries and commands: profiles/chain_step_pmc.md.
 # Valid only for the kernel sources it was measured on (their SHA-256 below); null otherwise.
 ATTN_TRAFFIC = {
@@ -65,8 +65,8 @@ ATTN_TRAFFIC = {
                 "draft_verify_sampling_specv_amd/csrc/attn_common.h",
                 "draft_verify_sampling_specv_amd/csrc/common.h",
                 "draft_verify_sampling_specv_amd/csrc/kernels.h"],
-    "sha256": "407e24844eb562afd50ab19908a414282213fd2196029eff8e1d9a102ef02e9f",
-    "fetch_kib": 132456.0, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131085.0, "write_scale": 1.0,
+    "sha256": "696b2e89ce7039f2563f05cc7c4022a0cc0336134034d77fae6f959f59ea5cdc",
+    "fetch_kib": 132319.0, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131084.5, "write_scale": 1.0,
 }
 
 # The same for the sampled accept kernel (accept_kernel<bf16, sampled>) on this workload: the
@@ -76,8 +76,8 @@ ACCEPT_TRAFFIC = {
     "sources": ["draft_verify_sampling_specv_amd/csrc/accept.hip",
                 "draft_verify_sampling_specv_amd/csrc/common.h",
                 "draft_verify_sampling_specv_amd/csrc/kernels.h"],
-    "sha256": "6ae10dac319e29fc57e844155dc40d6f8942dcc417f08134f5627bdf27cf0aab",
-    "fetch_kib": 13211.2, "write_kib": 2164.0, "fetch_scale": 262144.0 / 131085.0, "write_scale": 1.0,
+    "sha256": "24ac578e5f1f3ce57eec256b864e3d9577905faac31f36313298daafa204dbf6",
+    "fetch_kib": 13205.8, "write_kib": 2164.0, "fetch_scale": 262144.0 / 131084.5, "write_scale": 1.0,
 }
 
 
