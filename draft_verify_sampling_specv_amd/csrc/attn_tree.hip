@@ -427,23 +427,37 @@ attn_tree_combine_kernel(const uint16_t* __restrict__ opart, const float2* __res
     const int b = static_cast<int>(orow / (static_cast<int64_t>(Hq) * n1));
     const int kv = hh / G, g = hh % G;
     const int row = node * G + g;
+    // every load of a batch of kCombine splits is issued at once (their (max, sum) words and
+    // partial outputs, whatever the context length says), so a thread waits about one round trip
+    // per batch; batches merge online (the running sums rescaled to the new maximum)
+    constexpr int kCombine = 8;
     const int L = ctx_len[b];
-    const bool ok = L >= 0 && L <= Lmax - n1;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float den = 0.f, M = -INFINITY;
     const int64_t ubase = (static_cast<int64_t>(b) * Hkv + kv) * nsplit;
-    if (ok) {
-        for (int s = 0; s < nsplit; ++s) {
-            const float2 ml = mlpart[(ubase + s) * R + row];
-            if (ml.y > 0.f) M = fmaxf(M, ml.x);
+    for (int s0 = 0; s0 < nsplit; s0 += kCombine) {
+        float2 ml[kCombine];
+        uint4 v[kCombine];
+#pragma unroll
+        for (int i = 0; i < kCombine; ++i) {
+            const int64_t prow = (ubase + min(s0 + i, nsplit - 1)) * R + row;
+            ml[i] = mlpart[prow];
+            v[i] = *reinterpret_cast<const uint4*>(opart + prow * D + d0);
         }
-        for (int s = 0; s < nsplit; ++s) {
-            const int64_t prow = (ubase + s) * R + row;
-            const float2 ml = mlpart[prow];
-            if (!(ml.y > 0.f)) continue;
-            const float wgt = ml.y * __builtin_amdgcn_exp2f(ml.x - M);
-            const uint4 v = *reinterpret_cast<const uint4*>(opart + prow * D + d0);
-            const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+        float Mn = M;
+#pragma unroll
+        for (int i = 0; i < kCombine; ++i)
+            if (s0 + i < nsplit && ml[i].y > 0.f) Mn = fmaxf(Mn, ml[i].x);
+        const float sc = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+        den *= sc;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= sc;
+        M = Mn;
+#pragma unroll
+        for (int i = 0; i < kCombine; ++i) {
+            const bool use = s0 + i < nsplit && ml[i].y > 0.f;
+            const float wgt = use ? ml[i].y * __builtin_amdgcn_exp2f(ml[i].x - M) : 0.f;
+            const uint32_t x[4] = {use ? v[i].x : 0u, use ? v[i].y : 0u, use ? v[i].z : 0u, use ? v[i].w : 0u};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 acc[2 * e] += wgt * __uint_as_float(x[e] << 16);
@@ -452,6 +466,7 @@ attn_tree_combine_kernel(const uint16_t* __restrict__ opart, const float2* __res
             den += wgt;
         }
     }
+    const bool ok = L >= 0 && L <= Lmax - n1;
     const float inv = ok ? 1.f / den : NAN;
     uint4 st;
     st.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
