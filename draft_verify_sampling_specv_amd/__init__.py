@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     AttnBuffers,
     lib,
     library_path,
+    debug_bounds,
     build_tree_mask,
     tree_attn_verify,
     accept_resample,

@@ -8,7 +8,13 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "libspecv.so")
+# SPECV_LIBRARY=libspecv_checked.so selects the bounds-checked debug build (tests); only the two
+# library files built next to this module can be named
+_LIBRARIES = ("libspecv.so", "libspecv_checked.so")
+_name = os.environ.get("SPECV_LIBRARY", "libspecv.so")
+if _name not in _LIBRARIES:
+    raise ImportError(f"SPECV_LIBRARY={_name!r}: expected one of {_LIBRARIES}")
+library_path = os.path.join(_HERE, _name)
 
 if not os.path.exists(library_path):
     raise ImportError(
@@ -25,6 +31,14 @@ lib.specv_status_string.restype = ctypes.c_char_p
 lib.specv_status_string.argtypes = [ctypes.c_int]
 lib.specv_last_error.restype = ctypes.c_char_p
 lib.specv_last_error.argtypes = []
+lib.specv_debug_bounds.restype = ctypes.c_int64
+lib.specv_debug_bounds.argtypes = [ctypes.c_int32]
+
+
+def debug_bounds(reset=True):
+    """The bounds record of a checked build (0: no index out of range since the last reset), -1 in
+    the product build."""
+    return int(lib.specv_debug_bounds(1 if reset else 0))
 
 lib.specv_build_tree_mask.restype = ctypes.c_int
 lib.specv_build_tree_mask.argtypes = [_vp, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _vp]

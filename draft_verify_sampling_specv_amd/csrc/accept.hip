@@ -622,8 +622,9 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
         uint32_t gzt = 0, gzd = 0;
         if (!kGreedy && t > 0 && t < n1) {
             const int pa = par[t], x = tok[t];
-            gzt = raw_bits(target[(seq + pa) * V + x]);
-            if (rule != kRuleDeterministic) gzd = raw_bits(draft[(seq + pa) * V + x]);
+            const int64_t gi = (seq + SPECV_CHK(pa, n1, kSiteAcceptGatherRow)) * V + SPECV_CHK(x, V, kSiteAcceptGatherToken);
+            gzt = raw_bits(target[gi]);
+            if (rule != kRuleDeterministic) gzd = raw_bits(draft[gi]);
         }
         // both uniforms of every node (Philox; computed while the gathers are in flight)
         if (!kGreedy) {
@@ -639,9 +640,9 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
         const bool small = n1 <= kMaskNodes;
         for (int c = 1 + t; c < n1; c += kThreads) {
             const int pa = par[c];
-            info[pa] = 1;
-            atomicMin(&fch[pa], c);
-            if (small) atomicOr(&cmask[pa][c >> 6], 1ull << (c & 63));
+            info[SPECV_CHK(pa, n1, kSiteAcceptLink)] = 1;
+            atomicMin(&fch[SPECV_CHK(pa, n1, kSiteAcceptLink)], c);
+            if (small) atomicOr(&cmask[SPECV_CHK(pa, kMaskNodes, kSiteAcceptLink)][c >> 6], 1ull << (c & 63));
         }
         if (!small) {
             // larger trees: each wave walks all nodes 64 at a time, one LDS read per lane, the
@@ -680,7 +681,7 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                 int nx = -1, d = 0;
 #pragma unroll
                 for (int q = kMaskWords - 1; q >= 0; --q) {
-                    const uint64_t m = cmask[pa][q];
+                    const uint64_t m = cmask[SPECV_CHK(pa, kMaskNodes, kSiteAcceptLink)][q];
                     // siblings after c in this word (all of it if the word is past c's; cb <= 63,
                     // so 2 << cb wraps to 0 only for cb == 63, leaving no bits)
                     const uint64_t later = q > cw ? m : (q == cw ? m & ~((2ull << cb) - 1ull) : 0ull);
@@ -897,7 +898,8 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
             if (!kGreedy) {
                 if (v > 0) {
                     const int pa = par[v];
-                    const float zt = (v == t) ? widen<T>(gzt) : Elem<T>::load(target + (seq + pa) * V, tok[v]);
+                    const float zt = (v == t) ? widen<T>(gzt) : Elem<T>::load(target + (seq + SPECV_CHK(pa, n1, kSiteAcceptGatherRow)) * V,
+                                                                                  SPECV_CHK(tok[v], V, kSiteAcceptGatherToken));
                     const double lp = static_cast<double>(zt) * k - Mt[pa];     // (log2 units)
                     const double pd = exp2(lp) / St[pa];
                     pv_ = static_cast<float>(pd);
@@ -906,7 +908,8 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                         pq[v] = pd;
                         qx[v] = 1.f;
                     } else {
-                        const float zd = (v == t) ? widen<T>(gzd) : Elem<T>::load(draft + (seq + pa) * V, tok[v]);
+                        const float zd = (v == t) ? widen<T>(gzd) : Elem<T>::load(draft + (seq + SPECV_CHK(pa, n1, kSiteAcceptGatherRow)) * V,
+                                                                                     SPECV_CHK(tok[v], V, kSiteAcceptGatherToken));
                         const double lq = static_cast<double>(zd) * k - Md[pa];
                         const double qd = exp2(lq) / Sd[pa];
                         pq[v] = exp2(lp - lq) * (Sd[pa] / St[pa]);
@@ -945,7 +948,7 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                             int c = fch[v] < n1 ? fch[v] : -1;
                             while (c >= 0 && tok[c] != y) c = nsib[c];
                             if (c < 0) { cmd = 2; break; }
-                            if (lane == 0) path[n] = c;
+                            if (lane == 0) path[SPECV_CHK(n, n1, kSiteAcceptPath)] = c;
                             ++n;
                             v = c;
                             continue;
@@ -963,7 +966,7 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                                                  ? (cs < 1.0 ? pq[c] / (1.0 - cs) : pq[c])
                                                  : fmax(0.0, pq[c] - cs) * Q / R;
                         if (uacc[c] < ratio) {
-                            if (lane == 0) path[n] = c;
+                            if (lane == 0) path[SPECV_CHK(n, n1, kSiteAcceptPath)] = c;
                             ++n;
                             v = c;
                             cs = 0.0; R = 1.0; Q = 1.0;
@@ -1007,14 +1010,14 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                 }
                 __syncthreads();
                 if (s_cmd != 0) break;
-                const int64_t rr = (seq + s_row) * V;
+                const int64_t rr = (seq + SPECV_CHK(s_row, n1, kSiteAcceptEnd)) * V;
                 const int row = s_row;
                 const float ps = s_ps, qs = s_qs;
                 const double mine = range_pass<T, kVecOK>(target + rr, draft + rr, V, my_t0, my_t1, Mt[row], Md[row],
                                                           k, ps, qs, ilist, 0, nullptr, red, rt, rd);
                 double Rn = mine;
                 if (P > 1) {
-                    uint64_t* slots = pw + static_cast<int64_t>(npass) * P * 2;
+                    uint64_t* slots = pw + static_cast<int64_t>(SPECV_CHK(npass, n1 + 1, kSiteAcceptPass)) * P * 2;
                     // teammates whose share did not come in time: computed here
                     for (uint64_t miss = exchange_post(slots, P, rank, mine, tag, wait_ticks, s_vals, &s_mask); miss;
                          miss &= miss - 1) {
@@ -1046,13 +1049,13 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
             if (t == 0) accept_len[b] = na;
         }
         if (cmd == 2) {
-            if (rank == 0 && t == 0) out_tokens[seq + na] = info[e];
+            if (rank == 0 && t == 0) out_tokens[seq + SPECV_CHK(na, n1, kSiteAcceptOut)] = info[e];
             __syncthreads();
             continue;
         }
 
         // -- H. the draw at node e: w(x) = (p(x) - c q(x))+, smallest x whose CDF exceeds u * W
-        const int64_t rr = (seq + e) * V;
+        const int64_t rr = (seq + SPECV_CHK(e, n1, kSiteAcceptEnd)) * V;
         const float mt = Mt[e], ps = s_ps, qs = s_qs;
         const float md = (qs != 0.f) ? Md[e] : 0.f;
         const int nexcl = s_nexcl;
@@ -1060,7 +1063,7 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                                                   ilist, nexcl, seg, red, rt, rd);
         double before = 0.0, W = mine;
         if (P > 1) {
-            uint64_t* slots = pw + static_cast<int64_t>(npass) * P * 2;
+            uint64_t* slots = pw + static_cast<int64_t>(SPECV_CHK(npass, n1 + 1, kSiteAcceptPass)) * P * 2;
             for (uint64_t miss = exchange_post(slots, P, rank, mine, tag, wait_ticks, s_vals, &s_mask); miss;
                  miss &= miss - 1) {
                 const int r = __builtin_ctzll(miss);
@@ -1196,7 +1199,7 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
                 if (lane == 0) s_found = y;
             }
             __syncthreads();
-            if (t == 0) out_tokens[seq + na] = (s_found >= 0 && s_found < V) ? s_found : 0;
+            if (t == 0) out_tokens[seq + SPECV_CHK(na, n1, kSiteAcceptOut)] = (s_found >= 0 && s_found < V) ? s_found : 0;
         } else if (owner < 0 && rank == 0) {
             // no residual mass at all (a zero-probability event in exact arithmetic): the token with
             // the largest p(x) - c q(x), lowest index on ties
@@ -1214,7 +1217,7 @@ accept_kernel(const T* __restrict__ target, const T* __restrict__ draft,
             __syncthreads();
             if (t == 0) {
                 for (int i = 1; i < kWaves; ++i) argmax_merge(pv[0], pi[0], pv[i], pi[i]);
-                out_tokens[seq + na] = (pi[0] >= 0 && pi[0] < V) ? pi[0] : 0;
+                out_tokens[seq + SPECV_CHK(na, n1, kSiteAcceptOut)] = (pi[0] >= 0 && pi[0] < V) ? pi[0] : 0;
             }
         }
         __syncthreads();

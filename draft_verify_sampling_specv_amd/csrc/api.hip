@@ -77,6 +77,26 @@ const char* specv_status_string(specv_status s) {
 
 const char* specv_last_error(void) { return g_last_error; }
 
+#ifdef SPECV_CHECKED
+}  // extern "C"
+namespace specv {
+__device__ unsigned long long specv_oob_word = 0;
+}  // namespace specv
+extern "C" {
+int64_t specv_debug_bounds(int32_t reset) {
+    unsigned long long w = 0;
+    if (hipDeviceSynchronize() != hipSuccess) return -2;
+    if (hipMemcpyFromSymbol(&w, HIP_SYMBOL(specv::specv_oob_word), sizeof(w)) != hipSuccess) return -2;
+    if (reset) {
+        const unsigned long long z = 0;
+        if (hipMemcpyToSymbol(HIP_SYMBOL(specv::specv_oob_word), &z, sizeof(z)) != hipSuccess) return -2;
+    }
+    return static_cast<int64_t>(w);
+}
+#else
+int64_t specv_debug_bounds(int32_t) { return -1; }
+#endif
+
 specv_status specv_build_tree_mask(const int32_t* parent, int32_t B, int32_t K, uint32_t* mask,
                                    int32_t* depth, int32_t* tree_status, hipStream_t stream) {
     if (B < 0) return fail(SPECV_ERR_INVALID_ARG, "B = %d < 0", B);

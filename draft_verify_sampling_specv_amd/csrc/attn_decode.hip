@@ -73,7 +73,7 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     // always clamped to a real key).
     uint4 kn[kKS];
     auto load_k = [&](int t, int kclamp) {
-        const int kkey = min(t * kTileKeys + col, kclamp);
+        const int kkey = SPECV_CHK(min(t * kTileKeys + col, kclamp), Lmax, kSiteDecodeKey);
 #pragma unroll
         for (int s2 = 0; s2 < kKS; ++s2)
             kn[s2] = *reinterpret_cast<const uint4*>(kbase + static_cast<int64_t>(kkey) * D + 16 * s2 + 8 * h);
@@ -158,7 +158,7 @@ attn_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int key = min(kb + 16 * ks + 8 * (e / 4) + 4 * h + (e % 4), kmax);
+                const int key = SPECV_CHK(min(kb + 16 * ks + 8 * (e / 4) + 4 * h + (e % 4), kmax), Lmax, kSiteDecodeKey);
 #pragma unroll
                 for (int dh = 0; dh < kDH; ++dh)
                     vr[ks][dh][e] = load_nt32(vbase + static_cast<int64_t>(key) * D + 64 * dh + 2 * col);

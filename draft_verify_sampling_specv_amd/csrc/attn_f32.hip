@@ -41,9 +41,9 @@ attn_f32_kernel(const float* __restrict__ q, const float* __restrict__ kc,
     for (int key = lane; key < L + n1; key += kWave) {
         if (key >= L) {
             const int jj = key - L;
-            if (!((mrow[jj >> 5] >> (jj & 31)) & 1u)) continue;
+            if (!((mrow[SPECV_CHK(jj >> 5, words, kSiteF32MaskWord)] >> (jj & 31)) & 1u)) continue;
         }
-        const float* kr = kb + static_cast<int64_t>(key) * D;
+        const float* kr = kb + static_cast<int64_t>(SPECV_CHK(key, Lmax, kSiteF32Key)) * D;
         float s = 0.f;
 #pragma unroll
         for (int d = 0; d < D; ++d) s = fmaf(qv[d], kr[d], s);
@@ -51,7 +51,7 @@ attn_f32_kernel(const float* __restrict__ q, const float* __restrict__ kc,
         const float mn = fmaxf(m, s);
         const float a = exp2f(m - mn);
         const float p = exp2f(s - mn);
-        const float* vr = vb + static_cast<int64_t>(key) * D;
+        const float* vr = vb + static_cast<int64_t>(SPECV_CHK(key, Lmax, kSiteF32Key)) * D;
 #pragma unroll
         for (int d = 0; d < D; ++d) acc[d] = acc[d] * a + p * vr[d];
         l = l * a + p;

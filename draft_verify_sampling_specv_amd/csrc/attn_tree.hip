@@ -156,7 +156,7 @@ struct TileTransfers {
             } else {
                 int row, feat;
                 source(j, lane, row, feat);
-                const int key = min(t * kTreeTile + row, Ltot - 1);
+                const int key = SPECV_CHK(min(t * kTreeTile + row, Ltot - 1), Ltot, kSiteTreeKey);
                 dma16(base + static_cast<int64_t>(key) * D + feat, lds);
             }
         }
@@ -194,7 +194,7 @@ __device__ __forceinline__ void tile_compute(WaveRow<D>& wr, const uint16_t* kt,
                     bool vis = key < L;
                     if (!vis && key < Ltot) {
                         const int jj = key - L;
-                        vis = (wr.mrow[jj >> 5] >> (jj & 31)) & 1u;
+                        vis = (wr.mrow[SPECV_CHK(jj, Ltot - L, kSiteTreeMaskWord) >> 5] >> (jj & 31)) & 1u;
                     }
                     if (!vis) s[st][r] = -INFINITY;
                 }
@@ -352,7 +352,7 @@ attn_tree_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc
 
     const int L = ctx_len[b];
     const bool seq_ok = L >= 0 && L <= Lmax - n1;
-    const int Ltot = seq_ok ? L + n1 : 0;
+    const int Ltot = SPECV_CHK(seq_ok ? L + n1 : 0, int64_t(Lmax) + 1, kSiteTreeKey);   // (the key range read)
     const int ntiles = seq_ok ? (Ltot + kTreeTile - 1) / kTreeTile : 0;
     const int tps = (ntiles + nsplit - 1) / nsplit;
     const int t0 = min(ntiles, split * tps), t1 = min(ntiles, t0 + tps);

@@ -9,6 +9,35 @@ namespace specv {
 constexpr int kWave = 64;
 
 // ---------------------------------------------------------------------------------------------
+// Bounds-checked build.  Compiled with -DSPECV_CHECKED (libspecv_checked.so, a debug library),
+// every global or LDS access whose index is derived from input data -- parent and token values,
+// context lengths, accepted node ids, frontier entries -- goes through SPECV_CHK(i, n, site).  An index
+// outside [0, n) is recorded in specv_oob_word (the first one: site in the high half, the index in
+// the low half) and replaced by 0, so the access stays inside its buffer and the kernel runs to its
+// end.  In the product build SPECV_CHK(i, n, site) is the index expression itself.
+enum CheckSite : int {
+    kSiteMaskWalk = 1,
+    kSiteCommitNode, kSiteCommitSrc, kSiteCommitDst,
+    kSiteAcceptGatherRow, kSiteAcceptGatherToken, kSiteAcceptLink, kSiteAcceptPath, kSiteAcceptEnd,
+    kSiteAcceptPass, kSiteAcceptOut,
+    kSiteDecodeKey, kSiteTreeKey, kSiteTreeMaskWord, kSiteF32Key, kSiteF32MaskWord,
+    kSiteExpandFrontier, kSiteExpandNode, kSiteExpandPos, kSiteLayerCache,
+};
+#ifdef SPECV_CHECKED
+extern __device__ unsigned long long specv_oob_word;
+template <typename I>
+__device__ __forceinline__ I checked_index(I i, int64_t n, int site) {
+    if (static_cast<int64_t>(i) >= 0 && static_cast<int64_t>(i) < n) return i;
+    atomicCAS(&specv_oob_word, 0ull,
+              (static_cast<unsigned long long>(site) << 32) | static_cast<uint32_t>(static_cast<int64_t>(i)));
+    return I(0);
+}
+#define SPECV_CHK(i, n, site) ::specv::checked_index((i), (n), (site))
+#else
+#define SPECV_CHK(i, n, site) (i)
+#endif
+
+// ---------------------------------------------------------------------------------------------
 // Streaming loads with the non-temporal cache policy, for data read once (the KV cache, logit
 // rows, packed weights).  Plain streaming reads of HBM measured about 15% faster with it on this
 // device (16-byte loads over 1 GiB: 6.9-7.1 TB/s against 6.0-6.2 TB/s with the default policy).

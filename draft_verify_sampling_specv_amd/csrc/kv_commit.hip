@@ -46,7 +46,7 @@ kv_commit_kernel(uint4* __restrict__ kc, uint4* __restrict__ vc, const int32_t* 
     if (ok) {
         for (int d = 1 + t; d <= a; d += kCommitThreads) {
             const int nd = nodes[d - 1];
-            s_node[d] = nd;
+            s_node[SPECV_CHK(d, kMaxNodes, kSiteCommitNode)] = nd;
             if (nd < d || nd >= n1 || (d > 1 && nodes[d - 2] >= nd)) s_bad = 1;
         }
     }
@@ -64,7 +64,7 @@ kv_commit_kernel(uint4* __restrict__ kc, uint4* __restrict__ vc, const int32_t* 
             const int i = t + j * kCommitThreads;
             if (i < nv) {
                 const int d = d0 + i / nvec, e = i % nvec, nd = s_node[d];
-                if (nd != d) buf[j] = base[static_cast<int64_t>(L + nd) * nvec + e];
+                if (nd != d) buf[j] = base[static_cast<int64_t>(SPECV_CHK(L + nd, Lmax, kSiteCommitSrc)) * nvec + e];
             }
         }
         __syncthreads();    // (waits for the loads: the whole chunk is read before it is written)
@@ -73,7 +73,7 @@ kv_commit_kernel(uint4* __restrict__ kc, uint4* __restrict__ vc, const int32_t* 
             const int i = t + j * kCommitThreads;
             if (i < nv) {
                 const int d = d0 + i / nvec, e = i % nvec, nd = s_node[d];
-                if (nd != d) base[static_cast<int64_t>(L + d) * nvec + e] = buf[j];
+                if (nd != d) base[static_cast<int64_t>(SPECV_CHK(L + d, Lmax, kSiteCommitDst)) * nvec + e] = buf[j];
             }
         }
         __syncthreads();

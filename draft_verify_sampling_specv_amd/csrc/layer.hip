@@ -397,7 +397,8 @@ __global__ __launch_bounds__(64) void qkv_epilogue_kernel(
         qr[j + half] = ok ? f32_to_bf16(hi) : 0x7fc0;
     } else if (ok) {
         const int kvh = head < Hq + Hkv ? head - Hq : head - Hq - Hkv;
-        uint16_t* dst = (head < Hq + Hkv ? kc : vc) + ((static_cast<int64_t>(b) * Hkv + kvh) * Lmax + L + i) * D;
+        uint16_t* dst = (head < Hq + Hkv ? kc : vc) +
+                        ((static_cast<int64_t>(b) * Hkv + kvh) * Lmax + SPECV_CHK(L + i, Lmax, kSiteLayerCache)) * D;
         dst[j] = f32_to_bf16(lo);
         dst[j + half] = f32_to_bf16(hi);
     }

@@ -46,7 +46,7 @@ __global__ void __launch_bounds__(256) build_tree_mask_kernel(const int32_t* __r
             d = 0;
             while (true) {
                 if ((j >> 5) == w) word |= 1u << (j & 31);
-                int p = par[j];
+                int p = par[SPECV_CHK(j, n1, kSiteMaskWalk)];
                 if (p < 0) break;
                 j = p;
                 ++d;

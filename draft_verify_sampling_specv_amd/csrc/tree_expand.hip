@@ -326,7 +326,8 @@ expand_select_kernel(const RowTop* __restrict__ rows, const int32_t* __restrict_
         const int f = c / k, j = c % k;
         const RowTop& r = rb[f];
         double sc = -INFINITY;
-        if (j < r.count) sc = score[tb + frontier[b * F + f]] + (static_cast<double>(r.z[j]) * invT - r.lse);
+        if (j < r.count)
+            sc = score[tb + SPECV_CHK(frontier[b * F + f], nmax, kSiteExpandFrontier)] + (static_cast<double>(r.z[j]) * invT - r.lse);
         cs[c] = sc;
     }
     if (t == 0) s_total = 0;
@@ -363,11 +364,11 @@ expand_select_kernel(const RowTop* __restrict__ rows, const int32_t* __restrict_
         if (kept) {
             const int pos = before + __popcll(bal & ((1ull << lane) - 1ull));
             const int f = c / k, j = c % k;
-            const int node = n + pos;
+            const int node = SPECV_CHK(n + pos, nmax, kSiteExpandNode);
             parent[tb + node] = frontier[b * F + f];
             tokens[tb + node] = rb[f].tok[j];
             score[tb + node] = cs[c];
-            new_frontier[static_cast<int64_t>(b) * keep + pos] = node;
+            new_frontier[static_cast<int64_t>(b) * keep + SPECV_CHK(pos, keep, kSiteExpandPos)] = node;
         }
         done += all;
         __syncthreads();

@@ -471,6 +471,21 @@ const char* specv_status_string(specv_status s);
 /* Text of the last error returned to the calling thread ("" if none). */
 const char* specv_last_error(void);
 
+/*
+ * Debugging aid, for tests (not part of the method): the bounds record of a
+ * bounds-checked build of this library (libspecv_checked.so, compiled with
+ * SPECV_CHECKED).  In that build every kernel access whose index is derived
+ * from input data (parent and token values, context lengths, accepted node
+ * ids, frontier entries) is checked against its range; the first index out
+ * of range is recorded (site number in bits 32-63, the index in bits 0-31)
+ * and replaced by 0, so the access stays in its buffer.
+ *   reset  nonzero: clear the record after reading it
+ * Returns 0 if nothing was recorded, the record otherwise, and -1 in the
+ * product build (no checks compiled in).  Synchronises the current device
+ * first (in the checked build); -2 if that or the read fails.
+ */
+int64_t specv_debug_bounds(int32_t reset);
+
 #ifdef __cplusplus
 }
 #endif

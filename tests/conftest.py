@@ -1,6 +1,8 @@
 import os
 import sys
 
+import pytest
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -35,3 +37,15 @@ def pytest_terminal_summary(terminalreporter):
         else:
             tr.write_line("  " + name + ": " + ", ".join(
                 f"{k} {v:.3e}" if isinstance(v, float) else f"{k} {v}" for k, v in r.items() if k != "kind"))
+
+
+@pytest.fixture(autouse=True)
+def _bounds_record(request):
+    """Under the bounds-checked library (SPECV_LIBRARY=libspecv_checked.so) every GPU test must leave
+    the bounds record clear: no kernel index derived from input data fell outside its range."""
+    yield
+    if os.environ.get("SPECV_LIBRARY") != "libspecv_checked.so" or request.node.get_closest_marker("gpu") is None:
+        return
+    import draft_verify_sampling_specv_amd as specv
+    rec = specv.debug_bounds(reset=True)
+    assert rec == 0, f"bounds record {rec:#x}: check site {rec >> 32}, index {rec & 0xffffffff}"

@@ -40,6 +40,20 @@ def specv():
     return m
 
 
+def test_checked_build_exports_the_same_functions_and_the_product_build_has_no_record():
+    """The bounds-checked debug library (SPECV_CHECKED) is built beside the product one and exports
+    every declared function; the product library reports that it records nothing (-1)."""
+    checked = os.path.join(ROOT, "draft_verify_sampling_specv_amd", "libspecv_checked.so")
+    assert os.path.exists(checked), "libspecv_checked.so not built"
+    clib = ctypes.CDLL(checked)
+    for n in declared_functions():
+        assert hasattr(clib, n), f"{n} missing from libspecv_checked.so"
+    lib = ctypes.CDLL(LIB)
+    lib.specv_debug_bounds.restype = ctypes.c_int64
+    lib.specv_debug_bounds.argtypes = [ctypes.c_int32]
+    assert lib.specv_debug_bounds(0) == -1
+
+
 def test_status_strings(specv):
     lib = specv.lib
     assert lib.specv_status_string(0) == b"ok"
