@@ -65,8 +65,8 @@ ATTN_TRAFFIC = {
                 "draft_verify_sampling_specv_amd/csrc/attn_common.h",
                 "draft_verify_sampling_specv_amd/csrc/common.h",
                 "draft_verify_sampling_specv_amd/csrc/kernels.h"],
-    "sha256": "696b2e89ce7039f2563f05cc7c4022a0cc0336134034d77fae6f959f59ea5cdc",
-    "fetch_kib": 132319.0, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131084.5, "write_scale": 1.0,
+    "sha256": "6db737ccc47ad6e726625f10013159c5030bcc3513e52618a837bd61d4ade724",
+    "fetch_kib": 132319.8, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131084.5, "write_scale": 1.0,
 }
 
 # The same for the sampled accept kernel (accept_kernel<bf16, sampled>) on this workload: the
@@ -76,8 +76,8 @@ ACCEPT_TRAFFIC = {
     "sources": ["draft_verify_sampling_specv_amd/csrc/accept.hip",
                 "draft_verify_sampling_specv_amd/csrc/common.h",
                 "draft_verify_sampling_specv_amd/csrc/kernels.h"],
-    "sha256": "24ac578e5f1f3ce57eec256b864e3d9577905faac31f36313298daafa204dbf6",
-    "fetch_kib": 13205.8, "write_kib": 2164.0, "fetch_scale": 262144.0 / 131084.5, "write_scale": 1.0,
+    "sha256": "b2fc10342fb4f346e2473b42b2bc5178f078bcee37b74d9cb02b46dd40b58eb1",
+    "fetch_kib": 13203.5, "write_kib": 2164.0, "fetch_scale": 262144.0 / 131084.5, "write_scale": 1.0,
 }
 
 
