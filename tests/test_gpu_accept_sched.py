@@ -160,8 +160,11 @@ def test_accept_exact_beside_a_concurrent_stream():
         compare_accept(outs[-1], run_accept_oracle(w), name=f"concurrent-{name}")
 
 
-def test_accept_graph_replays_take_new_epochs():
-    """One captured call replayed with new logits each time matches the eager call every time."""
+@pytest.mark.parametrize("split", ["0", "1"])
+def test_accept_graph_replays_take_new_epochs(split, monkeypatch):
+    """One captured call replayed with new logits each time matches the eager call every time, with
+    the statistics inside the team kernel (one launch captured) and as a launch of their own (two)."""
+    monkeypatch.setenv("SPECV_ACCEPT_SPLIT", split)
     specv = _specv()
     base = workloads.eagle_config()
     dt = logits_dtype(base)
@@ -185,5 +188,5 @@ def test_accept_graph_replays_take_new_epochs():
         torch.cuda.synchronize()
         got = {k: getattr(bufs.result, k).cpu().numpy().copy() for k in KEYS}
         want = _run(base, (tl, dl, tok, par), eager)
-        _same(want, got, f"graph-replay{rep}")
-        log(f"graph replay {rep}: identical to the eager call")
+        _same(want, got, f"graph-replay{rep}-split{split}")
+        log(f"graph replay {rep} (split {split}): identical to the eager call")
