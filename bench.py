@@ -8,7 +8,9 @@ rotate over enough sets (> 2 x 256 MB) that the Infinity Cache cannot serve them
 
 Prints ONE JSON line.  Extra legs:
   roofline      attention call (HBM-bound here): algorithmic bytes / mean call time (HIP events
-                on the launch stream); the accept call's figure is reported beside it;
+                on the launch stream), against the nominal 8 TB/s and against the read ceiling
+                measured in the same run (specv_read_probe over 1 GiB); the accept call's figure
+                is reported beside it;
   cpu_baseline  the oracle (numpy fp64) on a bounded sample of the same workload, host cores.
 
   verify_layer  one whole target layer over the same 192 rows (specv_verify_layer): its time,
@@ -253,7 +255,16 @@ def main():
     big2.copy_(big)
     ms_copy = timed(lambda i: big2.copy_(big), 5)
     copy_gbs = 2 * (1 << 30) / (ms_copy * 1e-3) / 1e9
-    del big, big2
+    # measured streaming-read ceiling: the library's read probe (the 16-byte non-temporal loads of
+    # the streaming kernels) over the same two 1 GiB buffers in turn
+    big.fill_(1)
+    big2.fill_(2)
+    sink = torch.empty(int(specv.lib.specv_read_probe_sink_words()), dtype=torch.int32, device="cuda")
+    for i in range(2):
+        specv.read_probe(big if i % 2 == 0 else big2, sink)
+    ms_read = timed(lambda i: specv.read_probe(big if i % 2 == 0 else big2, sink), 10)
+    read_gbs = (1 << 30) / (ms_read * 1e-3) / 1e9
+    del big, big2, sink
 
     acc_sets0_w = acc_sets[0]["w"]
     # acceptance statistics of the timed configuration (set 0)
@@ -289,17 +300,20 @@ def main():
         "roofline": {"bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": attn_gbs / HBM_PEAK_GBS, "traffic": attn_traffic_bytes(),
                      "kernel": "attn_decode_kernel<128,8,1> (specv_tree_attn_verify, one launch)",
-                     "bytes_per_call": ab, "ms_per_call": ms_attn},
+                     "bytes_per_call": ab, "ms_per_call": ms_attn,
+                     "read_ceiling_gbs": read_gbs, "frac_of_read_ceiling": attn_gbs / read_gbs},
         "roofline_accept": {"bound": "hbm", "achieved": acc_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": acc_gbs / HBM_PEAK_GBS, "traffic": traffic_bytes(ACCEPT_TRAFFIC),
                             "bytes_per_call": cb, "ms_per_call": ms_accept,
-                            "kernel": "accept_kernel<bf16> (specv_accept_resample, one launch)"},
+                            "kernel": "accept_kernel<bf16> (specv_accept_resample, one launch)",
+                            "read_ceiling_gbs": read_gbs, "frac_of_read_ceiling": acc_gbs / read_gbs},
         "accept_only_positions_per_s": positions / (ms_accept * 1e-3),
         "ms_mask": ms_mask,
         "ms_greedy_accept": ms_greedy,
         "ms_kv_commit": ms_commit,
         "mean_accept_len": mean_len,
         "hbm_copy_gbs": copy_gbs,
+        "hbm_read_ceiling_gbs": read_gbs,
     }
 
     del attn_sets, acc_sets

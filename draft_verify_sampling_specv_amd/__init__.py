@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     lib,
     library_path,
     debug_bounds,
+    read_probe,
     build_tree_mask,
     tree_attn_verify,
     accept_resample,

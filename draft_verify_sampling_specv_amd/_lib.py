@@ -33,6 +33,17 @@ lib.specv_last_error.restype = ctypes.c_char_p
 lib.specv_last_error.argtypes = []
 lib.specv_debug_bounds.restype = ctypes.c_int64
 lib.specv_debug_bounds.argtypes = [ctypes.c_int32]
+lib.specv_read_probe.restype = ctypes.c_int
+lib.specv_read_probe.argtypes = [_vp, ctypes.c_size_t, _vp, ctypes.c_size_t, _vp]
+lib.specv_read_probe_sink_words.restype = ctypes.c_int32
+lib.specv_read_probe_sink_words.argtypes = []
+
+
+def read_probe(buf, sink):
+    """Stream `buf` (a CUDA tensor, 16-byte aligned, size a multiple of 16 bytes) once with the
+    non-temporal 16-byte loads of the streaming kernels, on the current stream (measurement aid)."""
+    nbytes = buf.numel() * buf.element_size()
+    _check("specv_read_probe", lib.specv_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), sink.numel(), _stream()))
 
 
 def debug_bounds(reset=True):

@@ -311,6 +311,19 @@ specv_status specv_kv_commit(void* k_cache, void* v_cache, const int32_t* ctx_le
     return hip_status(specv::launch_kv_commit(a, stream), "kv_commit");
 }
 
+int32_t specv_read_probe_sink_words(void) { return specv::read_probe_blocks(); }
+
+specv_status specv_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words,
+                              hipStream_t stream) {
+    if (bytes == 0) return ok();
+    if (!buf || !sink) return fail(SPECV_ERR_INVALID_ARG, "NULL pointer argument");
+    if ((reinterpret_cast<uintptr_t>(buf) & 15) || (bytes & 15))
+        return fail(SPECV_ERR_INVALID_ARG, "buf and bytes must be multiples of 16");
+    if (sink_words < static_cast<size_t>(specv::read_probe_blocks()))
+        return fail(SPECV_ERR_INVALID_ARG, "sink holds %zu words, needs %d", sink_words, specv::read_probe_blocks());
+    return hip_status(specv::launch_read_probe(buf, bytes, sink, stream), "read_probe");
+}
+
 size_t specv_verify_layer_workspace_bytes(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
                                           int32_t Lmax, int32_t inter) {
     if (B <= 0 || K < 0 || K > SPECV_MAX_NODES - 1 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 ||

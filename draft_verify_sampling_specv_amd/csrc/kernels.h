@@ -102,6 +102,10 @@ struct KvCommitArgs {
 
 hipError_t launch_kv_commit(const KvCommitArgs& a, hipStream_t stream);
 
+// ------------------------------------------------------------------------------------ read probe
+int read_probe_blocks();
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 // ------------------------------------------------------------------------------------ attention
 struct AttnArgs {
     const void* q;

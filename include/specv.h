@@ -472,6 +472,23 @@ const char* specv_status_string(specv_status s);
 const char* specv_last_error(void);
 
 /*
+ * Measurement aid, for benchmarks (not part of the method): the streaming-read
+ * ceiling that the HBM-bound kernels are compared with.  Reads `bytes` of
+ * device memory at `buf` once, with the 16-byte non-temporal loads the
+ * statistics and attention streams use, each of a fixed set of workgroups
+ * taking one contiguous slice; each workgroup stores one word (a fold of what
+ * it read) to sink, so the reads cannot be optimised away.
+ *   buf         device, 16-byte aligned, `bytes` a multiple of 16 (0: no-op)
+ *   sink        device uint32[sink_words], sink_words >= specv_read_probe_sink_words()
+ * Asynchronous on `stream`; time it with events on that stream.  Returns
+ * SPECV_ERR_INVALID_ARG (NULL pointer, misalignment, sink too small) or
+ * SPECV_ERR_HIP.
+ */
+specv_status specv_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words,
+                              hipStream_t stream);
+int32_t specv_read_probe_sink_words(void);
+
+/*
  * Debugging aid, for tests (not part of the method): the bounds record of a
  * bounds-checked build of this library (libspecv_checked.so, compiled with
  * SPECV_CHECKED).  In that build every kernel access whose index is derived

@@ -193,6 +193,17 @@ int main() {
     expect("pack N negative", specv_pack_weights(dev, -32, 64, fake(0x90000), nullptr), I);
     expect("pack NULL", specv_pack_weights(nullptr, 64, 64, fake(0x90000), nullptr), I);
 
+    // read probe (measurement aid)
+    const size_t sw = static_cast<size_t>(specv_read_probe_sink_words());
+    expect("probe empty", specv_read_probe(nullptr, 0, nullptr, 0, nullptr), SPECV_OK);
+    expect("probe NULL buf", specv_read_probe(nullptr, 1024, u32, sw, nullptr), I);
+    expect("probe misaligned", specv_read_probe(fake(0x30008), 1024, u32, sw, nullptr), I);
+    expect("probe size", specv_read_probe(dev, 1000, u32, sw, nullptr), I);
+    expect("probe sink", specv_read_probe(dev, 1024, u32, sw - 1, nullptr), I);
+    expect("probe huge size", specv_read_probe(dev, SIZE_MAX & ~size_t(15), u32, 0, nullptr), I);
+    // the bounds record of the product build
+    expect("bounds record", static_cast<int>(specv_debug_bounds(0)), -1);
+
     std::printf("%s: %d failing checks\n", failures ? "FAILED" : "ok", failures);
     return failures ? 1 : 0;
 }

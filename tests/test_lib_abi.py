@@ -134,6 +134,20 @@ def test_attention_and_mask_host_validation(specv):
     assert lib.specv_build_tree_mask(None, 0, 3, None, None, None, None) == 0
 
 
+def test_read_probe_host_validation(specv):
+    lib = specv.lib
+    v = ctypes.c_void_p(16)
+    n = lib.specv_read_probe_sink_words()
+    assert n > 0
+    assert lib.specv_read_probe(v, 0, None, 0, None) == 0                  # no bytes: nothing to do
+    assert lib.specv_read_probe(None, 1024, v, n, None) == 1
+    assert lib.specv_read_probe(v, 1024, None, n, None) == 1
+    assert lib.specv_read_probe(ctypes.c_void_p(24), 1024, v, n, None) == 1   # misaligned buffer
+    assert lib.specv_read_probe(v, 1000, v, n, None) == 1                  # size not a multiple of 16
+    assert lib.specv_read_probe(v, 1024, v, n - 1, None) == 1              # sink too small
+    assert b"sink" in lib.specv_last_error()
+
+
 def test_kv_commit_host_validation(specv):
     lib = specv.lib
     v = ctypes.c_void_p(16)
