@@ -326,6 +326,9 @@ def main():
         for name in ("tiny", "chain", "chain-greedy", "eagle", "stress", "ptd"):
             log(f"config {name}")
             out["configs"][name] = measure_config(name, args, torch, specv, workloads)
+            for leg in ("accept", "attention"):
+                if isinstance(out["configs"][name].get(leg), dict) and "GBps" in out["configs"][name][leg]:
+                    out["configs"][name][leg]["frac_of_read_ceiling"] = out["configs"][name][leg]["GBps"] / read_gbs
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(acc_sets0_w, a0)
     print(json.dumps(out))
