@@ -67,8 +67,8 @@ ATTN_TRAFFIC = {
                 "draft_verify_sampling_specv_amd/csrc/attn_common.h",
                 "draft_verify_sampling_specv_amd/csrc/common.h",
                 "draft_verify_sampling_specv_amd/csrc/kernels.h"],
-    "sha256": "6db737ccc47ad6e726625f10013159c5030bcc3513e52618a837bd61d4ade724",
-    "fetch_kib": 132319.8, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131084.5, "write_scale": 1.0,
+    "sha256": "39415d793b42e2def947e52b93f1c8aa32691554e646b07d440cbe75d69dcf9e",
+    "fetch_kib": 132320.6, "write_kib": 1584.0, "fetch_scale": 262144.0 / 131084.5, "write_scale": 1.0,
 }
 
 # The same for the sampled accept kernel (accept_kernel<bf16, sampled>) on this workload: the
@@ -78,8 +78,8 @@ ACCEPT_TRAFFIC = {
     "sources": ["draft_verify_sampling_specv_amd/csrc/accept.hip",
                 "draft_verify_sampling_specv_amd/csrc/common.h",
                 "draft_verify_sampling_specv_amd/csrc/kernels.h"],
-    "sha256": "b2fc10342fb4f346e2473b42b2bc5178f078bcee37b74d9cb02b46dd40b58eb1",
-    "fetch_kib": 13203.5, "write_kib": 2164.0, "fetch_scale": 262144.0 / 131084.5, "write_scale": 1.0,
+    "sha256": "6984583b9eb650fab22f538ef373df6d8748b611f31f6b2a18fb7349f15c67cb",
+    "fetch_kib": 13200.9, "write_kib": 2164.0, "fetch_scale": 262144.0 / 131084.5, "write_scale": 1.0,
 }
 
 
