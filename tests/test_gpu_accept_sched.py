@@ -95,7 +95,11 @@ def test_accept_exact_when_every_wait_gives_up(name, monkeypatch):
         compare_accept(outs[0], run_accept_oracle(w), name=f"wait0-{name}")
 
 
-SPLIT_CASES = dict(CASES, tiny=lambda: workloads.tiny_chain_trials(10_000))
+SPLIT_CASES = dict(CASES, tiny=lambda: workloads.tiny_chain_trials(10_000),
+                   # vocabularies that are no multiple of the 16-byte vector: the element-load path
+                   **{"oddV-f32": lambda: workloads.random_case(501, 40, 17, 20011, 0.9, dtype="f32"),
+                      "oddV-bf16": lambda: workloads.random_case(502, 24, 23, 65537, 1.2, dtype="bf16"),
+                      "oddV-greedy": lambda: workloads.random_case(503, 24, 23, 65537, 0.0, dtype="bf16")})
 
 
 @pytest.mark.parametrize("name", list(SPLIT_CASES))
