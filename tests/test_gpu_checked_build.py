@@ -5,7 +5,8 @@ values, context lengths, accepted node ids, frontier entries -- is range-checked
 range is recorded and replaced by 0, so the access stays in its buffer.  This test runs, in a child
 process on that library, the GPU tests that drive the kernels with arbitrary shapes and hostile
 inputs: random trees and chains up to 1024 nodes, invalid parent arrays, tokens and context lengths,
-random accepted paths for the cache commit, random expansion levels, random layer trees.  Each
+random accepted paths for the cache commit, random expansion levels, random layer trees, and the
+accept call with its statistics inside the team kernel and as a launch of their own.  Each
 must pass against the oracle as on the product library, and leave the bounds record clear (the
 conftest fixture reads it after every GPU test under SPECV_LIBRARY=libspecv_checked.so).
 """
@@ -20,9 +21,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CHECKED = os.path.join(ROOT, "draft_verify_sampling_specv_amd", "libspecv_checked.so")
 
 FILES = ["tests/test_gpu_parity.py", "tests/test_gpu_kv_commit.py", "tests/test_gpu_tree_expand.py",
-         "tests/test_gpu_layer.py", "tests/test_gpu_limits.py"]
+         "tests/test_gpu_layer.py", "tests/test_gpu_limits.py", "tests/test_gpu_accept_sched.py"]
 SELECT = ("random or invalid or tiny or mask or short_context or jumps or empty or replays or draft_equals "
-          "or long_path or after_gpu_accept or ties or max_nodes")
+          "or long_path or after_gpu_accept or ties or max_nodes or split_statistics")
 
 
 @pytest.mark.gpu
